@@ -1,0 +1,254 @@
+/*
+ * oracle_gemm.c -- plain CPU reference for the multi-precision square GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
+ * its Python binding) may include, link, load or call this file.  Only the
+ * tests, the smoke check and the benchmark's CPU-baseline leg use it.  It
+ * shares no code, header, table or constant with the GPU path.
+ *
+ * What it computes: C = A * B, written out as the textbook triple loop.
+ *   - "Hand-Written PTX Tensor-Core GEMM Kernels: A Multi-Precision Study on
+ *     NVIDIA L4": the abstract and Section I (Introduction) define the work as
+ *     GEMM in FP16, INT8 and INT4; Section II-A states the operation as
+ *     D = AB + C (here with C = 0); Section VI says the quantized kernels
+ *     return INT32 accumulations with no dequantization or scaling.
+ *   - Listing 2 of the same page (the m16n8k64 .row.col .s4 instruction)
+ *     fixes the operand roles: A is read along its rows ("row"), B along its
+ *     columns ("col"), both contiguous in K, and the 4-bit type is signed.
+ *   - "PTX Programming from Your First Kernel to Tensor Cores", section
+ *     "Multiply one tile with a full warp": FP16 inputs, FP32 accumulators,
+ *     with a worked 16x8x16 example that the tests check.
+ *
+ * Accumulation precision: integers in int64 (exact for every size this
+ * library accepts), FP16 in fp64.  A product of two binary16 values is exact
+ * in fp64 (11+11 significant bits), so only the fp64 summation rounds.
+ * Alongside each FP16 result the oracle returns S = sum_k |a_ik * b_kj|, the
+ * scale of the per-element error bound |C - R| <= 1e-3 * S.
+ *
+ * Layout (the library's operand contract; the pages leave C's layout open and
+ * the reading taken is row-major):
+ *   A[i*lda + k]      A is M x K row-major
+ *   B[j*ldb + k]      B is K x N column-major ("non-transposed" B)
+ *   C[i*ldc + j]      C is M x N row-major
+ * INT4: two signed 4-bit values per byte along K; element k of a row sits in
+ * byte k/2, in the low nibble when k is even and the high nibble when k is
+ * odd; lda/ldb count 4-bit elements (the pages do not give the nibble order;
+ * low-nibble-first is the reading taken).
+ *
+ * Parallelism: output rows are split over POSIX threads; each element is the
+ * same sequential k loop, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL (-1)
+
+/* IEEE 754 binary16 -> double, from the format's definition:
+ * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits; exponent 0 holds
+ * zero and the subnormals fraction * 2^-24; exponent 31 holds inf and NaN. */
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -24);
+    else if (expo == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + frac), expo - 25);
+    return sign ? -v : v;
+}
+
+/* Signed 4-bit element k of a packed row (two's complement, low nibble = even k). */
+static int s4_at(const uint8_t *row, int64_t k)
+{
+    uint8_t byte = row[k >> 1];
+    int v = (k & 1) ? (byte >> 4) : (byte & 0x0f);
+    return v < 8 ? v : v - 16;
+}
+
+/* ----------------------------------------------------------------------- */
+/* Full-matrix products, row-parallel.                                      */
+
+enum prec { P_F16, P_I8, P_I4 };
+
+struct job {
+    enum prec p;
+    int64_t M, N, K;
+    const void *A;
+    int64_t lda;
+    const void *B;
+    int64_t ldb;
+    void *C;        /* int64_t* (int) or double* R (f16) */
+    double *S;      /* f16 only */
+    int64_t ldc;
+    int64_t row0, row1;
+};
+
+static void one_row(const struct job *jb, int64_t i)
+{
+    int64_t j, k;
+    if (jb->p == P_F16) {
+        const uint16_t *a = (const uint16_t *)jb->A + i * jb->lda;
+        double *r = (double *)jb->C + i * jb->ldc;
+        double *s = jb->S + i * jb->ldc;
+        for (j = 0; j < jb->N; ++j) {
+            const uint16_t *b = (const uint16_t *)jb->B + j * jb->ldb;
+            double acc = 0.0, mag = 0.0;
+            for (k = 0; k < jb->K; ++k) {
+                double prod = oracle_half_to_double(a[k]) * oracle_half_to_double(b[k]);
+                acc += prod;
+                mag += fabs(prod);
+            }
+            r[j] = acc;
+            s[j] = mag;
+        }
+    } else if (jb->p == P_I8) {
+        const int8_t *a = (const int8_t *)jb->A + i * jb->lda;
+        int64_t *c = (int64_t *)jb->C + i * jb->ldc;
+        for (j = 0; j < jb->N; ++j) {
+            const int8_t *b = (const int8_t *)jb->B + j * jb->ldb;
+            int64_t acc = 0;
+            for (k = 0; k < jb->K; ++k)
+                acc += (int64_t)a[k] * (int64_t)b[k];
+            c[j] = acc;
+        }
+    } else {
+        const uint8_t *a = (const uint8_t *)jb->A + i * (jb->lda / 2);
+        int64_t *c = (int64_t *)jb->C + i * jb->ldc;
+        for (j = 0; j < jb->N; ++j) {
+            const uint8_t *b = (const uint8_t *)jb->B + j * (jb->ldb / 2);
+            int64_t acc = 0;
+            for (k = 0; k < jb->K; ++k)
+                acc += (int64_t)s4_at(a, k) * (int64_t)s4_at(b, k);
+            c[j] = acc;
+        }
+    }
+}
+
+static void *run_rows(void *arg)
+{
+    const struct job *jb = (const struct job *)arg;
+    for (int64_t i = jb->row0; i < jb->row1; ++i)
+        one_row(jb, i);
+    return NULL;
+}
+
+static int run(struct job base, int nthreads)
+{
+    if (base.M < 0 || base.N < 0 || base.K < 0)
+        return ORACLE_EINVAL;
+    if (base.M == 0 || base.N == 0)
+        return ORACLE_OK;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > base.M)
+        nthreads = (int)base.M;
+    struct job *jobs = (struct job *)calloc((size_t)nthreads, sizeof(struct job));
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) {
+        free(jobs);
+        free(th);
+        return ORACLE_EINVAL;
+    }
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = base;
+        jobs[t].row0 = base.M * t / nthreads;
+        jobs[t].row1 = base.M * (t + 1) / nthreads;
+    }
+    for (int t = 1; t < nthreads; ++t)
+        pthread_create(&th[t], NULL, run_rows, &jobs[t]);
+    run_rows(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t)
+        pthread_join(th[t], NULL);
+    free(jobs);
+    free(th);
+    return ORACLE_OK;
+}
+
+/* FP16 inputs, fp64 result R and magnitude sum S (both M x N, row stride ldr). */
+int oracle_gemm_f16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                    const uint16_t *B, int64_t ldb, double *R, double *S, int64_t ldr,
+                    int nthreads)
+{
+    struct job jb = {P_F16, M, N, K, A, lda, B, ldb, R, S, ldr, 0, 0};
+    return run(jb, nthreads);
+}
+
+/* INT8 inputs, exact int64 sums. */
+int oracle_gemm_i8(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
+                   const int8_t *B, int64_t ldb, int64_t *C, int64_t ldc, int nthreads)
+{
+    struct job jb = {P_I8, M, N, K, A, lda, B, ldb, C, NULL, ldc, 0, 0};
+    return run(jb, nthreads);
+}
+
+/* Packed INT4 inputs (K, lda, ldb in 4-bit elements; lda, ldb even), exact int64 sums. */
+int oracle_gemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+                   const uint8_t *B, int64_t ldb, int64_t *C, int64_t ldc, int nthreads)
+{
+    if ((lda & 1) || (ldb & 1))
+        return ORACLE_EINVAL;
+    struct job jb = {P_I4, M, N, K, A, lda, B, ldb, C, NULL, ldc, 0, 0};
+    return run(jb, nthreads);
+}
+
+/* ----------------------------------------------------------------------- */
+/* Single entries C[rows[t]][cols[t]] for t < count: the same sums, one at  */
+/* a time, for checking sampled outputs of products too large to form.     */
+
+int oracle_entries_f16(int64_t K, const uint16_t *A, int64_t lda, const uint16_t *B,
+                       int64_t ldb, int64_t count, const int64_t *rows, const int64_t *cols,
+                       double *R, double *S)
+{
+    for (int64_t t = 0; t < count; ++t) {
+        const uint16_t *a = A + rows[t] * lda;
+        const uint16_t *b = B + cols[t] * ldb;
+        double acc = 0.0, mag = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double prod = oracle_half_to_double(a[k]) * oracle_half_to_double(b[k]);
+            acc += prod;
+            mag += fabs(prod);
+        }
+        R[t] = acc;
+        S[t] = mag;
+    }
+    return ORACLE_OK;
+}
+
+int oracle_entries_i8(int64_t K, const int8_t *A, int64_t lda, const int8_t *B,
+                      int64_t ldb, int64_t count, const int64_t *rows, const int64_t *cols,
+                      int64_t *C)
+{
+    for (int64_t t = 0; t < count; ++t) {
+        const int8_t *a = A + rows[t] * lda;
+        const int8_t *b = B + cols[t] * ldb;
+        int64_t acc = 0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += (int64_t)a[k] * (int64_t)b[k];
+        C[t] = acc;
+    }
+    return ORACLE_OK;
+}
+
+int oracle_entries_i4(int64_t K, const uint8_t *A, int64_t lda, const uint8_t *B,
+                      int64_t ldb, int64_t count, const int64_t *rows, const int64_t *cols,
+                      int64_t *C)
+{
+    if ((lda & 1) || (ldb & 1))
+        return ORACLE_EINVAL;
+    for (int64_t t = 0; t < count; ++t) {
+        const uint8_t *a = A + rows[t] * (lda / 2);
+        const uint8_t *b = B + cols[t] * (ldb / 2);
+        int64_t acc = 0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += (int64_t)s4_at(a, k) * (int64_t)s4_at(b, k);
+        C[t] = acc;
+    }
+    return ORACLE_OK;
+}

@@ -1,0 +1,72 @@
+"""Plant plausible mistakes in a copy of the oracle's C source and check that
+the pins in test_oracle.py catch every one of them.
+
+The mutants are built in a temporary directory on the CPU; the committed
+oracle is never modified.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle as pins
+
+MUTANTS = {
+    "drop_last_k": ("for (k = 0; k < jb->K; ++k)", "for (k = 0; k < jb->K - 1; ++k)"),
+    "nibble_order": ("(k & 1) ? (byte >> 4) : (byte & 0x0f)", "(k & 1) ? (byte & 0x0f) : (byte >> 4)"),
+    "no_sign_extend": ("return v < 8 ? v : v - 16;", "return v;"),
+    "subnormal_scale": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
+    "exponent_bias": ("ldexp((double)(1024 + frac), expo - 25)", "ldexp((double)(1024 + frac), expo - 24)"),
+    "hidden_bit": ("(double)(1024 + frac)", "(double)(frac)"),
+    "transposed_B_i8": ("acc += (int64_t)a[k] * (int64_t)b[k];\n            c[j] = acc;\n        }\n    } else {",
+                        "acc += (int64_t)a[k] * (int64_t)((const int8_t *)jb->B)[k * jb->ldb + j];\n"
+                        "            c[j] = acc;\n        }\n    } else {"),
+    "B_uses_lda": ("const int8_t *b = (const int8_t *)jb->B + j * jb->ldb;",
+                   "const int8_t *b = (const int8_t *)jb->B + j * jb->lda;"),
+    "i4_byte_stride": ("const uint8_t *a = (const uint8_t *)jb->A + i * (jb->lda / 2);",
+                       "const uint8_t *a = (const uint8_t *)jb->A + i * jb->lda;"),
+    "magnitude_signed": ("mag += fabs(prod);\n            }\n            r[j]", "mag += prod;\n            }\n            r[j]"),
+    "subtract_product": ("acc += prod;\n                mag", "acc -= prod;\n                mag"),
+    "f16_B_uses_lda": ("const uint16_t *b = (const uint16_t *)jb->B + j * jb->ldb;",
+                       "const uint16_t *b = (const uint16_t *)jb->B + j * jb->lda;"),
+    "entries_swap_rc": ("const int8_t *a = A + rows[t] * lda;\n        const int8_t *b = B + cols[t] * ldb;",
+                        "const int8_t *a = A + cols[t] * lda;\n        const int8_t *b = B + rows[t] * ldb;"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SOURCE) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, source, name):
+    old, new = MUTANTS[name]
+    assert old in source, f"mutation site for {name} no longer exists in the oracle"
+    src = tmp_path / "mutant.c"
+    src.write_text(source.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-pthread",
+                           str(src), "-lm", "-o", str(lib)])
+    saved_lib, saved_path = oracle._lib, oracle.LIBRARY
+    caught = []
+    try:
+        oracle._lib = None
+        oracle.LIBRARY = str(lib)
+        small = [(m, n, k) for m in (1, 3, 8) for n in (1, 2, 7) for k in (1, 4, 8)]
+        for pin in pins.PINS:
+            try:
+                if pin is pins.pin_brute_force_tiny:
+                    pin(small)
+                else:
+                    pin()
+            except AssertionError:
+                caught.append(pin.__name__)
+    finally:
+        oracle._lib, oracle.LIBRARY = saved_lib, saved_path
+    assert caught, f"no pin caught the planted mistake {name}"
