@@ -1,0 +1,267 @@
+"""Benchmark of the multi-precision square GEMM on one MI355X.
+
+One step is one pass of the precision sweep: C = A*B at N = 512, 1024, 2048,
+4096 and 8192 (square) for FP16 (fp32 accumulate), INT8 and packed INT4
+(int32 accumulate), 15 GEMMs on seeded synthetic inputs that are resident in
+HBM before the timed region starts.  The JSON line reports:
+
+  value         whole-step throughput in TOPS (2*M*N*K per GEMM, summed over
+                the sweep, divided by the wall time of a step)
+  per_gemm      per (precision, N): mean kernel time from HIP events on the
+                launch stream over the timed steps, TOPS, fraction of peak
+  roofline      the GEMM that takes the largest share of a step, against the
+                MFMA peak of its own precision
+  cpu_baseline  the CPU oracle (plain triple loop) timed on a row sample of
+                every GEMM of the sweep and scaled to whole GEMMs
+
+Usage: python bench.py [--steps K] [--warmup W] [--case f16:8192] [--calib-copy]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TOPS at N=512–8192 per precision (FP16/INT8/INT4) + % of MFMA peak"
+SIZES = (512, 1024, 2048, 4096, 8192)
+PRECS = ("f16", "i8", "i4")
+# MI355X published dense MFMA peaks (TFLOP/s or TOPS).  gfx950 has no 4-bit
+# integer MFMA; INT4 runs on the INT8 MFMA, so its peak is the INT8 one.
+PEAK = {"f16": 2500.0, "i8": 5000.0, "i4": 5000.0}
+HBM_PEAK_GBS = 8000.0
+IN_BYTES = {"f16": 2.0, "i8": 1.0, "i4": 0.5}
+SWEEP_CFG_ID = 4  # seeds of the sweep workload: (cfg_id << 32) ^ (N << 8) ^ operand
+# the pages' own durations for these GEMMs on an NVIDIA L4 (ms; best kernel per
+# precision and size, Table I-c), reported as context only
+L4_MS = {
+    "f16": {512: 0.184, 1024: 1.430, 2048: 11.850, 4096: 102.350, 8192: 16500.0},
+    "i8": {512: 0.109, 1024: 0.726, 2048: 5.410, 4096: 42.000, 8192: 480.060},
+    "i4": {512: 0.056, 1024: 0.382, 2048: 2.810, 4096: 21.520, 8192: 167.100},
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--case", action="append", default=[],
+                    help="time only prec:N (repeatable), e.g. f16:8192")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of C per GEMM for the CPU baseline (default: oracle threads)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 1 GiB device copy, the reference for HBM counter scaling")
+    return ap.parse_args()
+
+
+def gemm_ops(n):
+    return 2.0 * n * n * n
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the GEMM shards by output panels with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import precision_dense_gemm_amd as pd
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cases = [(p, n) for n in SIZES for p in PRECS]
+    if args.case:
+        cases = [(c.split(":")[0], int(c.split(":")[1])) for c in args.case]
+
+    # ---- inputs, resident in HBM before timing ----
+    work = []
+    host = {}
+    for prec, n in cases:
+        t0 = time.time()
+        sa = synth.config_seed(SWEEP_CFG_ID, n, synth.OPERAND_A)
+        sb = synth.config_seed(SWEEP_CFG_ID, n, synth.OPERAND_B)
+        A, Bt = synth.operands(prec, n, n, n, sa, sb)
+        Ad = torch.from_numpy(A).to(dev)
+        Bd = torch.from_numpy(Bt).to(dev)
+        C = torch.empty((n, n), dtype=torch.float32 if prec == "f16" else torch.int32, device=dev)
+        host[(prec, n)] = (A, Bt)
+        work.append((prec, n, Ad, Bd, C))
+        log(f"[bench] inputs {prec} N={n} ready in {time.time() - t0:.1f}s")
+
+    def launch(prec, n, Ad, Bd, C):
+        if prec == "f16":
+            pd.gemm_f16(Ad, Bd, out=C)
+        elif prec == "i8":
+            pd.gemm_i8(Ad, Bd, out=C)
+        else:
+            pd.gemm_i4(Ad, Bd, n, out=C)
+
+    # ---- one parity check per GEMM (sampled entries against the oracle) ----
+    parity = {}
+    if not args.no_parity:
+        import oracle
+        for prec, n, Ad, Bd, C in work:
+            launch(prec, n, Ad, Bd, C)
+            torch.cuda.synchronize()
+            A, Bt = host[(prec, n)]
+            rng = np.random.default_rng(n)
+            rows = rng.integers(0, n, 256)
+            cols = rng.integers(0, n, 256)
+            got = C.cpu().numpy()[rows, cols]
+            if prec == "f16":
+                R, S = oracle.entries_f16(A, Bt, rows, cols)
+                ok = bool(np.all(np.abs(got.astype(np.float64) - R) <= 1e-3 * S))
+            elif prec == "i8":
+                ok = bool(np.array_equal(got.astype(np.int64), oracle.entries_i8(A, Bt, rows, cols)))
+            else:
+                ok = bool(np.array_equal(got.astype(np.int64), oracle.entries_i4(A, Bt, rows, cols)))
+            parity[f"{prec}:{n}"] = ok
+            log(f"[bench] parity {prec} N={n}: {'ok' if ok else 'FAIL'}")
+
+    # ---- warmup, then exactly K timed steps ----
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        for w in work:
+            launch(*w)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    ev = {(p, n): [] for p, n, *_ in work}
+    pool = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in work] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for step in range(args.steps):
+        for w, (s, e) in zip(work, pool[step]):
+            s.record(stream)
+            launch(*w)
+            e.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for step in range(args.steps):
+        for w, se in zip(work, pool[step]):
+            ev[(w[0], w[1])].append(se)
+    ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+
+    step_ops = sum(gemm_ops(n) for _, n, *_ in work)
+    value = step_ops / (ms_per_step * 1e-3) / 1e12
+
+    per = {}
+    for (prec, n), pairs in ev.items():
+        ms = float(np.mean([s.elapsed_time(e) for s, e in pairs])) if pairs else float("nan")
+        tops = gemm_ops(n) / (ms * 1e-3) / 1e12
+        hbm_bytes = n * n * (2 * IN_BYTES[prec] + 4)
+        per[f"{prec}:{n}"] = {
+            "ms": round(ms, 5),
+            "tops": round(tops, 2),
+            "frac_of_peak": round(tops / PEAK[prec], 4),
+            "min_hbm_gbs": round(hbm_bytes / (ms * 1e-3) / 1e9, 1),
+            "l4_tops_context": round(gemm_ops(n) / (L4_MS[prec][n] * 1e-3) / 1e12, 3),
+        }
+        if f"{prec}:{n}" in parity:
+            per[f"{prec}:{n}"]["parity"] = parity[f"{prec}:{n}"]
+
+    # dominant kernel: the largest share of a step
+    dom = max(per, key=lambda k: per[k]["ms"])
+    dprec, dn = dom.split(":")[0], int(dom.split(":")[1])
+    roofline = {
+        "bound": "mfma",
+        "kernel": f"gemm_kernel {dprec} N={dn}",
+        "achieved": per[dom]["tops"],
+        "peak": PEAK[dprec],
+        "unit": "TFLOP/s" if dprec == "f16" else "TOPS",
+        "frac": round(per[dom]["tops"] / PEAK[dprec], 4),
+        "traffic": None,
+    }
+
+    # ---- CPU baseline: the oracle on a row sample of every GEMM ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.default_threads()
+        rows = args.cpu_rows or max(threads, 16)
+        total_s = 0.0
+        sampled_ops = 0.0
+        for prec, n, *_ in work:
+            A, Bt = host[(prec, n)]
+            r = min(rows, n)
+            t0 = time.perf_counter()
+            if prec == "f16":
+                oracle.gemm_f16(A[:r], Bt, threads=threads)
+            elif prec == "i8":
+                oracle.gemm_i8(A[:r], Bt, threads=threads)
+            else:
+                oracle.gemm_i4(A[:r], Bt, threads=threads)
+            dt = time.perf_counter() - t0
+            sampled_ops += 2.0 * r * n * n
+            total_s += dt * (n / r)   # every row of C costs the same
+            log(f"[bench] cpu oracle {prec} N={n}: {r} rows in {dt:.2f}s")
+        cpu = {
+            "value": round(step_ops / total_s / 1e12, 6),
+            "unit": "TOPS",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {rows} rows of C for each of the {len(work)} GEMMs "
+                      f"({sampled_ops / 1e9:.1f} GOP), time scaled by N/{rows} per GEMM",
+        }
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 3 x 1 GiB device-to-device")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16,i8,i4",
+        "data": "synthetic (SplitMix64-seeded; f16 U[-1,1], i8 U[-128,127], i4 U[-8,7])",
+        "config": {
+            "workload": "square GEMM sweep N in {512,1024,2048,4096,8192} x {f16->f32, i8->i32, i4->i32}"
+                        if not args.case else "square GEMM " + ", ".join(args.case),
+            "gemms_per_step": len(work),
+            "layout": "A row-major, B column-major, C row-major",
+        },
+        "per_gemm": per,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    if parity and not all(parity.values()):
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

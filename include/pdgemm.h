@@ -1,0 +1,127 @@
+/*
+ * pdgemm.h -- multi-precision dense GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * C = A * B in three precisions, each a hand-written HIP kernel on the
+ * gfx950 matrix cores (MFMA):
+ *
+ *   gemm_f16  binary16 A, B -> fp32 accumulate -> fp32 C
+ *   gemm_i8   int8 A, B     -> int32 accumulate -> int32 C
+ *   gemm_i4   packed signed 4-bit A, B -> int32 accumulate -> int32 C
+ *
+ * The operation is the one studied in "Hand-Written PTX Tensor-Core GEMM
+ * Kernels: A Multi-Precision Study on NVIDIA L4": GEMM in FP16, INT8 and INT4
+ * (abstract; Section I), D = AB + C on the matrix units (Section II-A) taken
+ * here with C = 0, and INT32 results without dequantization or scaling
+ * (Section VI).  The operand roles follow the ".row.col" form of the MMA in
+ * that paper's Listing 2: A is read along rows and B along columns, both
+ * contiguous in K, which is also the "non-transposed B" layout that its
+ * Section IV-D ablation finds fastest.
+ *
+ * ---------------------------------------------------------------------------
+ * Layout (all three entry points)
+ *   A   M x K, row-major:    element (i, k) at A[i*lda + k],  lda >= K
+ *   B   K x N, column-major: element (k, j) at B[j*ldb + k],  ldb >= K
+ *   C   M x N, row-major:    element (i, j) at C[i*ldc + j],  ldc >= N
+ * The pages do not fix C's layout; row-major is the reading taken.
+ *
+ * gemm_i4: K, lda and ldb count 4-bit elements and must be even.  Element k
+ * of a row sits in byte k/2 of that row (byte stride lda/2), in the low
+ * nibble when k is even and the high nibble when k is odd, as a two's
+ * complement value in [-8, 7].  The paper's INT4 type is signed (".s4",
+ * Listing 2); the nibble order is not given there and low-nibble-first is the
+ * reading taken.
+ *
+ * Semantics: C is overwritten with A*B (no alpha/beta).  K = 0 stores zeros
+ * into the M x N block of C.  M = 0 or N = 0 is a no-op that returns 0.
+ * Integer results are exact.  The exact sum must fit in int32 (always true
+ * for K <= 131071); gemm_i4 additionally requires K <= 131071.  FP16 results
+ * carry fp32 rounding only: every element satisfies
+ * |C - sum_k a_ik b_kj| <= 1e-3 * sum_k |a_ik b_kj| for K up to 16384 (the
+ * worst-case bound of K fp32 additions, K * 2^-24, stays below 1e-3).
+ *
+ * Alignment (checked): A, B and C 16-byte aligned; lda, ldb and ldc span a
+ * multiple of 16 bytes (f16: lda, ldb % 8 == 0; i8: % 16; i4: % 32;
+ * C: ldc % 4 == 0).  M, N and K are otherwise arbitrary: partial tiles are
+ * masked inside the kernels.
+ *
+ * Ownership and execution: every pointer is device memory owned by the
+ * caller.  The library never allocates, frees, copies or synchronizes.  The
+ * call enqueues work on `stream` (a hipStream_t passed as void*; NULL is the
+ * default stream) and returns once it is enqueued.  Entry points are
+ * thread-safe and keep no state between calls.
+ *
+ * Errors: 0 on success.  Negative values are argument errors, found on the
+ * host before any HIP call is made, with nothing enqueued.  Positive values
+ * are hipError_t codes from the launch.  When the environment variable
+ * PDGEMM_SYNC_CHECK is set to 1 at the first call, every call also
+ * synchronizes its stream and returns any execution error.  The library
+ * never aborts or exits the process.
+ * ---------------------------------------------------------------------------
+ */
+#ifndef PDGEMM_H
+#define PDGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PDGEMM_OK 0
+#define PDGEMM_EINVAL_DIM (-1)  /* M, N or K negative, or gemm_i4 K > 131071 */
+#define PDGEMM_EINVAL_LD (-2)   /* lda < K, ldb < K or ldc < N */
+#define PDGEMM_ENULL (-3)       /* NULL pointer for an operand with nonzero extent */
+#define PDGEMM_EINVAL_I4 (-4)   /* gemm_i4: K, lda or ldb odd */
+#define PDGEMM_EALIGN (-5)      /* a base pointer or leading dimension breaks the alignment rule */
+#define PDGEMM_EINVAL_CFG (-6)  /* pdgemm_gemm_cfg: unknown precision or tile configuration */
+
+#define PDGEMM_I4_MAX_K 131071
+
+/* FP16 inputs (IEEE binary16 bit patterns), fp32 accumulation, fp32 output. */
+int gemm_f16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+             const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream);
+
+/* INT8 inputs, int32 accumulation, int32 output. */
+int gemm_i8(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
+            const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream);
+
+/* Packed signed INT4 inputs (two per byte along K, even k in the low nibble),
+ * int32 accumulation, int32 output.  K, lda, ldb count 4-bit elements. */
+int gemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+            const uint8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream);
+
+/* Precision ids and tile configurations, for the calls below. */
+#define PDGEMM_PREC_F16 0
+#define PDGEMM_PREC_I8 1
+#define PDGEMM_PREC_I4 2
+
+/* The same GEMM with an explicit tile configuration (0 <= cfg <
+ * pdgemm_num_configs()); the three entry points above pick one by shape.
+ * Same arguments, layout, alignment and error rules; A, B, C are passed as
+ * untyped device pointers of the precision's element type. */
+int pdgemm_gemm_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K,
+                    const void *A, int64_t lda, const void *B, int64_t ldb,
+                    void *C, int64_t ldc, void *stream);
+
+/* Number of tile configurations, and the one the entry points pick for a
+ * shape (-1 for an unknown precision). */
+int pdgemm_num_configs(void);
+int pdgemm_pick_config(int prec, int64_t M, int64_t N, int64_t K);
+
+/* Tile configuration cfg: block tile rows/cols, wave tile rows/cols,
+ * workgroup size in threads.  Returns 0, or PDGEMM_EINVAL_CFG.  Any output
+ * pointer may be NULL. */
+int pdgemm_config_info(int cfg, int *block_m, int *block_n, int *wave_m, int *wave_n,
+                       int *threads);
+
+/* Static message for a return code (never NULL). */
+const char *pdgemm_strerror(int code);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int pdgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PDGEMM_H */

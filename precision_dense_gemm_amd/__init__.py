@@ -1,0 +1,166 @@
+"""Python binding of libpdgemm: multi-precision dense GEMM on MI355X (gfx950).
+
+Argument marshalling only.  Every GEMM runs in the HIP kernels of
+libpdgemm.so, called through its C ABI (include/pdgemm.h) on the current
+torch stream.  torch is used for device memory and streams; nothing here
+computes.  If the library has not been built, importing this package fails.
+
+Operands are torch tensors on the GPU whose rows are contiguous in K:
+
+    A    (M, K) row-major; a column slice of a wider buffer is fine
+         (lda = A.stride(0))
+    Bt   (N, K): the column-major B of C = A*B, stored as the rows of its
+         transpose (ldb = Bt.stride(0))
+    out  (M, N) row-major (ldc = out.stride(0)); allocated when omitted
+
+INT4 operands are uint8 tensors of packed bytes, (rows, K/2), two signed
+4-bit values per byte with the even k in the low nibble; K is passed
+explicitly and the leading dimensions are counted in 4-bit elements.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libpdgemm.so")
+
+PREC_F16, PREC_I8, PREC_I4 = 0, 1, 2
+I4_MAX_K = 131071
+
+if not os.path.exists(LIBRARY):
+    raise ImportError(
+        f"{LIBRARY} is missing: build the HIP library first "
+        "(python -m precision_dense_gemm_amd.build, or __graft_entry__.build())")
+
+lib = ctypes.CDLL(LIBRARY)
+_i64, _p, _i = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+for _name in ("gemm_f16", "gemm_i8", "gemm_i4"):
+    getattr(lib, _name).argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+    getattr(lib, _name).restype = _i
+lib.pdgemm_gemm_cfg.argtypes = [_i, _i, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+lib.pdgemm_gemm_cfg.restype = _i
+lib.pdgemm_num_configs.argtypes = []
+lib.pdgemm_num_configs.restype = _i
+lib.pdgemm_pick_config.argtypes = [_i, _i64, _i64, _i64]
+lib.pdgemm_pick_config.restype = _i
+lib.pdgemm_config_info.argtypes = [_i] + [ctypes.POINTER(_i)] * 5
+lib.pdgemm_config_info.restype = _i
+lib.pdgemm_strerror.argtypes = [_i]
+lib.pdgemm_strerror.restype = ctypes.c_char_p
+lib.pdgemm_version.argtypes = []
+lib.pdgemm_version.restype = _i
+
+
+class PdgemmError(RuntimeError):
+    def __init__(self, code: int):
+        self.code = code
+        super().__init__(f"pdgemm error {code}: {strerror(code)}")
+
+
+def strerror(code: int) -> str:
+    return lib.pdgemm_strerror(code).decode()
+
+
+def version() -> int:
+    return lib.pdgemm_version()
+
+
+def num_configs() -> int:
+    return lib.pdgemm_num_configs()
+
+
+def pick_config(prec: int, M: int, N: int, K: int) -> int:
+    return lib.pdgemm_pick_config(prec, M, N, K)
+
+
+def config_info(cfg: int) -> dict:
+    vals = [_i() for _ in range(5)]
+    rc = lib.pdgemm_config_info(cfg, *[ctypes.byref(v) for v in vals])
+    if rc:
+        raise PdgemmError(rc)
+    keys = ("block_m", "block_n", "wave_m", "wave_n", "threads")
+    return {k: v.value for k, v in zip(keys, vals)}
+
+
+def _row_major_2d(t: torch.Tensor, name: str):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have contiguous rows (stride(1) == 1)")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _call(prec, A, Bt, out, K, lda, ldb, stream, cfg):
+    M, N = A.shape[0], Bt.shape[0]
+    ldc = _row_major_2d(out, "out")
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must have shape {(M, N)}")
+    args = (M, N, K, A.data_ptr(), lda, Bt.data_ptr(), ldb, out.data_ptr(), ldc, _stream(stream))
+    if cfg is None:
+        fn = (lib.gemm_f16, lib.gemm_i8, lib.gemm_i4)[prec]
+        rc = fn(*args)
+    else:
+        rc = lib.pdgemm_gemm_cfg(prec, cfg, *args)
+    if rc != 0:
+        raise PdgemmError(rc)
+    return out
+
+
+def gemm_f16(A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor | None = None,
+             stream=None, cfg: int | None = None) -> torch.Tensor:
+    """C = A * B for binary16 A (M, K) and Bt (N, K); fp32 accumulate, fp32 C (M, N)."""
+    if A.dtype != torch.float16 or Bt.dtype != torch.float16:
+        raise TypeError("gemm_f16 takes float16 operands")
+    K = A.shape[1]
+    if Bt.shape[1] != K:
+        raise ValueError("A and Bt disagree on K")
+    lda, ldb = _row_major_2d(A, "A"), _row_major_2d(Bt, "Bt")
+    if out is None:
+        out = torch.empty((A.shape[0], Bt.shape[0]), dtype=torch.float32, device=A.device)
+    elif out.dtype != torch.float32:
+        raise TypeError("gemm_f16 writes a float32 output")
+    return _call(PREC_F16, A, Bt, out, K, lda, ldb, stream, cfg)
+
+
+def gemm_i8(A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor | None = None,
+            stream=None, cfg: int | None = None) -> torch.Tensor:
+    """C = A * B for int8 A (M, K) and Bt (N, K); int32 accumulate, int32 C (M, N)."""
+    if A.dtype != torch.int8 or Bt.dtype != torch.int8:
+        raise TypeError("gemm_i8 takes int8 operands")
+    K = A.shape[1]
+    if Bt.shape[1] != K:
+        raise ValueError("A and Bt disagree on K")
+    lda, ldb = _row_major_2d(A, "A"), _row_major_2d(Bt, "Bt")
+    if out is None:
+        out = torch.empty((A.shape[0], Bt.shape[0]), dtype=torch.int32, device=A.device)
+    elif out.dtype != torch.int32:
+        raise TypeError("gemm_i8 writes an int32 output")
+    return _call(PREC_I8, A, Bt, out, K, lda, ldb, stream, cfg)
+
+
+def gemm_i4(A: torch.Tensor, Bt: torch.Tensor, K: int | None = None,
+            out: torch.Tensor | None = None, stream=None, cfg: int | None = None) -> torch.Tensor:
+    """C = A * B for packed INT4 A (M, K/2) and Bt (N, K/2) bytes; int32 C (M, N)."""
+    if A.dtype != torch.uint8 or Bt.dtype != torch.uint8:
+        raise TypeError("gemm_i4 takes uint8 tensors of packed 4-bit values")
+    if K is None:
+        K = 2 * A.shape[1]
+    if A.shape[1] * 2 < K or Bt.shape[1] * 2 < K:
+        raise ValueError("packed operands hold fewer than K values per row")
+    lda, ldb = 2 * _row_major_2d(A, "A"), 2 * _row_major_2d(Bt, "Bt")
+    if out is None:
+        out = torch.empty((A.shape[0], Bt.shape[0]), dtype=torch.int32, device=A.device)
+    elif out.dtype != torch.int32:
+        raise TypeError("gemm_i4 writes an int32 output")
+    return _call(PREC_I4, A, Bt, out, K, lda, ldb, stream, cfg)

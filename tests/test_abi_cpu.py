@@ -1,0 +1,156 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/pdgemm.h declares, and rejects bad arguments on the host before
+any HIP call (dummy, never-dereferenced pointers are enough for that)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pdgemm.h")
+LIB = os.path.join(ROOT, "precision_dense_gemm_amd", "libpdgemm.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libpdgemm.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def codes():
+    text = open(HEADER).read()
+    return {m.group(1): int(m.group(2)) for m in
+            re.finditer(r"#define\s+(PDGEMM_E\w+|PDGEMM_OK)\s+\(?(-?\d+)\)?", text)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    L = ctypes.CDLL(LIB)
+    i64, p, i = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    for name in ("gemm_f16", "gemm_i8", "gemm_i4"):
+        getattr(L, name).argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+        getattr(L, name).restype = i
+    L.pdgemm_gemm_cfg.argtypes = [i, i, i64, i64, i64, p, i64, p, i64, p, i64, p]
+    L.pdgemm_gemm_cfg.restype = i
+    L.pdgemm_strerror.argtypes = [i]
+    L.pdgemm_strerror.restype = ctypes.c_char_p
+    L.pdgemm_pick_config.argtypes = [i, i64, i64, i64]
+    L.pdgemm_config_info.argtypes = [i] + [ctypes.POINTER(i)] * 5
+    return L
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("gemm_f16", "gemm_i8", "gemm_i4", "pdgemm_gemm_cfg", "pdgemm_strerror", "pdgemm_version"):
+        assert n in names
+
+
+def test_every_declared_function_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        getattr(lib, name)  # resolvable through the dynamic loader
+
+
+def test_no_torch_or_oracle_in_the_library():
+    out = subprocess.run(["ldd", LIB], capture_output=True, text=True).stdout
+    assert "torch" not in out and "oracle" not in out
+    out = subprocess.run(["nm", "-D", LIB], capture_output=True, text=True).stdout
+    assert "oracle_" not in out
+
+
+# dummy device pointers: 16-byte aligned, never dereferenced by the host checks
+PA, PB, PC = 0x10000, 0x20000, 0x30000
+
+
+def call(lib, name, M, N, K, A=PA, lda=None, B=PB, ldb=None, C=PC, ldc=None):
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return getattr(lib, name)(M, N, K, A, lda, B, ldb, C, ldc, None)
+
+
+@pytest.mark.parametrize("name", ["gemm_f16", "gemm_i8", "gemm_i4"])
+def test_argument_errors(lib, name):
+    c = codes()
+    assert call(lib, name, -1, 64, 64) == c["PDGEMM_EINVAL_DIM"]
+    assert call(lib, name, 64, -1, 64) == c["PDGEMM_EINVAL_DIM"]
+    assert call(lib, name, 64, 64, -2) == c["PDGEMM_EINVAL_DIM"]
+    assert call(lib, name, 64, 64, 64, lda=32) == c["PDGEMM_EINVAL_LD"]
+    assert call(lib, name, 64, 64, 64, ldb=32) == c["PDGEMM_EINVAL_LD"]
+    assert call(lib, name, 64, 64, 64, ldc=32) == c["PDGEMM_EINVAL_LD"]
+    assert call(lib, name, 64, 64, 64, A=None) == c["PDGEMM_ENULL"]
+    assert call(lib, name, 64, 64, 64, B=None) == c["PDGEMM_ENULL"]
+    assert call(lib, name, 64, 64, 64, C=None) == c["PDGEMM_ENULL"]
+    # misaligned base pointers and leading dimensions
+    assert call(lib, name, 64, 64, 64, A=PA + 2) == c["PDGEMM_EALIGN"]
+    assert call(lib, name, 64, 64, 64, B=PB + 8) == c["PDGEMM_EALIGN"]
+    assert call(lib, name, 64, 64, 64, C=PC + 4) == c["PDGEMM_EALIGN"]
+    assert call(lib, name, 64, 64, 64, ldc=66) == c["PDGEMM_EALIGN"]
+    # empty outputs are a no-op that succeeds without touching HIP
+    assert call(lib, name, 0, 64, 64) == 0
+    assert call(lib, name, 64, 0, 64) == 0
+    assert call(lib, name, 0, 0, 0, A=None, B=None, C=None) == 0
+
+
+def test_alignment_of_leading_dims_per_precision(lib):
+    c = codes()
+    # f16 rows must span multiples of 8 elements, i8 of 16, i4 of 32
+    assert call(lib, "gemm_f16", 64, 64, 60, lda=60) == c["PDGEMM_EALIGN"]
+    assert call(lib, "gemm_i8", 64, 64, 60, lda=60) == c["PDGEMM_EALIGN"]
+    assert call(lib, "gemm_i4", 64, 64, 60, lda=60) == c["PDGEMM_EALIGN"]
+    assert call(lib, "gemm_i4", 64, 64, 48, lda=48) == c["PDGEMM_EALIGN"]
+
+
+def test_int4_specific_errors(lib):
+    c = codes()
+    assert call(lib, "gemm_i4", 64, 64, 63, lda=64, ldb=64) == c["PDGEMM_EINVAL_I4"]
+    assert call(lib, "gemm_i4", 64, 64, 64, lda=65) == c["PDGEMM_EINVAL_I4"]
+    assert call(lib, "gemm_i4", 64, 64, 131072) == c["PDGEMM_EINVAL_DIM"]
+
+
+def test_config_errors_and_info(lib):
+    c = codes()
+    n = lib.pdgemm_num_configs()
+    assert n >= 1
+    assert lib.pdgemm_gemm_cfg(0, n, 64, 64, 64, PA, 64, PB, 64, PC, 64, None) == c["PDGEMM_EINVAL_CFG"]
+    assert lib.pdgemm_gemm_cfg(3, 0, 64, 64, 64, PA, 64, PB, 64, PC, 64, None) == c["PDGEMM_EINVAL_CFG"]
+    assert lib.pdgemm_gemm_cfg(0, -1, 64, 64, 64, PA, 64, PB, 64, PC, 64, None) == c["PDGEMM_EINVAL_CFG"]
+    for cfg in range(n):
+        vals = [ctypes.c_int() for _ in range(5)]
+        assert lib.pdgemm_config_info(cfg, *[ctypes.byref(v) for v in vals]) == 0
+        bm, bn, wm, wn, threads = (v.value for v in vals)
+        assert bm % wm == 0 and bn % wn == 0 and wm % 32 == 0 and wn % 32 == 0
+        assert threads == (bm // wm) * (bn // wn) * 64
+    assert lib.pdgemm_config_info(n, None, None, None, None, None) == c["PDGEMM_EINVAL_CFG"]
+    for prec in (0, 1, 2):
+        for size in (1, 512, 2048, 8192):
+            assert 0 <= lib.pdgemm_pick_config(prec, size, size, size) < n
+    assert lib.pdgemm_pick_config(7, 64, 64, 64) == -1
+
+
+def test_strerror_and_version(lib):
+    for name, code in codes().items():
+        msg = lib.pdgemm_strerror(code)
+        assert msg and len(msg) > 3, name
+    assert lib.pdgemm_strerror(-999)
+    assert lib.pdgemm_version() >= 100
+
+
+def test_binding_imports_and_marshals_without_gpu():
+    import torch
+    import precision_dense_gemm_amd as pd
+    assert pd.version() == pd.lib.pdgemm_version()
+    assert pd.config_info(0)["threads"] > 0
+    with pytest.raises(TypeError):
+        pd.gemm_i8(torch.zeros(4, 4, dtype=torch.float16), torch.zeros(4, 4, dtype=torch.int8))
+    with pytest.raises(ValueError):
+        pd.gemm_i8(torch.zeros(4, 4, dtype=torch.int8), torch.zeros(4, 4, dtype=torch.int8))  # CPU tensors
