@@ -39,10 +39,10 @@
  * |C - sum_k a_ik b_kj| <= 1e-3 * sum_k |a_ik b_kj| for K up to 16384 (the
  * worst-case bound of K fp32 additions, K * 2^-24, stays below 1e-3).
  *
- * Alignment (checked): A, B and C 16-byte aligned; lda, ldb and ldc span a
- * multiple of 16 bytes (f16: lda, ldb % 8 == 0; i8: % 16; i4: % 32;
- * C: ldc % 4 == 0).  M, N and K are otherwise arbitrary: partial tiles are
- * masked inside the kernels.
+ * Alignment (checked): A and B 16-byte aligned, with lda and ldb spanning a
+ * multiple of 16 bytes (f16: lda, ldb % 8 == 0; i8: % 16; i4: % 32); C
+ * 4-byte aligned with any ldc >= N.  M, N and K are otherwise arbitrary:
+ * partial tiles are masked inside the kernels.
  *
  * Ownership and execution: every pointer is device memory owned by the
  * caller.  The library never allocates, frees, copies or synchronizes.  The

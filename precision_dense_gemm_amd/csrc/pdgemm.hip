@@ -384,8 +384,8 @@ int validate(int prec, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     if (!C || (K > 0 && (!A || !B))) return PDGEMM_ENULL;
     const int64_t lda_bytes = lda * elem_bits(prec) / 8;
     const int64_t ldb_bytes = ldb * elem_bits(prec) / 8;
-    if ((lda_bytes & 15) || (ldb_bytes & 15) || ((ldc * 4) & 15)) return PDGEMM_EALIGN;
-    if (((uintptr_t)A & 15) || ((uintptr_t)B & 15) || ((uintptr_t)C & 15)) return PDGEMM_EALIGN;
+    if ((lda_bytes & 15) || (ldb_bytes & 15)) return PDGEMM_EALIGN;
+    if (((uintptr_t)A & 15) || ((uintptr_t)B & 15) || ((uintptr_t)C & 3)) return PDGEMM_EALIGN;
     return PDGEMM_OK;
 }
 
@@ -480,7 +480,7 @@ const char *pdgemm_strerror(int code) {
     case PDGEMM_EINVAL_LD: return "leading dimension smaller than the row length";
     case PDGEMM_ENULL: return "null pointer for an operand with nonzero extent";
     case PDGEMM_EINVAL_I4: return "INT4 K, lda and ldb must be even";
-    case PDGEMM_EALIGN: return "pointers must be 16-byte aligned and rows must span a multiple of 16 bytes";
+    case PDGEMM_EALIGN: return "A and B must be 16-byte aligned with rows spanning a multiple of 16 bytes; C 4-byte aligned";
     case PDGEMM_EINVAL_CFG: return "unknown precision or tile configuration";
     default: return code > 0 ? hipGetErrorString((hipError_t)code) : "unknown error";
     }

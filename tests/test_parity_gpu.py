@@ -209,10 +209,24 @@ def test_misaligned_operand_is_rejected(pd, dev):
     with pytest.raises(pd.PdgemmError) as e:
         pd.gemm_f16(buf[:, 1:65], B)  # base pointer off by 2 bytes
     assert e.value.code == -5
-    out = torch.zeros((64, 66), dtype=torch.float32, device=dev)[:, :64]  # ldc 66: rows not 16-byte multiples
+    pd.gemm_f16(buf[:, :60], B[:, :60])  # lda 72 and ldb 64 are legal with K = 60
+    Bw = torch.zeros((64, 68), dtype=torch.float16, device=dev)  # ldb 68: rows span 136 bytes
     with pytest.raises(pd.PdgemmError) as e:
-        pd.gemm_f16(buf[:, :64], B, out=out)
+        pd.gemm_f16(buf[:, :64], Bw[:, :64])
     assert e.value.code == -5
+
+
+def test_unpadded_output_rows(pd, dev):
+    # C needs no alignment beyond 4 bytes: ldc = N = 70 and an offset view work
+    gu.note("[case] odd ldc")
+    M, N, K = 50, 70, 96
+    A, Bt = synth.operands("i8", M, N, K, 3, 4)
+    buf = torch.full((M, N + 1), -7, dtype=torch.int32, device=dev)
+    out = buf[:, 1:]
+    pd.gemm_i8(torch.from_numpy(A).to(dev), torch.from_numpy(Bt).to(dev), out=out)
+    C = buf.cpu().numpy()
+    assert np.all(C[:, 0] == -7)
+    gu.assert_int_equal(C[:, 1:], gu.oracle_full("i8", A, Bt, K), "odd ldc")
 
 
 # ---------------------------------------------------------------------------
