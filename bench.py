@@ -62,10 +62,48 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0,
-                    help="rows of C per GEMM for the CPU baseline (default: oracle threads)")
+                    help="rows of C per GEMM for the CPU baseline (default 192)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device copy, the reference for HBM counter scaling")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="summarise a rocprofv3 kernel_trace.csv (or counter_collection.csv) "
+                         "per kernel and grid size, then exit (no GPU needed)")
     return ap.parse_args()
+
+
+def trace_summary(path):
+    """Per (kernel, grid) dispatch statistics from rocprofv3 CSV output: durations
+    from a kernel trace, and the mean of every counter from a counter collection."""
+    import csv
+    from collections import defaultdict
+    rows = list(csv.DictReader(open(path)))
+    if not rows:
+        print("no rows")
+        return
+    keys = rows[0].keys()
+    grid = [k for k in ("Grid_Size", "Grid_Size_X") if k in keys]
+    wg = [k for k in ("Workgroup_Size", "Workgroup_Size_X") if k in keys]
+
+    def short(name):
+        return name.replace("(anonymous namespace)::", "").split("(")[0][:110]
+
+    if "Start_Timestamp" in keys:
+        groups = defaultdict(list)
+        for r in rows:
+            g = (short(r["Kernel_Name"]), r[grid[0]] if grid else "?", r[wg[0]] if wg else "?")
+            groups[g].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        print(f"{'calls':>6} {'mean_us':>10} {'min_us':>10} {'max_us':>10} {'grid':>10} {'wg':>5}  kernel")
+        for (name, g, w), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            print(f"{len(d):6d} {np.mean(d):10.2f} {np.min(d):10.2f} {np.max(d):10.2f} {g:>10} {w:>5}  {name}")
+    else:
+        groups = defaultdict(lambda: defaultdict(list))
+        for r in rows:
+            g = (short(r["Kernel_Name"]), r[grid[0]] if grid else "?")
+            groups[g][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        for (name, g), ctrs in groups.items():
+            print(f"grid {g:>10}  {name}")
+            for c, v in sorted(ctrs.items()):
+                print(f"    {c:28s} dispatches {len(v):5d}  mean {np.mean(v):16.1f}")
 
 
 def gemm_ops(n):
@@ -74,6 +112,9 @@ def gemm_ops(n):
 
 def main():
     args = parse()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the GEMM shards by output panels with no exchange; see DESIGN.md)", file=sys.stderr)
@@ -201,7 +242,7 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         threads = oracle.default_threads()
-        rows = args.cpu_rows or max(threads, 16)
+        rows = args.cpu_rows or 192
         total_s = 0.0
         sampled_ops = 0.0
         for prec, n, *_ in work:

@@ -33,7 +33,7 @@ I4_MAX_K = 131071
 if not os.path.exists(LIBRARY):
     raise ImportError(
         f"{LIBRARY} is missing: build the HIP library first "
-        "(python -m precision_dense_gemm_amd.build, or __graft_entry__.build())")
+        "(python precision_dense_gemm_amd/build.py, or __graft_entry__.build())")
 
 lib = ctypes.CDLL(LIBRARY)
 _i64, _p, _i = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int

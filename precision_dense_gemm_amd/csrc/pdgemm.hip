@@ -62,7 +62,7 @@ constexpr int kF16 = PDGEMM_PREC_F16;
 constexpr int kI8 = PDGEMM_PREC_I8;
 constexpr int kI4 = PDGEMM_PREC_I4;
 
-constexpr int kRowBytes = 128;   // LDS bytes per tile row per K tile
+constexpr int kRowBytes = 128;   // bytes of K per tile row per K tile (global and LDS)
 constexpr int kChunks = kRowBytes / 16;
 constexpr int kWave = 64;
 
@@ -70,62 +70,37 @@ template <int P> struct Prec;
 template <> struct Prec<kF16> {
     using Out = float;
     using Acc = floatx16_t;
-    static constexpr int kGlobalRowBytes = 128;  // global bytes per row per K tile
-    static constexpr int kElemsPerTile = 64;     // K elements per K tile
 };
 template <> struct Prec<kI8> {
     using Out = int32_t;
     using Acc = intx16_t;
-    static constexpr int kGlobalRowBytes = 128;
-    static constexpr int kElemsPerTile = 128;
 };
 template <> struct Prec<kI4> {
     using Out = int32_t;
     using Acc = intx16_t;
-    static constexpr int kGlobalRowBytes = 64;
-    static constexpr int kElemsPerTile = 128;
 };
 
-// Physical 16-byte chunk of logical chunk c in LDS row r.
-__device__ __forceinline__ int swz(int c, int r) { return c ^ (r & 7); }
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
-__device__ __forceinline__ uint4 load16(const uint8_t *p) {
-    return *reinterpret_cast<const uint4 *>(p);
+// Buffer resource word 3 for raw (untyped) buffer loads on gfx9-family parts.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ floatx16_t mfma_f16(const uint4 &a, const uint4 &b, const floatx16_t &c) {
+    half8_t av, bv;
+    __builtin_memcpy(&av, &a, 16);
+    __builtin_memcpy(&bv, &b, 16);
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, c, 0, 0, 0);
 }
 
-// The chunk [cb, cb + 16) of a row whose first `valid` bytes are data; bytes
-// at or past `valid` read as zero and are never touched.
-__device__ __forceinline__ uint4 load16_tail(const uint8_t *row, int cb, int valid) {
-    if (cb + 16 <= valid) return load16(row + cb);
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (cb >= valid) return v;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    for (int b = 0; b < 16; ++b)
-        if (cb + b < valid) w[b >> 2] |= (uint32_t)row[cb + b] << (8 * (b & 3));
-    v.x = w[0];
-    v.y = w[1];
-    v.z = w[2];
-    v.w = w[3];
-    return v;
+__device__ __forceinline__ intx16_t mfma_i8(const uint4 &a, const uint4 &b, const intx16_t &c) {
+    intx4_t av, bv;
+    __builtin_memcpy(&av, &a, 16);
+    __builtin_memcpy(&bv, &b, 16);
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, c, 0, 0, 0);
 }
 
-template <int P>
-__device__ __forceinline__ typename Prec<P>::Acc mfma(const uint4 &a, const uint4 &b,
-                                                      const typename Prec<P>::Acc &c) {
-    if constexpr (P == kF16) {
-        half8_t av, bv;
-        __builtin_memcpy(&av, &a, 16);
-        __builtin_memcpy(&bv, &b, 16);
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, c, 0, 0, 0);
-    } else {
-        intx4_t av, bv;
-        __builtin_memcpy(&av, &a, 16);
-        __builtin_memcpy(&bv, &b, 16);
-        return __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, c, 0, 0, 0);
-    }
-}
-
-// The two signed-byte planes of 16 packed INT4 bytes (see the file header).
+// The two signed-byte planes of 16 packed INT4 bytes (see the file header):
+// `even` holds 16*a for the even k, `odd` 16*a for the odd k.
 __device__ __forceinline__ void split_s4(const uint4 &w, uint4 &even, uint4 &odd) {
     const uint32_t m = 0xF0F0F0F0u;
     even.x = (w.x << 4) & m;
@@ -149,27 +124,49 @@ struct Args {
     int tiles_m, tiles_n;
 };
 
+// One workgroup computes a BM x BN block of C with (BM/WM) x (BN/WN) waves.
+//
+// LDS holds two stages; a stage is BM rows of A then BN rows of B, each row
+// 128 bytes of K (64 f16, 128 int8 or 256 packed int4 values) split in eight
+// 16-byte chunks, chunk c of row r stored at position c ^ (r & 7).  A stage is
+// filled by buffer_load_dwordx4 ... lds: each instruction of a wave writes
+// 1 KB = 8 whole rows, lane l landing in row l/8 at position l%8, so lane l
+// fetches logical chunk (l%8) ^ (l/8) of its row.
+//
+// Per K tile a wave runs 4 k-steps; a k-step reads one 16-byte fragment per
+// lane for each of its WM/32 row blocks of A and WN/32 column blocks of B
+// (row = lane%32, 16-byte half = lane/32) and issues the MFMAs on them.
+// Fragments are read one k-step ahead.  The single barrier of a K tile sits
+// before its last k-step: by then every wave has its last fragments in
+// registers (so the stage can be refilled with tile t+2) and the DMA of tile
+// t+1 has landed (so its first fragments can be read while the last k-step's
+// MFMAs run).
 template <int P, int BM, int BN, int WM, int WN, int GM>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Args args) {
+    // The body uses gfx950-only types (buffer resources), which the host
+    // pass cannot type-check; the host pass only needs the launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
     using Acc = typename Prec<P>::Acc;
     using Out = typename Prec<P>::Out;
     constexpr int kWavesN = BN / WN;
-    constexpr int kThreads = (BM / WM) * kWavesN * kWave;
-    constexpr int kGRow = Prec<P>::kGlobalRowBytes;
-    constexpr int kGChunks = kGRow / 16;                 // global chunks per row per K tile
-    constexpr int kLoadsA = BM * kGChunks / kThreads;    // chunks per thread per K tile
-    constexpr int kLoadsB = BN * kGChunks / kThreads;
+    constexpr int NW = (BM / WM) * kWavesN;
+    constexpr int kRows = BM + BN;           // LDS rows per stage
+    constexpr int kDma = kRows / 8 / NW;     // 1 KB DMA instructions per wave per stage
+    constexpr int kDmaA = BM / 8 / NW;       // ... of which fill A rows
     constexpr int FM = WM / 32;
     constexpr int FN = WN / 32;
-    static_assert(BM * kGChunks % kThreads == 0 && BN * kGChunks % kThreads == 0, "tile/threads");
+    static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "stage rows must split evenly over waves");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
 
-    __shared__ uint4 sA[2][BM][kChunks];
-    __shared__ uint4 sB[2][BN][kChunks];
+    // the two stages are separate objects so that the compiler can tell a
+    // DMA into one from fragment reads of the other (no false waits)
+    __shared__ uint4 lds0[kRows][kChunks];
+    __shared__ uint4 lds1[kRows][kChunks];
+    using Stage = uint4[kRows][kChunks];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int M = args.M, N = args.N, K = args.K;
 
     // ---- block id -> tile, XCD-aware and banded by GM block rows ----
@@ -190,72 +187,88 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     const int m0 = tile_m * BM;
     const int n0 = tile_n * BN;
 
-    // ---- global staging assignment: chunk q of the tile -> (row, chunk) ----
-    const uint8_t *a_rows[kLoadsA];
-    const uint8_t *b_rows[kLoadsB];
-    int a_r[kLoadsA], a_c[kLoadsA], b_r[kLoadsB], b_c[kLoadsB];
+    // ---- stage geometry ----
+    // Each lane has one 32-bit offset per DMA instruction: its row (clamped to
+    // the last valid row of A or B) times the leading dimension, plus its
+    // chunk.  K tile t is addressed by a buffer resource based t*128 bytes
+    // further on, whose range ends at the last 16-byte chunk that holds data
+    // of the last valid row: the hardware returns zeros for offsets outside
+    // it without touching memory, so no DMA reads past an operand.  A range
+    // of zero turns a stage past the last K tile into a no-op.
+    const int valid = (P == kF16) ? 2 * K : (P == kI8 ? K : K / 2);  // data bytes per row
+    const int n_tiles = (valid + kRowBytes - 1) / kRowBytes;
+    const int valid16 = (valid + 15) & ~15;
+    const uint8_t *a_base = args.A + (int64_t)m0 * args.lda_bytes;
+    const uint8_t *b_base = args.B + (int64_t)n0 * args.ldb_bytes;
+    const int a_end = (int)((min(BM, M - m0) - 1) * args.lda_bytes) + valid16;
+    const int b_end = (int)((min(BN, N - n0) - 1) * args.ldb_bytes) + valid16;
+    const int lrow = lane >> 3;              // row within the 8-row group
+    const int lpos = lane & 7;               // LDS position written by this lane
+    const int lchunk = lpos ^ lrow;          // logical chunk it fetches
+    uint32_t voff[kDma];
 #pragma unroll
-    for (int i = 0; i < kLoadsA; ++i) {
-        const int q = tid + i * kThreads;
-        a_r[i] = q / kGChunks;
-        a_c[i] = q % kGChunks;
-        const int gr = min(m0 + a_r[i], M - 1);
-        a_rows[i] = args.A + (int64_t)gr * args.lda_bytes;
+    for (int j = 0; j < kDma; ++j) {
+        const int cr = (j * NW + wave) * 8 + lrow;  // row within the stage
+        if (j < kDmaA)
+            voff[j] = (uint32_t)((min(m0 + cr, M - 1) - m0) * args.lda_bytes) + lchunk * 16;
+        else
+            voff[j] = (uint32_t)((min(n0 + cr - BM, N - 1) - n0) * args.ldb_bytes) + lchunk * 16;
     }
-#pragma unroll
-    for (int i = 0; i < kLoadsB; ++i) {
-        const int q = tid + i * kThreads;
-        b_r[i] = q / kGChunks;
-        b_c[i] = q % kGChunks;
-        const int gr = min(n0 + b_r[i], N - 1);
-        b_rows[i] = args.B + (int64_t)gr * args.ldb_bytes;
-    }
-    // valid bytes per row: f16 2K, i8 K, i4 K/2
-    const int valid = (P == kF16) ? 2 * K : (P == kI8 ? K : K / 2);
-    const int n_tiles = (K + Prec<P>::kElemsPerTile - 1) / Prec<P>::kElemsPerTile;
 
-    uint4 ra[kLoadsA], rb[kLoadsB];
+    auto stage = [&](int t, Stage &buf) __attribute__((always_inline)) {
+        const int kb = t * kRowBytes;
+        const bool live = t < n_tiles;
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a_base + kb), (short)0, live ? a_end - kb : 0, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(b_base + kb), (short)0, live ? b_end - kb : 0, kRsrcWord3);
+#pragma unroll
+        for (int j = 0; j < kDma; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kDmaA ? ra : rb,
+                                                     LDS_PTR(&buf[(j * NW + wave) * 8][0]),
+                                                     16, voff[j], 0, 0, 0);
+    };
 
-    auto load_tile = [&](int t) {
-        const int kb = t * kGRow;
-        if (kb + kGRow <= valid) {
+    const int wm0 = (wave / kWavesN) * WM;   // wave's first row / column in the block tile
+    const int wn0 = (wave % kWavesN) * WN;
+    const int frow = lane & 31;              // fragment row (A) / column (B) of this lane
+    const int fhalf = lane >> 5;             // which 16-byte half of a 32-byte k-step
+
+    auto read_frags = [&](const Stage &buf, int s, uint4 (&fa)[FM], uint4 (&fb)[FN]) __attribute__((always_inline)) {
+        const int ch = (2 * s + fhalf) ^ (frow & 7);
 #pragma unroll
-            for (int i = 0; i < kLoadsA; ++i) ra[i] = load16(a_rows[i] + kb + a_c[i] * 16);
+        for (int i = 0; i < FM; ++i) fa[i] = buf[wm0 + i * 32 + frow][ch];
 #pragma unroll
-            for (int i = 0; i < kLoadsB; ++i) rb[i] = load16(b_rows[i] + kb + b_c[i] * 16);
-        } else {
+        for (int j = 0; j < FN; ++j) fb[j] = buf[BM + wn0 + j * 32 + frow][ch];
+    };
+
+    // Zero the bytes of this lane's fragments of K tile t, k-step s, that lie
+    // at or beyond K (the last tile may be partial; what DMA left there is
+    // either zeros or bytes of the row's padding).
+    auto mask_frags = [&](int t, int s, uint4 (&fa)[FM], uint4 (&fb)[FN]) __attribute__((always_inline)) {
+        const int nb = valid - (t * kRowBytes + (2 * s + fhalf) * 16);
+        uint32_t m[4];
 #pragma unroll
-            for (int i = 0; i < kLoadsA; ++i) ra[i] = load16_tail(a_rows[i], kb + a_c[i] * 16, valid);
+        for (int d = 0; d < 4; ++d) {
+            const int r = nb - 4 * d;
+            m[d] = r >= 4 ? 0xFFFFFFFFu : (r <= 0 ? 0u : (1u << (8 * r)) - 1u);
+        }
 #pragma unroll
-            for (int i = 0; i < kLoadsB; ++i) rb[i] = load16_tail(b_rows[i], kb + b_c[i] * 16, valid);
+        for (int i = 0; i < FM; ++i) {
+            fa[i].x &= m[0];
+            fa[i].y &= m[1];
+            fa[i].z &= m[2];
+            fa[i].w &= m[3];
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            fb[j].x &= m[0];
+            fb[j].y &= m[1];
+            fb[j].z &= m[2];
+            fb[j].w &= m[3];
         }
     };
 
-    auto store_tile = [&](int buf) {
-        if constexpr (P == kI4) {
-#pragma unroll
-            for (int i = 0; i < kLoadsA; ++i) {
-                uint4 e, o;
-                split_s4(ra[i], e, o);
-                sA[buf][a_r[i]][swz(2 * a_c[i], a_r[i])] = e;
-                sA[buf][a_r[i]][swz(2 * a_c[i] + 1, a_r[i])] = o;
-            }
-#pragma unroll
-            for (int i = 0; i < kLoadsB; ++i) {
-                uint4 e, o;
-                split_s4(rb[i], e, o);
-                sB[buf][b_r[i]][swz(2 * b_c[i], b_r[i])] = e;
-                sB[buf][b_r[i]][swz(2 * b_c[i] + 1, b_r[i])] = o;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < kLoadsA; ++i) sA[buf][a_r[i]][swz(a_c[i], a_r[i])] = ra[i];
-#pragma unroll
-            for (int i = 0; i < kLoadsB; ++i) sB[buf][b_r[i]][swz(b_c[i], b_r[i])] = rb[i];
-        }
-    };
-
-    // ---- accumulators ----
     Acc acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -264,38 +277,94 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-    const int wm0 = (wave / kWavesN) * WM;   // wave's first row in the block tile
-    const int wn0 = (wave % kWavesN) * WN;
-    const int frow = lane & 31;              // fragment row (A) / column (B) of this lane
-    const int fhalf = lane >> 5;             // which 16-byte half of a 32-byte K step
-
-    if (n_tiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
-
-    for (int t = 0; t < n_tiles; ++t) {
-        const int cur = t & 1;
-        const bool more = t + 1 < n_tiles;
-        if (more) load_tile(t + 1);
-
-#pragma unroll
-        for (int s = 0; s < kChunks / 2; ++s) {
-            const int ch = swz(2 * s + fhalf, frow);
-            uint4 af[FM], bf[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) af[i] = sA[cur][wm0 + i * 32 + frow][ch];
-#pragma unroll
-            for (int j = 0; j < FN; ++j) bf[j] = sB[cur][wn0 + j * 32 + frow][ch];
+    auto mma = [&](const uint4 (&fa)[FM], const uint4 (&fb)[FN]) __attribute__((always_inline)) {
+        if constexpr (P == kF16) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = mfma<P>(af[i], bf[j], acc[i][j]);
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma_f16(fa[i], fb[j], acc[i][j]);
+        } else if constexpr (P == kI8) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma_i8(fa[i], fb[j], acc[i][j]);
+        } else {
+            // planes of all B fragments, then one A fragment at a time; the
+            // even and odd products of one accumulator are FN MFMAs apart
+            uint4 eb[FN], ob[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) split_s4(fb[j], eb[j], ob[j]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                uint4 ea, oa;
+                split_s4(fa[i], ea, oa);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma_i8(ea, eb[j], acc[i][j]);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma_i8(oa, ob[j], acc[i][j]);
+            }
         }
+    };
 
-        if (more) store_tile(cur ^ 1);
+    uint4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+
+    // K tile t (not the last) from stage `cur`; refills `cur` with tile t+2
+    // (a no-op past the last tile) and reads tile t+1's first fragments from
+    // `next` while its last k-step's MFMAs run
+    // (sched_barrier keeps the compiler from sinking the fragment reads and
+    // the DMA issue below the MFMAs they are meant to run under)
+    auto tile = [&](Stage &cur, const Stage &next, int t) __attribute__((always_inline)) {
+        read_frags(cur, 1, fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fa0, fb0);
+        read_frags(cur, 2, fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fa1, fb1);
+        read_frags(cur, 3, fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fa0, fb0);
         __syncthreads();
+        stage(t + 2, cur);
+        read_frags(next, 0, fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fa1, fb1);
+    };
+
+    // the last K tile, with the bytes at or beyond K masked off
+    auto last_tile = [&](const Stage &cur, int t) __attribute__((always_inline)) {
+        mask_frags(t, 0, fa0, fb0);
+        read_frags(cur, 1, fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fa0, fb0);
+        mask_frags(t, 1, fa1, fb1);
+        read_frags(cur, 2, fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fa1, fb1);
+        mask_frags(t, 2, fa0, fb0);
+        read_frags(cur, 3, fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fa0, fb0);
+        mask_frags(t, 3, fa1, fb1);
+        mma(fa1, fb1);
+    };
+
+    if (n_tiles > 0) {
+        stage(0, lds0);
+        __syncthreads();
+        stage(1, lds1);
+        read_frags(lds0, 0, fa0, fb0);
+        int t = 0;
+        for (; t + 2 < n_tiles; t += 2) {
+            tile(lds0, lds1, t);
+            tile(lds1, lds0, t + 1);
+        }
+        if (t + 1 < n_tiles) {
+            tile(lds0, lds1, t);
+            ++t;
+        }
+        last_tile((t & 1) ? lds1 : lds0, t);
+        // no DMA may still be writing this workgroup's LDS when it exits
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
     // ---- epilogue: 32x32 MFMA result layout -> row-major C ----
@@ -320,6 +389,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
             }
         }
     }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 // ---------------------------------------------------------------------------
@@ -351,6 +421,8 @@ const void *kernel_ptr(int cfg) {
     default: return nullptr;
     }
 }
+
+constexpr int64_t kMaxRowBytes = int64_t(1) << 22;  // 4 MiB: a 256-row tile spans at most 1 GiB
 
 int elem_bits(int prec) { return prec == kF16 ? 16 : (prec == kI8 ? 8 : 4); }
 
@@ -385,6 +457,8 @@ int validate(int prec, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     const int64_t lda_bytes = lda * elem_bits(prec) / 8;
     const int64_t ldb_bytes = ldb * elem_bits(prec) / 8;
     if ((lda_bytes & 15) || (ldb_bytes & 15)) return PDGEMM_EALIGN;
+    // operand tiles are addressed with 32-bit offsets from the tile's first row
+    if (lda_bytes > kMaxRowBytes || ldb_bytes > kMaxRowBytes) return PDGEMM_EINVAL_LD;
     if (((uintptr_t)A & 15) || ((uintptr_t)B & 15) || ((uintptr_t)C & 3)) return PDGEMM_EALIGN;
     return PDGEMM_OK;
 }
