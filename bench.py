@@ -87,7 +87,7 @@ def trace_summary(path):
     def short(name):
         return name.replace("(anonymous namespace)::", "").split("(")[0][:110]
 
-    if "Start_Timestamp" in keys:
+    if "Start_Timestamp" in keys and "Counter_Name" not in keys:
         groups = defaultdict(list)
         for r in rows:
             g = (short(r["Kernel_Name"]), r[grid[0]] if grid else "?", r[wg[0]] if wg else "?")
@@ -103,11 +103,32 @@ def trace_summary(path):
         for (name, g), ctrs in groups.items():
             print(f"grid {g:>10}  {name}")
             for c, v in sorted(ctrs.items()):
-                print(f"    {c:28s} dispatches {len(v):5d}  mean {np.mean(v):16.1f}")
+                print(f"    {c:28s} dispatches {len(v):5d}  mean {np.mean(v):18.1f}")
 
 
 def gemm_ops(n):
     return 2.0 * n * n * n
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_n8192_hbm_counters.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "precision_dense_gemm_amd", "csrc", "pdgemm.hip")
+
+
+def measured_traffic(path=TRAFFIC_FILE, source=KERNEL_SOURCE):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
+    keyed "prec:N"; empty when the summary is missing or was taken on another kernel
+    source (its sha256 differs from the current one)."""
+    import hashlib
+    import re
+    try:
+        text = open(path).read()
+        sha = hashlib.sha256(open(source, "rb").read()).hexdigest()
+    except OSError:
+        return {}
+    m = re.search(r"^source_sha256 = ([0-9a-f]{64})$", text, flags=re.M)
+    if not m or m.group(1) != sha:
+        return {}
+    return {k: int(v) for k, v in re.findall(r"^traffic_bytes\[(\w+:\d+)\] = (\d+)$", text, flags=re.M)}
 
 
 def main():
@@ -224,6 +245,11 @@ def main():
         if f"{prec}:{n}" in parity:
             per[f"{prec}:{n}"]["parity"] = parity[f"{prec}:{n}"]
 
+    traffic = measured_traffic()
+    for key, nbytes in traffic.items():
+        if key in per:
+            per[key]["hbm_bytes_profiled"] = nbytes
+
     # dominant kernel: the largest share of a step
     dom = max(per, key=lambda k: per[k]["ms"])
     dprec, dn = dom.split(":")[0], int(dom.split(":")[1])
@@ -234,7 +260,8 @@ def main():
         "peak": PEAK[dprec],
         "unit": "TFLOP/s" if dprec == "f16" else "TOPS",
         "frac": round(per[dom]["tops"] / PEAK[dprec], 4),
-        "traffic": None,
+        # HBM bytes per launch, rocprofv3 counters scaled by a 1 GiB copy
+        "traffic": traffic.get(dom),
     }
 
     # ---- CPU baseline: the oracle on a row sample of every GEMM ----

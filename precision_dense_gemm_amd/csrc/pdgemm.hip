@@ -62,8 +62,9 @@ constexpr int kF16 = PDGEMM_PREC_F16;
 constexpr int kI8 = PDGEMM_PREC_I8;
 constexpr int kI4 = PDGEMM_PREC_I4;
 
-constexpr int kRowBytes = 128;   // bytes of K per tile row per K tile (global and LDS)
+constexpr int kRowBytes = 64;    // bytes of K per row per K tile (global and LDS)
 constexpr int kChunks = kRowBytes / 16;
+constexpr int kStages = 4;       // LDS stages: a K tile is fetched four tiles ahead
 constexpr int kWave = 64;
 
 template <int P> struct Prec;
@@ -84,6 +85,15 @@ template <> struct Prec<kI4> {
 
 // Buffer resource word 3 for raw (untyped) buffer loads on gfx9-family parts.
 constexpr int kRsrcWord3 = 0x00020000;
+
+// LDS position of logical 16-byte chunk c (0..3) of stage row r (64 bytes) is
+// c ^ swizzle(r).  A fragment read has the 16 lanes of a quarter-wave on 16
+// consecutive rows at the same logical chunk.  With 64 four-byte banks, row
+// r's position p covers banks 16*(r%4) + 4p .. +3, so those 16 lanes are
+// conflict-free iff the pairs (r%4, p) are all distinct; with 32 banks, iff
+// any 8 consecutive rows have distinct pairs (r%2, p).
+// ((r >> 1) & 3) ^ ((r >> 3) & 1) satisfies both.
+__device__ __forceinline__ int swizzle(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
 __device__ __forceinline__ floatx16_t mfma_f16(const uint4 &a, const uint4 &b, const floatx16_t &c) {
     half8_t av, bv;
@@ -126,21 +136,23 @@ struct Args {
 
 // One workgroup computes a BM x BN block of C with (BM/WM) x (BN/WN) waves.
 //
-// LDS holds two stages; a stage is BM rows of A then BN rows of B, each row
-// 128 bytes of K (64 f16, 128 int8 or 256 packed int4 values) split in eight
-// 16-byte chunks, chunk c of row r stored at position c ^ (r & 7).  A stage is
-// filled by buffer_load_dwordx4 ... lds: each instruction of a wave writes
-// 1 KB = 8 whole rows, lane l landing in row l/8 at position l%8, so lane l
-// fetches logical chunk (l%8) ^ (l/8) of its row.
+// K is consumed in tiles of 64 bytes per row (32 f16, 64 int8 or 128 packed
+// int4 values).  LDS holds kStages stages; a stage is BM rows of A then BN
+// rows of B, 64 bytes each, in four 16-byte chunks, logical chunk c of row r
+// at position c ^ swizzle(r).  A stage is filled by buffer_load_dwordx4 ...
+// lds: each instruction of a wave writes 1 KB = 16 whole rows, lane l landing
+// in row l/4 at position l%4, so lane l fetches logical chunk
+// (l%4) ^ swizzle(row) of its row.
 //
-// Per K tile a wave runs 4 k-steps; a k-step reads one 16-byte fragment per
-// lane for each of its WM/32 row blocks of A and WN/32 column blocks of B
-// (row = lane%32, 16-byte half = lane/32) and issues the MFMAs on them.
-// Fragments are read one k-step ahead.  The single barrier of a K tile sits
-// before its last k-step: by then every wave has its last fragments in
-// registers (so the stage can be refilled with tile t+2) and the DMA of tile
-// t+1 has landed (so its first fragments can be read while the last k-step's
-// MFMAs run).
+// Tile t lives in stage t % kStages and is fetched kStages tiles before it
+// is consumed.  Per tile a wave runs two k-steps; a k-step reads one 16-byte
+// fragment per lane for each of its WM/32 row blocks of A and WN/32 column
+// blocks of B (row = lane%32, 16-byte half = lane/32) and issues the MFMAs
+// on them; fragments are read one k-step ahead.  The one barrier of a tile
+// comes after its second fragments are in registers: each wave first waits
+// only for its own DMA of tile t+1 (tiles t+2 .. t+kStages-1 stay in
+// flight), so after the barrier tile t+1 is complete in LDS and stage t is
+// free for tile t+kStages.
 template <int P, int BM, int BN, int WM, int WN, int GM>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Args args) {
     // The body uses gfx950-only types (buffer resources), which the host
@@ -151,17 +163,21 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     constexpr int kWavesN = BN / WN;
     constexpr int NW = (BM / WM) * kWavesN;
     constexpr int kRows = BM + BN;           // LDS rows per stage
-    constexpr int kDma = kRows / 8 / NW;     // 1 KB DMA instructions per wave per stage
-    constexpr int kDmaA = BM / 8 / NW;       // ... of which fill A rows
+    constexpr int kDma = kRows / 16 / NW;    // 1 KB DMA instructions per wave per stage
+    constexpr int kDmaA = BM / 16 / NW;      // ... of which fill A rows
     constexpr int FM = WM / 32;
     constexpr int FN = WN / 32;
-    static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "stage rows must split evenly over waves");
+    static_assert((BM / 16) % NW == 0 && (BN / 16) % NW == 0, "stage rows must split evenly over waves");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
+    static_assert(kStages == 4, "the main loop is unrolled for four stages");
+    static_assert((kStages - 2) * kDma <= 63, "vmcnt holds at most 63 outstanding loads");
 
-    // the two stages are separate objects so that the compiler can tell a
-    // DMA into one from fragment reads of the other (no false waits)
+    // The stages are separate objects so that the compiler can tell a DMA
+    // into one from fragment reads of another (no false waits).
     __shared__ uint4 lds0[kRows][kChunks];
     __shared__ uint4 lds1[kRows][kChunks];
+    __shared__ uint4 lds2[kRows][kChunks];
+    __shared__ uint4 lds3[kRows][kChunks];
     using Stage = uint4[kRows][kChunks];
 
     const int tid = threadIdx.x;
@@ -190,7 +206,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     // ---- stage geometry ----
     // Each lane has one 32-bit offset per DMA instruction: its row (clamped to
     // the last valid row of A or B) times the leading dimension, plus its
-    // chunk.  K tile t is addressed by a buffer resource based t*128 bytes
+    // chunk.  K tile t is addressed by a buffer resource based t*64 bytes
     // further on, whose range ends at the last 16-byte chunk that holds data
     // of the last valid row: the hardware returns zeros for offsets outside
     // it without touching memory, so no DMA reads past an operand.  A range
@@ -202,13 +218,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     const uint8_t *b_base = args.B + (int64_t)n0 * args.ldb_bytes;
     const int a_end = (int)((min(BM, M - m0) - 1) * args.lda_bytes) + valid16;
     const int b_end = (int)((min(BN, N - n0) - 1) * args.ldb_bytes) + valid16;
-    const int lrow = lane >> 3;              // row within the 8-row group
-    const int lpos = lane & 7;               // LDS position written by this lane
-    const int lchunk = lpos ^ lrow;          // logical chunk it fetches
+    const int lrow = lane >> 2;              // row within the 16-row group
+    const int lpos = lane & 3;               // LDS position written by this lane
     uint32_t voff[kDma];
 #pragma unroll
     for (int j = 0; j < kDma; ++j) {
-        const int cr = (j * NW + wave) * 8 + lrow;  // row within the stage
+        const int cr = (j * NW + wave) * 16 + lrow;  // row within the stage
+        const int lchunk = lpos ^ swizzle(cr);       // logical chunk this lane fetches
         if (j < kDmaA)
             voff[j] = (uint32_t)((min(m0 + cr, M - 1) - m0) * args.lda_bytes) + lchunk * 16;
         else
@@ -225,7 +241,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
 #pragma unroll
         for (int j = 0; j < kDma; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kDmaA ? ra : rb,
-                                                     LDS_PTR(&buf[(j * NW + wave) * 8][0]),
+                                                     LDS_PTR(&buf[(j * NW + wave) * 16][0]),
                                                      16, voff[j], 0, 0, 0);
     };
 
@@ -235,7 +251,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     const int fhalf = lane >> 5;             // which 16-byte half of a 32-byte k-step
 
     auto read_frags = [&](const Stage &buf, int s, uint4 (&fa)[FM], uint4 (&fb)[FN]) __attribute__((always_inline)) {
-        const int ch = (2 * s + fhalf) ^ (frow & 7);
+        const int ch = (2 * s + fhalf) ^ swizzle(frow);  // fragment rows start at multiples of 32
 #pragma unroll
         for (int i = 0; i < FM; ++i) fa[i] = buf[wm0 + i * 32 + frow][ch];
 #pragma unroll
@@ -308,26 +324,37 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
 
     uint4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
 
-    // K tile t (not the last) from stage `cur`; refills `cur` with tile t+2
-    // (a no-op past the last tile) and reads tile t+1's first fragments from
-    // `next` while its last k-step's MFMAs run
-    // (sched_barrier keeps the compiler from sinking the fragment reads and
-    // the DMA issue below the MFMAs they are meant to run under)
+    // Issue order of a k-step: its MFMAs with the next fragment reads (and,
+    // after the barrier, the DMA of a later tile) slotted one by one between
+    // them, so that no burst of memory instructions holds up MFMA issue.
+    constexpr int kMfma = FM * FN * (P == kI4 ? 2 : 1);   // MFMAs per k-step
+    constexpr int kReads = FM + FN;                       // fragment reads per k-step
+    auto interleave = [&](int dma) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kMfma; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // 1 MFMA
+            if (i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+            if (i < dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // 1 VMEM (DMA)
+            if (P == kI4) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // 2 VALU (planes)
+        }
+    };
+
+    // K tile t (not the last) from stage `cur`, whose first fragments are in
+    // fa0/fb0; refills `cur` with tile t+kStages (a no-op past the last tile)
+    // and reads tile t+1's first fragments from `next`.
     auto tile = [&](Stage &cur, const Stage &next, int t) __attribute__((always_inline)) {
         read_frags(cur, 1, fa1, fb1);
-        __builtin_amdgcn_sched_barrier(0);
         mma(fa0, fb0);
-        read_frags(cur, 2, fa0, fb0);
-        __builtin_amdgcn_sched_barrier(0);
-        mma(fa1, fb1);
-        read_frags(cur, 3, fa1, fb1);
-        __builtin_amdgcn_sched_barrier(0);
-        mma(fa0, fb0);
-        __syncthreads();
-        stage(t + 2, cur);
+        interleave(0);
+        // this wave's DMA of tile t+1 has landed (only tiles t+2 .. t+3 may
+        // still be in flight) and its reads of `cur` are done; after the
+        // barrier the same holds for every wave
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((kStages - 2) * kDma) : "memory");
+        stage(t + kStages, cur);
         read_frags(next, 0, fa0, fb0);
-        __builtin_amdgcn_sched_barrier(0);
         mma(fa1, fb1);
+        interleave(kDma);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // the last K tile, with the bytes at or beyond K masked off
@@ -337,32 +364,33 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
         __builtin_amdgcn_sched_barrier(0);
         mma(fa0, fb0);
         mask_frags(t, 1, fa1, fb1);
-        read_frags(cur, 2, fa0, fb0);
-        __builtin_amdgcn_sched_barrier(0);
-        mma(fa1, fb1);
-        mask_frags(t, 2, fa0, fb0);
-        read_frags(cur, 3, fa1, fb1);
-        __builtin_amdgcn_sched_barrier(0);
-        mma(fa0, fb0);
-        mask_frags(t, 3, fa1, fb1);
         mma(fa1, fb1);
     };
 
     if (n_tiles > 0) {
         stage(0, lds0);
-        __syncthreads();
         stage(1, lds1);
+        stage(2, lds2);
+        stage(3, lds3);
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kStages - 1) * kDma) : "memory");
         read_frags(lds0, 0, fa0, fb0);
         int t = 0;
-        for (; t + 2 < n_tiles; t += 2) {
+        for (; t + kStages < n_tiles; t += kStages) {
             tile(lds0, lds1, t);
-            tile(lds1, lds0, t + 1);
+            tile(lds1, lds2, t + 1);
+            tile(lds2, lds3, t + 2);
+            tile(lds3, lds0, t + 3);
         }
+        // 1 to 4 tiles remain, the first of them in lds0
         if (t + 1 < n_tiles) {
-            tile(lds0, lds1, t);
-            ++t;
+            tile(lds0, lds1, t++);
+            if (t + 1 < n_tiles) {
+                tile(lds1, lds2, t++);
+                if (t + 1 < n_tiles) tile(lds2, lds3, t++);
+            }
         }
-        last_tile((t & 1) ? lds1 : lds0, t);
+        const int last = t & 3;
+        last_tile(last == 0 ? lds0 : last == 1 ? lds1 : last == 2 ? lds2 : lds3, t);
         // no DMA may still be writing this workgroup's LDS when it exits
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }

@@ -1,0 +1,31 @@
+"""Host-side pieces of bench.py that need no GPU."""
+from __future__ import annotations
+
+import subprocess
+import sys
+
+import bench
+
+
+def test_traffic_summary_matches_current_kernel_or_is_ignored(tmp_path):
+    got = bench.measured_traffic()
+    # either the committed summary was taken on this exact kernel source, or it is ignored
+    for key, val in got.items():
+        assert key.count(":") == 1 and val > 0
+    fake = tmp_path / "t.txt"
+    fake.write_text("source_sha256 = " + "0" * 64 + "\ntraffic_bytes[f16:8192] = 5\n")
+    assert bench.measured_traffic(str(fake)) == {}
+
+
+def test_multi_gpu_request_is_refused():
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_trace_summary_of_a_small_trace(tmp_path):
+    csv = tmp_path / "k.csv"
+    csv.write_text('"Kernel_Name","Grid_Size","Workgroup_Size","Start_Timestamp","End_Timestamp"\n'
+                   '"void (anonymous namespace)::gemm_kernel<0, 256, 256, 128, 128, 4>((anonymous namespace)::Args)",262144,256,1000,3000\n'
+                   '"void (anonymous namespace)::gemm_kernel<0, 256, 256, 128, 128, 4>((anonymous namespace)::Args)",262144,256,5000,9000\n')
+    r = subprocess.run([sys.executable, bench.__file__, "--trace-summary", str(csv)], capture_output=True, text=True)
+    assert r.returncode == 0 and "3.00" in r.stdout and "gemm_kernel<0, 256, 256, 128, 128, 4>" in r.stdout
