@@ -41,7 +41,8 @@
  *
  * Alignment (checked): A and B 16-byte aligned, with lda and ldb spanning a
  * multiple of 16 bytes (f16: lda, ldb % 8 == 0; i8: % 16; i4: % 32); C
- * 4-byte aligned with any ldc >= N.  M, N and K are otherwise arbitrary:
+ * 4-byte aligned with any ldc >= N.  A row of A, B or C (lda, ldb, ldc
+ * elements) may span at most 4 MiB.  M, N and K are otherwise arbitrary:
  * partial tiles are masked inside the kernels.
  *
  * Ownership and execution: every pointer is device memory owned by the
@@ -69,7 +70,7 @@ extern "C" {
 
 #define PDGEMM_OK 0
 #define PDGEMM_EINVAL_DIM (-1)  /* M, N or K negative, or gemm_i4 K > 131071 */
-#define PDGEMM_EINVAL_LD (-2)   /* lda < K, ldb < K or ldc < N */
+#define PDGEMM_EINVAL_LD (-2)   /* lda < K, ldb < K, ldc < N, or a row of A, B or C above 4 MiB */
 #define PDGEMM_ENULL (-3)       /* NULL pointer for an operand with nonzero extent */
 #define PDGEMM_EINVAL_I4 (-4)   /* gemm_i4: K, lda or ldb odd */
 #define PDGEMM_EALIGN (-5)      /* a base pointer or leading dimension breaks the alignment rule */

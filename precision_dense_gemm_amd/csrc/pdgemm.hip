@@ -329,13 +329,15 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     // them, so that no burst of memory instructions holds up MFMA issue.
     constexpr int kMfma = FM * FN * (P == kI4 ? 2 : 1);   // MFMAs per k-step
     constexpr int kReads = FM + FN;                       // fragment reads per k-step
+    // INT4 plane split: 3 VALU per packed dword, 12 per fragment
+    constexpr int kValu = P == kI4 ? (12 * kReads + kMfma - 1) / kMfma : 0;
     auto interleave = [&](int dma) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < kMfma; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // 1 MFMA
             if (i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
             if (i < dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // 1 VMEM (DMA)
-            if (P == kI4) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // 2 VALU (planes)
+            if (kValu) __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU (planes)
         }
     };
 
@@ -396,26 +398,44 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     }
 
     // ---- epilogue: 32x32 MFMA result layout -> row-major C ----
-    // Register e of lane l holds row 8*(e/4) + 4*(l/32) + e%4, column l%32.
-    Out *C = reinterpret_cast<Out *>(args.C);
+    // Register e of lane l in MFMA block (i, j) holds row
+    // i*32 + 8*(e/4) + 4*(l/32) + e%4 and column j*32 + l%32 of the wave's
+    // tile.  Row offsets are wave-uniform (scalar registers); each lane adds
+    // one 32-bit offset, so a store costs no vector address arithmetic.
+    {
+        char *const wave_c = reinterpret_cast<char *>(args.C) +
+                             ((int64_t)(m0 + wm0) * args.ldc + n0 + wn0) * (int64_t)sizeof(Out);
+        const int64_t row_bytes = args.ldc * (int64_t)sizeof(Out);
+        const uint32_t lane_off = (uint32_t)(4 * fhalf * row_bytes) + frow * (uint32_t)sizeof(Out);
+        const bool interior = m0 + BM <= M && n0 + BN <= N;
+        const int rows_left = M - (m0 + wm0) - 4 * fhalf;  // rows this lane may write: r < rows_left
+        const int cols_left = N - (n0 + wn0) - frow;        // columns: j*32 < cols_left
+        auto store_all = [&](auto &&keep) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+            for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = n0 + wn0 + j * 32 + frow;
+                for (int e = 0; e < 16; ++e) {
+                    const int r = i * 32 + 8 * (e >> 2) + (e & 3);   // wave-uniform part of the row
+                    char *const row_c = wave_c + r * row_bytes;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = m0 + wm0 + i * 32 + 8 * (e >> 2) + 4 * fhalf + (e & 3);
-                if (row < M && col < N) {
-                    Out v;
-                    if constexpr (P == kI4)
-                        v = acc[i][j][e] >> 8;
-                    else
-                        v = acc[i][j][e];
-                    C[(int64_t)row * args.ldc + col] = v;
+                    for (int j = 0; j < FN; ++j) {
+                        Out v;
+                        if constexpr (P == kI4)
+                            v = acc[i][j][e] >> 8;
+                        else
+                            v = acc[i][j][e];
+                        if (keep(r, j))
+                            *reinterpret_cast<Out *>(row_c + lane_off + j * 32 * (int)sizeof(Out)) = v;
+                    }
                 }
+                // one row block at a time keeps accumulator reads from piling up
+                __builtin_amdgcn_sched_barrier(0);
             }
-        }
+        };
+        if (interior)
+            store_all([](int, int) { return true; });
+        else
+            store_all([&](int r, int j) { return r < rows_left && j * 32 < cols_left; });
     }
 #endif  // __HIP_DEVICE_COMPILE__
 }
@@ -486,7 +506,7 @@ int validate(int prec, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     const int64_t ldb_bytes = ldb * elem_bits(prec) / 8;
     if ((lda_bytes & 15) || (ldb_bytes & 15)) return PDGEMM_EALIGN;
     // operand tiles are addressed with 32-bit offsets from the tile's first row
-    if (lda_bytes > kMaxRowBytes || ldb_bytes > kMaxRowBytes) return PDGEMM_EINVAL_LD;
+    if (lda_bytes > kMaxRowBytes || ldb_bytes > kMaxRowBytes || ldc * 4 > kMaxRowBytes) return PDGEMM_EINVAL_LD;
     if (((uintptr_t)A & 15) || ((uintptr_t)B & 15) || ((uintptr_t)C & 3)) return PDGEMM_EALIGN;
     return PDGEMM_OK;
 }
