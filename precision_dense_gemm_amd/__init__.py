@@ -101,17 +101,21 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _call(prec, A, Bt, out, K, lda, ldb, stream, cfg):
+def _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg):
+    """The C function and its argument tuple for one GEMM."""
     M, N = A.shape[0], Bt.shape[0]
     ldc = _row_major_2d(out, "out")
     if tuple(out.shape) != (M, N):
         raise ValueError(f"out must have shape {(M, N)}")
     args = (M, N, K, A.data_ptr(), lda, Bt.data_ptr(), ldb, out.data_ptr(), ldc, _stream(stream))
     if cfg is None:
-        fn = (lib.gemm_f16, lib.gemm_i8, lib.gemm_i4)[prec]
-        rc = fn(*args)
-    else:
-        rc = lib.pdgemm_gemm_cfg(prec, cfg, *args)
+        return (lib.gemm_f16, lib.gemm_i8, lib.gemm_i4)[prec], args
+    return lib.pdgemm_gemm_cfg, (prec, cfg) + args
+
+
+def _call(prec, A, Bt, out, K, lda, ldb, stream, cfg):
+    fn, args = _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg)
+    rc = fn(*args)
     if rc != 0:
         raise PdgemmError(rc)
     return out
@@ -164,3 +168,44 @@ def gemm_i4(A: torch.Tensor, Bt: torch.Tensor, K: int | None = None,
     elif out.dtype != torch.int32:
         raise TypeError("gemm_i4 writes an int32 output")
     return _call(PREC_I4, A, Bt, out, K, lda, ldb, stream, cfg)
+
+
+def prepare(prec: str, A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor, K: int | None = None,
+            stream=None, cfg: int | None = None):
+    """Check and marshal one GEMM once; return a no-argument callable that
+    enqueues it again (on the stream current now) through the C ABI.
+
+    For repeated launches of the same operands, e.g. timing loops: the
+    callable skips the per-call Python checks, so host time stays far below
+    the kernel time even for small shapes.  The tensors must stay alive.
+    """
+    if prec == "f16":
+        if A.dtype != torch.float16 or Bt.dtype != torch.float16 or out.dtype != torch.float32:
+            raise TypeError("f16 takes float16 operands and a float32 output")
+        K = A.shape[1] if K is None else K
+        lda, ldb, p = _row_major_2d(A, "A"), _row_major_2d(Bt, "Bt"), PREC_F16
+    elif prec == "i8":
+        if A.dtype != torch.int8 or Bt.dtype != torch.int8 or out.dtype != torch.int32:
+            raise TypeError("i8 takes int8 operands and an int32 output")
+        K = A.shape[1] if K is None else K
+        lda, ldb, p = _row_major_2d(A, "A"), _row_major_2d(Bt, "Bt"), PREC_I8
+    elif prec == "i4":
+        if A.dtype != torch.uint8 or Bt.dtype != torch.uint8 or out.dtype != torch.int32:
+            raise TypeError("i4 takes uint8 packed operands and an int32 output")
+        K = 2 * A.shape[1] if K is None else K
+        lda, ldb, p = 2 * _row_major_2d(A, "A"), 2 * _row_major_2d(Bt, "Bt"), PREC_I4
+    else:
+        raise ValueError(f"unknown precision {prec!r}")
+    if A.shape[1] * (2 if prec == "i4" else 1) < K or Bt.shape[1] * (2 if prec == "i4" else 1) < K:
+        raise ValueError("operands hold fewer than K values per row")
+    fn, args = _marshal(p, A, Bt, out, K, lda, ldb, stream, cfg)
+    rc = fn(*args)  # validates the arguments once, and is a first launch
+    if rc != 0:
+        raise PdgemmError(rc)
+
+    def launch():
+        rc = fn(*args)
+        if rc != 0:
+            raise PdgemmError(rc)
+
+    return launch

@@ -287,3 +287,21 @@ def test_workload_full_size(pd, dev, name, prec, n, dist, cfg_id):
         gu.freivalds_f16(A, Bt, K, C, seed=n)
     else:
         gu.freivalds_int(prec, A, Bt, K, C, seed=n)
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_prepared_launch_matches_plain_call(pd, dev, prec):
+    M, N, K = 300, 260, 512
+    gu.note(f"[case] {prec} prepared launch")
+    A, Bt = synth.operands(prec, M, N, K, 21, 22)
+    Ad, Bd = torch.from_numpy(A).to(dev), torch.from_numpy(Bt).to(dev)
+    out_dtype = torch.float32 if prec == "f16" else torch.int32
+    ref = torch.empty((M, N), dtype=out_dtype, device=dev)
+    f = {"f16": pd.gemm_f16, "i8": pd.gemm_i8, "i4": lambda a, b, out: pd.gemm_i4(a, b, K, out=out)}[prec]
+    f(Ad, Bd, out=ref)
+    out = torch.full((M, N), -1, dtype=out_dtype, device=dev)
+    go = pd.prepare(prec, Ad, Bd, out, K=K)
+    for _ in range(3):
+        go()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
