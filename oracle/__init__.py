@@ -61,6 +61,10 @@ def _load():
         lib.oracle_entries_f16.argtypes = [i64, p, i64, p, i64, i64, p, p, p, p]
         lib.oracle_entries_i8.argtypes = [i64, p, i64, p, i64, i64, p, p, p]
         lib.oracle_entries_i4.argtypes = [i64, p, i64, p, i64, i64, p, p, p]
+        lib.oracle_float_to_half.argtypes = [ctypes.c_float]
+        lib.oracle_float_to_half.restype = ctypes.c_uint16
+        lib.oracle_dequant.argtypes = [i64, i64, p, i64, p, p, p, i64, i32]
+        lib.oracle_dequant.restype = i32
         for f in (lib.oracle_gemm_f16, lib.oracle_gemm_i8, lib.oracle_gemm_i4,
                   lib.oracle_entries_f16, lib.oracle_entries_i8, lib.oracle_entries_i4):
             f.restype = i32
@@ -176,3 +180,24 @@ def entries_i4(Ap, Btp, rows, cols, K=None):
 def fp16_bound(R, S, rel=1e-3):
     """Per-element tolerance of the FP16 path: rel * S (fp64 summation error is far below)."""
     return rel * S
+
+
+def float_to_half(x: float) -> int:
+    """binary32 value -> binary16 bits (round to nearest even), the oracle's own conversion."""
+    return int(_load().oracle_float_to_half(x))
+
+
+def dequant(S, scale_a, scale_b, half_out=False):
+    """C[i][j] = ((float)S[i][j] * scale_a[i]) * scale_b[j] in binary32, optionally rounded to
+    binary16.  S is an int64 (M, N) array of exact integer sums.  Returns float32, or float16
+    when half_out."""
+    S, ps = _c(S, np.int64)
+    sa, pa = _c(scale_a, np.float32)
+    sb, pb = _c(scale_b, np.float32)
+    M, N = S.shape
+    if sa.shape != (M,) or sb.shape != (N,):
+        raise ValueError("scale_a must hold M values and scale_b N values")
+    C = np.zeros((M, N), np.uint16 if half_out else np.float32)
+    _check(_load().oracle_dequant(M, N, ps, N, pa, pb, C.ctypes.data_as(ctypes.c_void_p), N,
+                                  1 if half_out else 0))
+    return C.view(np.float16) if half_out else C

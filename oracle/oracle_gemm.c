@@ -42,6 +42,7 @@
 #include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #define ORACLE_OK 0
 #define ORACLE_EINVAL (-1)
@@ -250,5 +251,86 @@ int oracle_entries_i4(int64_t K, const uint8_t *A, int64_t lda, const uint8_t *B
             acc += (int64_t)s4_at(a, k) * (int64_t)s4_at(b, k);
         C[t] = acc;
     }
+    return ORACLE_OK;
+}
+
+/* ----------------------------------------------------------------------- */
+/* Dequantizing epilogue for the integer products.                          */
+/*                                                                          */
+/* The paper ("Hand-Written PTX Tensor-Core GEMM Kernels ...", Section VI)  */
+/* returns INT32 sums without dequantization or scaling; this is the step   */
+/* that follows it in an inference pipeline.  The library's definition is   */
+/*     C[i][j] = ((float)S_ij * scale_a[i]) * scale_b[j]                    */
+/* in IEEE binary32 arithmetic (round to nearest even, in that order), then */
+/* optionally rounded to binary16 (round to nearest even, overflow to inf). */
+/* S_ij is the exact integer sum computed above.                            */
+
+/* binary32 -> binary16 bits, round to nearest even, from the formats'
+ * definitions (no library conversion). */
+uint16_t oracle_float_to_half(float f)
+{
+    uint32_t x;
+    memcpy(&x, &f, 4);
+    uint32_t sign = (x >> 16) & 0x8000u;
+    int expo = (int)((x >> 23) & 0xff);
+    uint32_t mant = x & 0x7fffffu;
+    if (expo == 0xff)                              /* inf or NaN */
+        return (uint16_t)(sign | 0x7c00u | (mant ? 0x200u : 0u));
+    int e = expo - 127;                            /* unbiased exponent */
+    if (e > 15)
+        return (uint16_t)(sign | 0x7c00u);         /* overflow */
+    uint32_t sig = mant | (expo ? 0x800000u : 0u); /* 24-bit significand */
+    /* value = sig * 2^(e - 23); a half keeps 11 significant bits, or fewer
+     * below 2^-14 (subnormals, quantum 2^-24) */
+    int shift;
+    if (e >= -14)
+        shift = 13;                                /* keep the top 11 of 24 bits */
+    else
+        shift = 13 + (-14 - e);                    /* subnormal: quantum 2^-24 */
+    if (expo == 0 || shift > 24 + 1)
+        return (uint16_t)sign;                     /* below half of the smallest subnormal */
+    uint32_t q = sig >> shift;
+    uint32_t rem = sig & ((1u << shift) - 1u);
+    uint32_t half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (q & 1u)))
+        q += 1u;                                   /* round to nearest, ties to even */
+    if (e >= -14) {
+        /* q in [2^10, 2^11]; a carry to 2^11 moves to the next binade */
+        int he = e + 15;
+        if (q == 0x800u) {
+            q = 0x400u;
+            he += 1;
+        }
+        if (he >= 31)
+            return (uint16_t)(sign | 0x7c00u);
+        return (uint16_t)(sign | ((uint32_t)he << 10) | (q & 0x3ffu));
+    }
+    /* subnormal: q counts 2^-24; q == 2^10 is the smallest normal */
+    return (uint16_t)(sign | q);
+}
+
+static float dequant(int64_t s, float sa, float sb)
+{
+    volatile float c = (float)s; /* volatile: one binary32 rounding per step */
+    c = c * sa;
+    c = c * sb;
+    return c;
+}
+
+/* Dequantize int64 sums S (M x N, row stride lds) into C: binary32 when
+ * half_out == 0 (C is float*), binary16 bits when half_out != 0 (uint16_t*). */
+int oracle_dequant(int64_t M, int64_t N, const int64_t *S, int64_t lds, const float *scale_a,
+                   const float *scale_b, void *C, int64_t ldc, int half_out)
+{
+    if (M < 0 || N < 0)
+        return ORACLE_EINVAL;
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            float c = dequant(S[i * lds + j], scale_a[i], scale_b[j]);
+            if (half_out)
+                ((uint16_t *)C)[i * ldc + j] = oracle_float_to_half(c);
+            else
+                ((float *)C)[i * ldc + j] = c;
+        }
     return ORACLE_OK;
 }

@@ -253,8 +253,62 @@ def pin_invariants():
     assert np.array_equal(oracle.gemm_i4(B4, A4), C4.T)
 
 
+def pin_half_rounding():
+    """binary32 -> binary16 (round to nearest even) against numpy's IEEE conversion."""
+    # every binary16 value converts to itself
+    halves = np.arange(65536, dtype=np.uint16).view(np.float16)
+    finite = halves[np.isfinite(halves)]
+    got = np.array([oracle.float_to_half(float(np.float32(h))) for h in finite], np.uint16)
+    assert np.array_equal(got, finite.view(np.uint16))
+    # every midpoint between consecutive positive binary16 values (exact in binary32): ties to even
+    pos = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    for m in np.concatenate([mids, -mids]):
+        assert oracle.float_to_half(float(m)) == np.float32(m).astype(np.float16).view(np.uint16), m
+    # random binary32 values across the whole binary16 range, subnormals and overflow
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(200000) * np.exp2(rng.uniform(-30, 17, 200000))).astype(np.float32)
+    x = np.concatenate([x, np.float32([65504, 65519.996, 65520, 65536, 1e30, -1e30, 2 ** -24, 2 ** -25,
+                                       2 ** -26, 3 * 2 ** -26, 1e-30, 0.0, -0.0])])
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.float_to_half(float(v)) for v in x], np.uint16)
+    assert np.array_equal(got, want)
+
+
+def pin_dequant():
+    """The dequantizing epilogue: ((float)S * scale_a[i]) * scale_b[j] in binary32."""
+    rng = np.random.default_rng(9)
+    M, N = 7, 5
+    S = rng.integers(-2 ** 31, 2 ** 31, (M, N), dtype=np.int64)
+    # unit scales give the sum rounded to binary32
+    C = oracle.dequant(S, np.ones(M, np.float32), np.ones(N, np.float32))
+    assert np.array_equal(C, S.astype(np.float32))
+    # power-of-two scales are exact on sums below 2^24
+    Ss = rng.integers(-2 ** 24, 2 ** 24, (M, N), dtype=np.int64)
+    ea = rng.integers(-20, 20, M)
+    eb = rng.integers(-20, 20, N)
+    C = oracle.dequant(Ss, np.exp2(ea).astype(np.float32), np.exp2(eb).astype(np.float32))
+    assert np.array_equal(C.astype(np.float64), Ss * np.exp2(ea)[:, None] * np.exp2(eb)[None, :])
+    # arbitrary scales: the same three binary32 roundings, in the same order, done by numpy
+    sa = rng.uniform(1e-3, 4, M).astype(np.float32)
+    sb = rng.uniform(1e-3, 4, N).astype(np.float32)
+    C = oracle.dequant(S, sa, sb)
+    want = (S.astype(np.float32) * sa[:, None]) * sb[None, :]
+    assert want.dtype == np.float32 and np.array_equal(C, want)
+    # and within three roundings of the exact real product
+    exact = S.astype(np.float64) * sa.astype(np.float64)[:, None] * sb.astype(np.float64)[None, :]
+    assert np.all(np.abs(C - exact) <= 3 * 2.0 ** -24 * np.abs(exact))
+    # binary16 output: the binary32 result rounded once more
+    Sm = rng.integers(-2 ** 20, 2 ** 20, (M, N), dtype=np.int64)
+    Ch = oracle.dequant(Sm, sa * 1e-3, sb, half_out=True)
+    wanth = ((Sm.astype(np.float32) * (sa * np.float32(1e-3))[:, None]) * sb[None, :]).astype(np.float16)
+    assert Ch.dtype == np.float16 and np.array_equal(Ch.view(np.uint16), wanth.view(np.uint16))
+
+
 PINS = [pin_half_decoder, pin_mma_lab_f16, pin_mma_lab_integer, pin_closed_forms,
-        pin_identities, pin_brute_force_tiny, pin_product_tables, pin_invariants]
+        pin_identities, pin_brute_force_tiny, pin_product_tables, pin_invariants,
+        pin_half_rounding, pin_dequant]
 
 
 # --------------------------------------------------------------------------

@@ -33,6 +33,12 @@ MUTANTS = {
     "subtract_product": ("acc += prod;\n                mag", "acc -= prod;\n                mag"),
     "f16_B_uses_lda": ("const uint16_t *b = (const uint16_t *)jb->B + j * jb->ldb;",
                        "const uint16_t *b = (const uint16_t *)jb->B + j * jb->lda;"),
+    "dequant_swapped_scales": ("float c = dequant(S[i * lds + j], scale_a[i], scale_b[j]);",
+                               "float c = dequant(S[i * lds + j], scale_a[j % M], scale_b[i % N]);"),
+    "dequant_scale_product_first": ("    c = c * sa;\n    c = c * sb;", "    c = c * (sa * sb);"),
+    "half_truncates": ("    if (rem > half || (rem == half && (q & 1u)))\n        q += 1u;", ""),
+    "half_ties_away": ("(rem == half && (q & 1u))", "(rem == half)"),
+    "half_no_binade_carry": ("        if (q == 0x800u) {\n            q = 0x400u;\n            he += 1;\n        }", ""),
     "entries_swap_rc": ("const int8_t *a = A + rows[t] * lda;\n        const int8_t *b = B + cols[t] * ldb;",
                         "const int8_t *a = A + cols[t] * lda;\n        const int8_t *b = B + rows[t] * ldb;"),
 }
