@@ -14,6 +14,10 @@ HBM before the timed region starts.  The JSON line reports:
                 MFMA peak of its own precision
   cpu_baseline  the CPU oracle (plain triple loop) timed on a row sample of
                 every GEMM of the sweep and scaled to whole GEMMs
+  dequant       (outside the step) the INT8 / INT4 GEMMs at N = 8192 with the
+                dequantizing epilogue, ((float)S * scale_a[i]) * scale_b[j]
+                rounded to binary16, timed back to back alternately with the
+                plain GEMM (medians of 3), with a bit-exact sampled parity check
 
 Usage: python bench.py [--steps K] [--warmup W] [--case f16:8192] [--calib-copy]
 """
@@ -62,6 +66,8 @@ def parse():
                     help="time only prec:N (repeatable), e.g. f16:8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-dequant", action="store_true",
+                    help="skip the dequantizing-epilogue measurement")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of C per GEMM for the CPU baseline (default 192)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -249,6 +255,60 @@ def main():
         e0.synchronize()
         b2b[(prec, n)] = s0.elapsed_time(e0) / reps
 
+    def time_b2b(go, est_ms):
+        reps = int(min(200, max(5, 2.0 / max(est_ms, 1e-3))))
+        go()
+        s0 = torch.cuda.Event(enable_timing=True)
+        e0 = torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for _ in range(reps):
+            go()
+        e0.record(stream)
+        e0.synchronize()
+        return s0.elapsed_time(e0) / reps
+
+    # ---- the dequantizing epilogue at N = 8192 (not part of the step) ----
+    dequant = {}
+    if not args.no_dequant:
+        for prec, n, Ad, Bd, C in work:
+            if prec == "f16" or n != 8192:
+                continue
+            sa_h = synth.f32_scales(n, synth.config_seed(SWEEP_CFG_ID, n, synth.OPERAND_A) + 2)
+            sb_h = synth.f32_scales(n, synth.config_seed(SWEEP_CFG_ID, n, synth.OPERAND_B) + 3)
+            sad, sbd = torch.from_numpy(sa_h).to(dev), torch.from_numpy(sb_h).to(dev)
+            Ch = torch.empty((n, n), dtype=torch.float16, device=dev)
+            go = pd.prepare(prec, Ad, Bd, Ch, K=n, scales=(sad, sbd))
+            torch.cuda.synchronize()
+            entry = {"out": "f16"}
+            if not args.no_parity:
+                import oracle
+                A, Bt = host[(prec, n)]
+                rng = np.random.default_rng(n + 1)
+                rows, cols = rng.integers(0, n, 256), rng.integers(0, n, 256)
+                S = (oracle.entries_i8 if prec == "i8" else oracle.entries_i4)(A, Bt, rows, cols)
+                want = oracle.dequant_entries(S, sa_h[rows], sb_h[cols], half_out=True)
+                got = Ch.cpu().numpy()[rows, cols]
+                ok = bool(np.array_equal(got.view(np.uint16), want.view(np.uint16)))
+                entry["parity"] = ok
+                parity[f"{prec}:{n}:dequant"] = ok
+                log(f"[bench] parity {prec} N={n} dequant->f16: {'ok' if ok else 'FAIL'}")
+            # alternate the two so that clock and power drift hit both alike
+            ds, rs = [], []
+            for _ in range(3):
+                ds.append(time_b2b(go, b2b[(prec, n)]))
+                rs.append(time_b2b(launchers[(prec, n)], b2b[(prec, n)]))
+            ms_d, ms_r = float(np.median(ds)), float(np.median(rs))
+            entry.update({
+                "ms_back_to_back": round(ms_d, 5),
+                "tops_back_to_back": round(gemm_ops(n) / (ms_d * 1e-3) / 1e12, 2),
+                "frac_of_peak": round(gemm_ops(n) / (ms_d * 1e-3) / 1e12 / PEAK[prec], 4),
+                "plain_ms_back_to_back": round(ms_r, 5),
+                "time_vs_plain": round(ms_d / ms_r, 4),
+            })
+            dequant[f"{prec}:{n}"] = entry
+            log(f"[bench] dequant {prec} N={n}: {ms_d:.4f} ms (plain {ms_r:.4f} ms)")
+            del Ch, sad, sbd
+
     per = {}
     for (prec, n), pairs in ev.items():
         ms = float(np.mean([s.elapsed_time(e) for s, e in pairs])) if pairs else float("nan")
@@ -347,6 +407,7 @@ def main():
         "per_gemm": per,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "dequant": dequant or None,
     }
     print(json.dumps(out), flush=True)
     if parity and not all(parity.values()):

@@ -73,8 +73,8 @@ extern "C" {
 #define PDGEMM_EINVAL_LD (-2)   /* lda < K, ldb < K, ldc < N, or a row of A, B or C above 4 MiB */
 #define PDGEMM_ENULL (-3)       /* NULL pointer for an operand with nonzero extent */
 #define PDGEMM_EINVAL_I4 (-4)   /* gemm_i4: K, lda or ldb odd */
-#define PDGEMM_EALIGN (-5)      /* a base pointer or leading dimension breaks the alignment rule */
-#define PDGEMM_EINVAL_CFG (-6)  /* pdgemm_gemm_cfg: unknown precision or tile configuration */
+#define PDGEMM_EALIGN (-5)      /* a pointer or leading dimension breaks the alignment rules */
+#define PDGEMM_EINVAL_CFG (-6)  /* unknown precision or tile configuration; dequantizing FP16 */
 
 #define PDGEMM_I4_MAX_K 131071
 
@@ -91,6 +91,31 @@ int gemm_i8(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
 int gemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
             const uint8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream);
 
+/* INT8 / INT4 GEMM followed by a dequantizing epilogue.
+ *
+ * The paper ("Hand-Written PTX Tensor-Core GEMM Kernels ...", Section VI)
+ * stops at the INT32 sums and leaves dequantization out; this is the step an
+ * inference pipeline applies next.  With S the exact integer sum of gemm_i8 /
+ * gemm_i4,
+ *     C[i][j] = ((float)S[i][j] * scale_a[i]) * scale_b[j]
+ * evaluated in IEEE binary32 in that order (each step rounded to nearest
+ * even), then stored as binary32 (out_f16 = 0; C is float*) or rounded once
+ * more to binary16 (out_f16 = 1; C holds binary16 bit patterns, overflow
+ * gives infinity).  The result is unique, so it is reproducible bit for bit.
+ * scale_a holds M floats (one per row of A), scale_b N floats (one per
+ * column of B), both 4-byte aligned device memory owned by the caller and
+ * only read.  K = 0 gives (0 * scale_a[i]) * scale_b[j] (a signed zero, or
+ * NaN for an infinite scale).  C is 4-byte aligned for binary32 output and
+ * 2-byte aligned for binary16; ldc counts output elements.  Other arguments,
+ * layouts and errors as gemm_i8 / gemm_i4; a null scale pointer with
+ * M, N > 0 returns PDGEMM_ENULL. */
+int gemm_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
+                    const int8_t *B, int64_t ldb, const float *scale_a, const float *scale_b,
+                    void *C, int64_t ldc, int out_f16, void *stream);
+int gemm_i4_dequant(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+                    const uint8_t *B, int64_t ldb, const float *scale_a, const float *scale_b,
+                    void *C, int64_t ldc, int out_f16, void *stream);
+
 /* Precision ids and tile configurations, for the calls below. */
 #define PDGEMM_PREC_F16 0
 #define PDGEMM_PREC_I8 1
@@ -103,6 +128,12 @@ int gemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
 int pdgemm_gemm_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K,
                     const void *A, int64_t lda, const void *B, int64_t ldb,
                     void *C, int64_t ldc, void *stream);
+
+/* The dequantizing GEMM with an explicit tile configuration (prec is
+ * PDGEMM_PREC_I8 or PDGEMM_PREC_I4; FP16 returns PDGEMM_EINVAL_CFG). */
+int pdgemm_dequant_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K, const void *A,
+                       int64_t lda, const void *B, int64_t ldb, const float *scale_a,
+                       const float *scale_b, void *C, int64_t ldc, int out_f16, void *stream);
 
 /* Number of tile configurations, and the one the entry points pick for a
  * shape (-1 for an unknown precision). */

@@ -49,7 +49,7 @@ def default_threads() -> int:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIBRARY):
+        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
             build()
         lib = ctypes.CDLL(LIBRARY)
         i64, p, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
@@ -65,6 +65,8 @@ def _load():
         lib.oracle_float_to_half.restype = ctypes.c_uint16
         lib.oracle_dequant.argtypes = [i64, i64, p, i64, p, p, p, i64, i32]
         lib.oracle_dequant.restype = i32
+        lib.oracle_dequant_entries.argtypes = [i64, p, p, p, p, i32]
+        lib.oracle_dequant_entries.restype = i32
         for f in (lib.oracle_gemm_f16, lib.oracle_gemm_i8, lib.oracle_gemm_i4,
                   lib.oracle_entries_f16, lib.oracle_entries_i8, lib.oracle_entries_i4):
             f.restype = i32
@@ -200,4 +202,18 @@ def dequant(S, scale_a, scale_b, half_out=False):
     C = np.zeros((M, N), np.uint16 if half_out else np.float32)
     _check(_load().oracle_dequant(M, N, ps, N, pa, pb, C.ctypes.data_as(ctypes.c_void_p), N,
                                   1 if half_out else 0))
+    return C.view(np.float16) if half_out else C
+
+
+def dequant_entries(S, scale_a, scale_b, half_out=False):
+    """Elementwise form of dequant: C[t] = ((float)S[t] * scale_a[t]) * scale_b[t] for
+    equal-length 1-D arrays (the row and column scale of each listed entry)."""
+    S, ps = _c(S, np.int64)
+    sa, pa = _c(scale_a, np.float32)
+    sb, pb = _c(scale_b, np.float32)
+    if S.ndim != 1 or sa.shape != S.shape or sb.shape != S.shape:
+        raise ValueError("S, scale_a and scale_b must be 1-D and of equal length")
+    C = np.zeros(S.shape, np.uint16 if half_out else np.float32)
+    _check(_load().oracle_dequant_entries(S.size, ps, pa, pb, C.ctypes.data_as(ctypes.c_void_p),
+                                          1 if half_out else 0))
     return C.view(np.float16) if half_out else C

@@ -334,3 +334,20 @@ int oracle_dequant(int64_t M, int64_t N, const int64_t *S, int64_t lds, const fl
         }
     return ORACLE_OK;
 }
+
+/* The same per-element dequantization for n listed entries: C[t] from the
+ * sum S[t] with the row scale sa[t] and the column scale sb[t]. */
+int oracle_dequant_entries(int64_t n, const int64_t *S, const float *sa, const float *sb, void *C,
+                           int half_out)
+{
+    if (n < 0)
+        return ORACLE_EINVAL;
+    for (int64_t t = 0; t < n; ++t) {
+        float c = dequant(S[t], sa[t], sb[t]);
+        if (half_out)
+            ((uint16_t *)C)[t] = oracle_float_to_half(c);
+        else
+            ((float *)C)[t] = c;
+    }
+    return ORACLE_OK;
+}

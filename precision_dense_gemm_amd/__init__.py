@@ -16,6 +16,10 @@ Operands are torch tensors on the GPU whose rows are contiguous in K:
 INT4 operands are uint8 tensors of packed bytes, (rows, K/2), two signed
 4-bit values per byte with the even k in the low nibble; K is passed
 explicitly and the leading dimensions are counted in 4-bit elements.
+
+The dequantizing variants of the integer GEMMs take float32 scale vectors
+scale_a (M,) and scale_b (N,) and write ((float)sum * scale_a[i]) *
+scale_b[j] as float32, or rounded to float16.
 """
 from __future__ import annotations
 
@@ -40,6 +44,12 @@ _i64, _p, _i = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
 for _name in ("gemm_f16", "gemm_i8", "gemm_i4"):
     getattr(lib, _name).argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
     getattr(lib, _name).restype = _i
+for _name in ("gemm_i8_dequant", "gemm_i4_dequant"):
+    getattr(lib, _name).argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i64, _i, _p]
+    getattr(lib, _name).restype = _i
+lib.pdgemm_dequant_cfg.argtypes = [_i, _i, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i64,
+                                   _i, _p]
+lib.pdgemm_dequant_cfg.restype = _i
 lib.pdgemm_gemm_cfg.argtypes = [_i, _i, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
 lib.pdgemm_gemm_cfg.restype = _i
 lib.pdgemm_num_configs.argtypes = []
@@ -101,20 +111,45 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg):
-    """The C function and its argument tuple for one GEMM."""
+def _scale(t: torch.Tensor, n: int, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 1:
+        raise TypeError(f"{name} must be a 1-D float32 tensor")
+    if t.shape[0] != n:
+        raise ValueError(f"{name} must hold {n} values")
+    if n > 1 and t.stride(0) != 1:
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t.data_ptr()
+
+
+def _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None):
+    """The C function and its argument tuple for one GEMM (dequantizing when
+    scales = (scale_a, scale_b) is given)."""
     M, N = A.shape[0], Bt.shape[0]
     ldc = _row_major_2d(out, "out")
     if tuple(out.shape) != (M, N):
         raise ValueError(f"out must have shape {(M, N)}")
-    args = (M, N, K, A.data_ptr(), lda, Bt.data_ptr(), ldb, out.data_ptr(), ldc, _stream(stream))
+    if scales is None:
+        args = (M, N, K, A.data_ptr(), lda, Bt.data_ptr(), ldb, out.data_ptr(), ldc,
+                _stream(stream))
+        if cfg is None:
+            return (lib.gemm_f16, lib.gemm_i8, lib.gemm_i4)[prec], args
+        return lib.pdgemm_gemm_cfg, (prec, cfg) + args
+    if prec == PREC_F16:
+        raise ValueError("the dequantizing epilogue is for INT8 and INT4")
+    if out.dtype not in (torch.float32, torch.float16):
+        raise TypeError("a dequantizing GEMM writes float32 or float16")
+    args = (M, N, K, A.data_ptr(), lda, Bt.data_ptr(), ldb, _scale(scales[0], M, "scale_a"),
+            _scale(scales[1], N, "scale_b"), out.data_ptr(), ldc,
+            1 if out.dtype == torch.float16 else 0, _stream(stream))
     if cfg is None:
-        return (lib.gemm_f16, lib.gemm_i8, lib.gemm_i4)[prec], args
-    return lib.pdgemm_gemm_cfg, (prec, cfg) + args
+        return (None, lib.gemm_i8_dequant, lib.gemm_i4_dequant)[prec], args
+    return lib.pdgemm_dequant_cfg, (prec, cfg) + args
 
 
-def _call(prec, A, Bt, out, K, lda, ldb, stream, cfg):
-    fn, args = _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg)
+def _call(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None):
+    fn, args = _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales)
     rc = fn(*args)
     if rc != 0:
         raise PdgemmError(rc)
@@ -170,35 +205,72 @@ def gemm_i4(A: torch.Tensor, Bt: torch.Tensor, K: int | None = None,
     return _call(PREC_I4, A, Bt, out, K, lda, ldb, stream, cfg)
 
 
+def gemm_i8_dequant(A: torch.Tensor, Bt: torch.Tensor, scale_a: torch.Tensor,
+                    scale_b: torch.Tensor, out: torch.Tensor | None = None,
+                    out_dtype: torch.dtype = torch.float32, stream=None,
+                    cfg: int | None = None) -> torch.Tensor:
+    """INT8 GEMM, then C[i][j] = ((float)sum * scale_a[i]) * scale_b[j] in binary32,
+    stored as float32 or rounded to float16 (out's dtype, else out_dtype)."""
+    if A.dtype != torch.int8 or Bt.dtype != torch.int8:
+        raise TypeError("gemm_i8_dequant takes int8 operands")
+    K = A.shape[1]
+    if Bt.shape[1] != K:
+        raise ValueError("A and Bt disagree on K")
+    lda, ldb = _row_major_2d(A, "A"), _row_major_2d(Bt, "Bt")
+    if out is None:
+        out = torch.empty((A.shape[0], Bt.shape[0]), dtype=out_dtype, device=A.device)
+    return _call(PREC_I8, A, Bt, out, K, lda, ldb, stream, cfg, (scale_a, scale_b))
+
+
+def gemm_i4_dequant(A: torch.Tensor, Bt: torch.Tensor, scale_a: torch.Tensor,
+                    scale_b: torch.Tensor, K: int | None = None,
+                    out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+                    stream=None, cfg: int | None = None) -> torch.Tensor:
+    """Packed INT4 GEMM with the dequantizing epilogue of gemm_i8_dequant."""
+    if A.dtype != torch.uint8 or Bt.dtype != torch.uint8:
+        raise TypeError("gemm_i4_dequant takes uint8 tensors of packed 4-bit values")
+    if K is None:
+        K = 2 * A.shape[1]
+    if A.shape[1] * 2 < K or Bt.shape[1] * 2 < K:
+        raise ValueError("packed operands hold fewer than K values per row")
+    lda, ldb = 2 * _row_major_2d(A, "A"), 2 * _row_major_2d(Bt, "Bt")
+    if out is None:
+        out = torch.empty((A.shape[0], Bt.shape[0]), dtype=out_dtype, device=A.device)
+    return _call(PREC_I4, A, Bt, out, K, lda, ldb, stream, cfg, (scale_a, scale_b))
+
+
 def prepare(prec: str, A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor, K: int | None = None,
-            stream=None, cfg: int | None = None):
+            stream=None, cfg: int | None = None, scales=None):
     """Check and marshal one GEMM once; return a no-argument callable that
     enqueues it again (on the stream current now) through the C ABI.
 
     For repeated launches of the same operands, e.g. timing loops: the
     callable skips the per-call Python checks, so host time stays far below
     the kernel time even for small shapes.  The tensors must stay alive.
+    With scales = (scale_a, scale_b) an INT8 / INT4 GEMM is the dequantizing
+    one, and out is float32 or float16.
     """
+    integer_out = (torch.int32,) if scales is None else (torch.float32, torch.float16)
     if prec == "f16":
         if A.dtype != torch.float16 or Bt.dtype != torch.float16 or out.dtype != torch.float32:
             raise TypeError("f16 takes float16 operands and a float32 output")
         K = A.shape[1] if K is None else K
         lda, ldb, p = _row_major_2d(A, "A"), _row_major_2d(Bt, "Bt"), PREC_F16
     elif prec == "i8":
-        if A.dtype != torch.int8 or Bt.dtype != torch.int8 or out.dtype != torch.int32:
-            raise TypeError("i8 takes int8 operands and an int32 output")
+        if A.dtype != torch.int8 or Bt.dtype != torch.int8 or out.dtype not in integer_out:
+            raise TypeError("i8 takes int8 operands and an int32 (dequantizing: float) output")
         K = A.shape[1] if K is None else K
         lda, ldb, p = _row_major_2d(A, "A"), _row_major_2d(Bt, "Bt"), PREC_I8
     elif prec == "i4":
-        if A.dtype != torch.uint8 or Bt.dtype != torch.uint8 or out.dtype != torch.int32:
-            raise TypeError("i4 takes uint8 packed operands and an int32 output")
+        if A.dtype != torch.uint8 or Bt.dtype != torch.uint8 or out.dtype not in integer_out:
+            raise TypeError("i4 takes uint8 packed operands and an int32 (dequantizing: float) output")
         K = 2 * A.shape[1] if K is None else K
         lda, ldb, p = 2 * _row_major_2d(A, "A"), 2 * _row_major_2d(Bt, "Bt"), PREC_I4
     else:
         raise ValueError(f"unknown precision {prec!r}")
     if A.shape[1] * (2 if prec == "i4" else 1) < K or Bt.shape[1] * (2 if prec == "i4" else 1) < K:
         raise ValueError("operands hold fewer than K values per row")
-    fn, args = _marshal(p, A, Bt, out, K, lda, ldb, stream, cfg)
+    fn, args = _marshal(p, A, Bt, out, K, lda, ldb, stream, cfg, scales)
     rc = fn(*args)  # validates the arguments once, and is a first launch
     if rc != 0:
         raise PdgemmError(rc)

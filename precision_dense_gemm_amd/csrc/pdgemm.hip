@@ -127,12 +127,24 @@ struct Args {
     const uint8_t *A;
     const uint8_t *B;
     void *C;
+    const float *scale_a;  // dequantizing epilogue only: one scale per row of A
+    const float *scale_b;  // ... and per column of B
     int64_t lda_bytes;
     int64_t ldb_bytes;
     int64_t ldc;
     int M, N, K;
     int tiles_m, tiles_n;
 };
+
+// Epilogues: the int32 / fp32 sums as they are, or (integer paths) the
+// dequantized ((float)sum * scale_a[i]) * scale_b[j] as fp32 or binary16.
+constexpr int kRaw = 0;
+constexpr int kDequantF32 = 1;
+constexpr int kDequantF16 = 2;
+
+template <int P, int E> struct OutOf { using type = typename Prec<P>::Out; };
+template <int P> struct OutOf<P, kDequantF32> { using type = float; };
+template <int P> struct OutOf<P, kDequantF16> { using type = _Float16; };
 
 // One workgroup computes a BM x BN block of C with (BM/WM) x (BN/WN) waves.
 //
@@ -153,13 +165,14 @@ struct Args {
 // only for its own DMA of tile t+1 (tiles t+2 .. t+kStages-1 stay in
 // flight), so after the barrier tile t+1 is complete in LDS and stage t is
 // free for tile t+kStages.
-template <int P, int BM, int BN, int WM, int WN, int GM>
+template <int P, int BM, int BN, int WM, int WN, int GM, int E>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Args args) {
     // The body uses gfx950-only types (buffer resources), which the host
     // pass cannot type-check; the host pass only needs the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
     using Acc = typename Prec<P>::Acc;
-    using Out = typename Prec<P>::Out;
+    using Out = typename OutOf<P, E>::type;
+    static_assert(E == kRaw || P != kF16, "the dequantizing epilogue is for the integer paths");
     constexpr int kWavesN = BN / WN;
     constexpr int NW = (BM / WM) * kWavesN;
     constexpr int kRows = BM + BN;           // LDS rows per stage
@@ -369,12 +382,31 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
         mma(fa1, fb1);
     };
 
+    // Dequantizing epilogue: the block tile's row scales (BM entries) and
+    // column scales (BN entries) are staged in LDS once; rows and columns
+    // past the edge take the last valid scale (their results are not
+    // stored).  The loads are issued before the first DMAs and written to
+    // LDS after them; the first barrier makes them visible.
+    constexpr int kThreads = NW * kWave;
+    constexpr int kScaleLoads = E == kRaw ? 0 : (BM + BN + kThreads - 1) / kThreads;
+    __shared__ __align__(16) float lds_scale[E == kRaw ? 1 : BM + BN];
+    float scale_v[kScaleLoads + 1];
+#pragma unroll
+    for (int x = 0; x < kScaleLoads; ++x) {
+        const int idx = tid + x * kThreads;
+        if (idx < BM + BN)
+            scale_v[x] = idx < BM ? args.scale_a[min(m0 + idx, M - 1)] : args.scale_b[min(n0 + idx - BM, N - 1)];
+    }
+
     if (n_tiles > 0) {
         stage(0, lds0);
         stage(1, lds1);
         stage(2, lds2);
         stage(3, lds3);
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kStages - 1) * kDma) : "memory");
+#pragma unroll
+        for (int x = 0; x < kScaleLoads; ++x)
+            if (tid + x * kThreads < BM + BN) lds_scale[tid + x * kThreads] = scale_v[x];
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((kStages - 1) * kDma) : "memory");
         read_frags(lds0, 0, fa0, fb0);
         int t = 0;
         for (; t + kStages < n_tiles; t += kStages) {
@@ -395,6 +427,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
         last_tile(last == 0 ? lds0 : last == 1 ? lds1 : last == 2 ? lds2 : lds3, t);
         // no DMA may still be writing this workgroup's LDS when it exits
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else if constexpr (E != kRaw) {
+        // K == 0: no main loop, so stage the scales here
+#pragma unroll
+        for (int x = 0; x < kScaleLoads; ++x)
+            if (tid + x * kThreads < BM + BN) lds_scale[tid + x * kThreads] = scale_v[x];
+        __syncthreads();
     }
 
     // ---- epilogue: 32x32 MFMA result layout -> row-major C ----
@@ -410,9 +448,23 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
         const bool interior = m0 + BM <= M && n0 + BN <= N;
         const int rows_left = M - (m0 + wm0) - 4 * fhalf;  // rows this lane may write: r < rows_left
         const int cols_left = N - (n0 + wn0) - frow;        // columns: j*32 < cols_left
+
+        // this lane's scales: 4 consecutive rows per quarter of a 32-row
+        // block (one 16-byte LDS read each), one column per column block
+        float sb[E == kRaw ? 1 : FN];
+        if constexpr (E != kRaw) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) sb[j] = lds_scale[BM + wn0 + j * 32 + frow];
+        }
         auto store_all = [&](auto &&keep) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
+                float4 sa[E == kRaw ? 1 : 4];
+                if constexpr (E != kRaw) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        sa[q] = *reinterpret_cast<const float4 *>(&lds_scale[wm0 + i * 32 + 8 * q + 4 * fhalf]);
+                }
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int r = i * 32 + 8 * (e >> 2) + (e & 3);   // wave-uniform part of the row
@@ -420,22 +472,44 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
                         Out v;
-                        if constexpr (P == kI4)
+                        if constexpr (E != kRaw) {
+                            // ((float)sum * scale_a) * scale_b, rounded once per step
+                            const int32_t sum = P == kI4 ? acc[i][j][e] >> 8 : acc[i][j][e];
+                            float c = (float)sum;
+                            const float4 a4 = sa[e >> 2];
+                            c = c * ((e & 3) == 0 ? a4.x : (e & 3) == 1 ? a4.y : (e & 3) == 2 ? a4.z : a4.w);
+                            c = c * sb[j];
+                            // The binary16 result is the binary32 product rounded
+                            // again.  The backend would otherwise fold product and
+                            // narrowing into one mixed-precision FMA, which rounds
+                            // once (and turns -0 into +0): the empty asm makes the
+                            // binary32 value opaque to it.
+                            if constexpr (E == kDequantF16) asm("" : "+v"(c));
+                            v = (Out)c;
+                        } else if constexpr (P == kI4) {
                             v = acc[i][j][e] >> 8;
-                        else
+                        } else {
                             v = acc[i][j][e];
+                        }
                         if (keep(r, j))
                             *reinterpret_cast<Out *>(row_c + lane_off + j * 32 * (int)sizeof(Out)) = v;
                     }
+                    // dequantized values are converted one row at a time
+                    if constexpr (E != kRaw) __builtin_amdgcn_sched_barrier(0);
                 }
                 // one row block at a time keeps accumulator reads from piling up
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        if (interior)
+        if constexpr (E != kRaw) {
+            // one path: with two, more of the accumulators are copied out of
+            // the accumulation registers ahead of the branch
+            store_all([&](int r, int j) { return interior || (r < rows_left && j * 32 < cols_left); });
+        } else if (interior) {
             store_all([](int, int) { return true; });
-        else
+        } else {
             store_all([&](int r, int j) { return r < rows_left && j * 32 < cols_left; });
+        }
     }
 #endif  // __HIP_DEVICE_COMPILE__
 }
@@ -454,18 +528,31 @@ constexpr Config kConfigs[] = {
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
-template <int P, int C>
+template <int P, int C, int E>
 const void *kernel_for() {
     constexpr Config c = kConfigs[C];
-    return reinterpret_cast<const void *>(&gemm_kernel<P, c.bm, c.bn, c.wm, c.wn, c.gm>);
+    return reinterpret_cast<const void *>(&gemm_kernel<P, c.bm, c.bn, c.wm, c.wn, c.gm, E>);
 }
 
-template <int P>
+template <int P, int E>
 const void *kernel_ptr(int cfg) {
     switch (cfg) {
-    case 0: return kernel_for<P, 0>();
-    case 1: return kernel_for<P, 1>();
-    case 2: return kernel_for<P, 2>();
+    case 0: return kernel_for<P, 0, E>();
+    case 1: return kernel_for<P, 1, E>();
+    case 2: return kernel_for<P, 2, E>();
+    default: return nullptr;
+    }
+}
+
+const void *kernel_ptr(int prec, int cfg, int epi) {
+    switch (prec * 3 + epi) {
+    case kF16 * 3 + kRaw: return kernel_ptr<kF16, kRaw>(cfg);
+    case kI8 * 3 + kRaw: return kernel_ptr<kI8, kRaw>(cfg);
+    case kI8 * 3 + kDequantF32: return kernel_ptr<kI8, kDequantF32>(cfg);
+    case kI8 * 3 + kDequantF16: return kernel_ptr<kI8, kDequantF16>(cfg);
+    case kI4 * 3 + kRaw: return kernel_ptr<kI4, kRaw>(cfg);
+    case kI4 * 3 + kDequantF32: return kernel_ptr<kI4, kDequantF32>(cfg);
+    case kI4 * 3 + kDequantF16: return kernel_ptr<kI4, kDequantF16>(cfg);
     default: return nullptr;
     }
 }
@@ -493,8 +580,9 @@ int pick(int prec, int64_t M, int64_t N, int64_t K) {
     return kNumConfigs - 1;
 }
 
-int validate(int prec, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
-             const void *B, int64_t ldb, const void *C, int64_t ldc) {
+int validate(int prec, int epi, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+             const void *B, int64_t ldb, const void *C, int64_t ldc, const float *scale_a,
+             const float *scale_b) {
     if (M < 0 || N < 0 || K < 0) return PDGEMM_EINVAL_DIM;
     if (M > INT32_MAX || N > INT32_MAX || K > (int64_t(1) << 30)) return PDGEMM_EINVAL_DIM;
     if (prec == kI4 && K > PDGEMM_I4_MAX_K) return PDGEMM_EINVAL_DIM;
@@ -502,19 +590,25 @@ int validate(int prec, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     if (prec == kI4 && ((K & 1) || (lda & 1) || (ldb & 1))) return PDGEMM_EINVAL_I4;
     if (M == 0 || N == 0) return PDGEMM_OK;
     if (!C || (K > 0 && (!A || !B))) return PDGEMM_ENULL;
+    if (epi != kRaw && (!scale_a || !scale_b)) return PDGEMM_ENULL;
     const int64_t lda_bytes = lda * elem_bits(prec) / 8;
     const int64_t ldb_bytes = ldb * elem_bits(prec) / 8;
+    const int64_t c_size = epi == kDequantF16 ? 2 : 4;
     if ((lda_bytes & 15) || (ldb_bytes & 15)) return PDGEMM_EALIGN;
     // operand tiles are addressed with 32-bit offsets from the tile's first row
-    if (lda_bytes > kMaxRowBytes || ldb_bytes > kMaxRowBytes || ldc * 4 > kMaxRowBytes) return PDGEMM_EINVAL_LD;
-    if (((uintptr_t)A & 15) || ((uintptr_t)B & 15) || ((uintptr_t)C & 3)) return PDGEMM_EALIGN;
+    if (lda_bytes > kMaxRowBytes || ldb_bytes > kMaxRowBytes || ldc * c_size > kMaxRowBytes)
+        return PDGEMM_EINVAL_LD;
+    if (((uintptr_t)A & 15) || ((uintptr_t)B & 15) || ((uintptr_t)C & (c_size - 1))) return PDGEMM_EALIGN;
+    if (epi != kRaw && (((uintptr_t)scale_a & 3) || ((uintptr_t)scale_b & 3))) return PDGEMM_EALIGN;
     return PDGEMM_OK;
 }
 
-int launch(int prec, int cfg, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
-           const void *B, int64_t ldb, void *C, int64_t ldc, void *stream) {
+int launch(int prec, int cfg, int epi, int64_t M, int64_t N, int64_t K, const void *A,
+           int64_t lda, const void *B, int64_t ldb, const float *scale_a, const float *scale_b,
+           void *C, int64_t ldc, void *stream) {
     if (prec < 0 || prec > 2 || cfg < 0 || cfg >= kNumConfigs) return PDGEMM_EINVAL_CFG;
-    int rc = validate(prec, M, N, K, A, lda, B, ldb, C, ldc);
+    if (epi != kRaw && prec == kF16) return PDGEMM_EINVAL_CFG;
+    int rc = validate(prec, epi, M, N, K, A, lda, B, ldb, C, ldc, scale_a, scale_b);
     if (rc != PDGEMM_OK) return rc;
     if (M == 0 || N == 0) return PDGEMM_OK;
 
@@ -525,6 +619,8 @@ int launch(int prec, int cfg, int64_t M, int64_t N, int64_t K, const void *A, in
     args.A = K > 0 ? static_cast<const uint8_t *>(A) : static_cast<const uint8_t *>(C);
     args.B = K > 0 ? static_cast<const uint8_t *>(B) : static_cast<const uint8_t *>(C);
     args.C = C;
+    args.scale_a = scale_a;
+    args.scale_b = scale_b;
     args.lda_bytes = lda * elem_bits(prec) / 8;
     args.ldb_bytes = ldb * elem_bits(prec) / 8;
     args.ldc = ldc;
@@ -536,9 +632,7 @@ int launch(int prec, int cfg, int64_t M, int64_t N, int64_t K, const void *A, in
     const int64_t blocks = (int64_t)args.tiles_m * args.tiles_n;
     if (blocks > INT32_MAX) return PDGEMM_EINVAL_DIM;
 
-    const void *fn = prec == kF16 ? kernel_ptr<kF16>(cfg)
-                     : prec == kI8 ? kernel_ptr<kI8>(cfg)
-                                   : kernel_ptr<kI4>(cfg);
+    const void *fn = kernel_ptr(prec, cfg, epi);
     const int threads = (c.bm / c.wm) * (c.bn / c.wn) * kWave;
     void *kargs[] = {&args};
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -557,23 +651,48 @@ extern "C" {
 
 int gemm_f16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
              const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream) {
-    return launch(kF16, pick(kF16, M, N, K), M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return launch(kF16, pick(kF16, M, N, K), kRaw, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
+                  stream);
 }
 
 int gemm_i8(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
             const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
-    return launch(kI8, pick(kI8, M, N, K), M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return launch(kI8, pick(kI8, M, N, K), kRaw, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
+                  stream);
 }
 
 int gemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
             const uint8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
-    return launch(kI4, pick(kI4, M, N, K), M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return launch(kI4, pick(kI4, M, N, K), kRaw, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
+                  stream);
+}
+
+int gemm_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
+                    const int8_t *B, int64_t ldb, const float *scale_a, const float *scale_b,
+                    void *C, int64_t ldc, int out_f16, void *stream) {
+    return launch(kI8, pick(kI8, M, N, K), out_f16 ? kDequantF16 : kDequantF32, M, N, K, A, lda, B,
+                  ldb, scale_a, scale_b, C, ldc, stream);
+}
+
+int gemm_i4_dequant(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+                    const uint8_t *B, int64_t ldb, const float *scale_a, const float *scale_b,
+                    void *C, int64_t ldc, int out_f16, void *stream) {
+    return launch(kI4, pick(kI4, M, N, K), out_f16 ? kDequantF16 : kDequantF32, M, N, K, A, lda, B,
+                  ldb, scale_a, scale_b, C, ldc, stream);
 }
 
 int pdgemm_gemm_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K, const void *A,
                     int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc,
                     void *stream) {
-    return launch(prec, cfg, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return launch(prec, cfg, kRaw, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc, stream);
+}
+
+int pdgemm_dequant_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K, const void *A,
+                       int64_t lda, const void *B, int64_t ldb, const float *scale_a,
+                       const float *scale_b, void *C, int64_t ldc, int out_f16, void *stream) {
+    if (prec == kF16) return PDGEMM_EINVAL_CFG;
+    return launch(prec, cfg, out_f16 ? kDequantF16 : kDequantF32, M, N, K, A, lda, B, ldb, scale_a,
+                  scale_b, C, ldc, stream);
 }
 
 int pdgemm_num_configs(void) { return kNumConfigs; }
@@ -602,8 +721,8 @@ const char *pdgemm_strerror(int code) {
     case PDGEMM_EINVAL_LD: return "leading dimension smaller than the row length";
     case PDGEMM_ENULL: return "null pointer for an operand with nonzero extent";
     case PDGEMM_EINVAL_I4: return "INT4 K, lda and ldb must be even";
-    case PDGEMM_EALIGN: return "A and B must be 16-byte aligned with rows spanning a multiple of 16 bytes; C 4-byte aligned";
-    case PDGEMM_EINVAL_CFG: return "unknown precision or tile configuration";
+    case PDGEMM_EALIGN: return "A and B must be 16-byte aligned, A and B rows must span a multiple of 16 bytes, C and the scales must be element-aligned";
+    case PDGEMM_EINVAL_CFG: return "unknown precision or tile configuration, or a dequantizing epilogue for FP16";
     default: return code > 0 ? hipGetErrorString((hipError_t)code) : "unknown error";
     }
 }

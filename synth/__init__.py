@@ -15,6 +15,10 @@ Value mappings (the pages fix only the distributions; these are our readings):
             (round-to-nearest-even; 1 - 2**-12 and above round to 1.0)
   N(0, 1)   Box-Muller on consecutive draws (u1 in (0, 1], u2 in [0, 1)),
             scaled by 1/sqrt(K), then rounded to binary16
+  scales    positive binary32, log-uniform over [2**lo, 2**hi): exponent
+            lo + (draw >> 32) % (hi - lo), mantissa the low 23 bits of the draw
+            (per-row / per-column quantization scales of the dequantizing
+            epilogue)
 
 Operand formats (the layout of the GEMM's operands):
   A   M x K, row-major, K contiguous        -> numpy array shape (M, K)
@@ -135,6 +139,16 @@ def f16_normal(rows: int, cols: int, seed: int, scale: float = 1.0) -> np.ndarra
         z = np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * math.pi * u2)
         out[lo:hi] = (z * scale).astype(np.float16)
     return out.reshape(rows, cols)
+
+
+def f32_scales(n: int, seed: int, lo: int = -12, hi: int = -2) -> np.ndarray:
+    """n positive binary32 scales, log-uniform over [2**lo, 2**hi)."""
+    if not -126 <= lo < hi <= 128:
+        raise ValueError("scale exponents must stay in the normal binary32 range")
+    x = splitmix64(seed, n)
+    e = (x >> np.uint64(32)) % np.uint64(hi - lo)
+    bits = ((e.astype(np.int64) + lo + 127) << 23) | (x & np.uint64(0x7FFFFF)).astype(np.int64)
+    return bits.astype(np.uint32).view(np.float32)
 
 
 def operands(prec: str, m: int, n: int, k: int, seed_a: int, seed_b: int,

@@ -37,6 +37,11 @@ def lib():
     for name in ("gemm_f16", "gemm_i8", "gemm_i4"):
         getattr(L, name).argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
         getattr(L, name).restype = i
+    for name in ("gemm_i8_dequant", "gemm_i4_dequant"):
+        getattr(L, name).argtypes = [i64, i64, i64, p, i64, p, i64, p, p, p, i64, i, p]
+        getattr(L, name).restype = i
+    L.pdgemm_dequant_cfg.argtypes = [i, i, i64, i64, i64, p, i64, p, i64, p, p, p, i64, i, p]
+    L.pdgemm_dequant_cfg.restype = i
     L.pdgemm_gemm_cfg.argtypes = [i, i, i64, i64, i64, p, i64, p, i64, p, i64, p]
     L.pdgemm_gemm_cfg.restype = i
     L.pdgemm_strerror.argtypes = [i]
@@ -46,9 +51,10 @@ def lib():
     return L
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("gemm_f16", "gemm_i8", "gemm_i4", "pdgemm_gemm_cfg", "pdgemm_strerror", "pdgemm_version"):
+    for n in ("gemm_f16", "gemm_i8", "gemm_i4", "gemm_i8_dequant", "gemm_i4_dequant",
+              "pdgemm_gemm_cfg", "pdgemm_dequant_cfg", "pdgemm_strerror", "pdgemm_version"):
         assert n in names
 
 
@@ -98,6 +104,53 @@ def test_argument_errors(lib, name):
     assert call(lib, name, 0, 64, 64) == 0
     assert call(lib, name, 64, 0, 64) == 0
     assert call(lib, name, 0, 0, 0, A=None, B=None, C=None) == 0
+
+
+PSA, PSB = 0x40000, 0x50000
+
+
+def call_dq(lib, name, M, N, K, A=PA, lda=None, B=PB, ldb=None, sa=PSA, sb=PSB, C=PC, ldc=None,
+            f16=0):
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return getattr(lib, name)(M, N, K, A, lda, B, ldb, sa, sb, C, ldc, f16, None)
+
+
+@pytest.mark.parametrize("name", ["gemm_i8_dequant", "gemm_i4_dequant"])
+def test_dequant_argument_errors(lib, name):
+    c = codes()
+    assert call_dq(lib, name, -1, 64, 64) == c["PDGEMM_EINVAL_DIM"]
+    assert call_dq(lib, name, 64, 64, 64, lda=32) == c["PDGEMM_EINVAL_LD"]
+    assert call_dq(lib, name, 64, 64, 64, ldc=32) == c["PDGEMM_EINVAL_LD"]
+    assert call_dq(lib, name, 64, 64, 64, A=None) == c["PDGEMM_ENULL"]
+    assert call_dq(lib, name, 64, 64, 64, C=None) == c["PDGEMM_ENULL"]
+    assert call_dq(lib, name, 64, 64, 64, sa=None) == c["PDGEMM_ENULL"]
+    assert call_dq(lib, name, 64, 64, 64, sb=None) == c["PDGEMM_ENULL"]
+    assert call_dq(lib, name, 64, 64, 0, A=None, B=None, sa=None) == c["PDGEMM_ENULL"]
+    # scales are element-aligned; a binary16 output needs only 2 bytes
+    assert call_dq(lib, name, 64, 64, 64, sa=PSA + 2) == c["PDGEMM_EALIGN"]
+    assert call_dq(lib, name, 64, 64, 64, sb=PSB + 1) == c["PDGEMM_EALIGN"]
+    assert call_dq(lib, name, 64, 64, 64, C=PC + 2) == c["PDGEMM_EALIGN"]
+    assert call_dq(lib, name, 64, 64, 64, C=PC + 1, f16=1) == c["PDGEMM_EALIGN"]
+    # a row of C above 4 MiB: the byte span depends on the output type
+    assert call_dq(lib, name, 64, 64, 64, ldc=(1 << 20) + 64) == c["PDGEMM_EINVAL_LD"]
+    assert call_dq(lib, name, 64, 64, 64, ldc=(1 << 21) + 64, f16=1) == c["PDGEMM_EINVAL_LD"]
+    # empty outputs succeed without touching HIP, scales unused
+    assert call_dq(lib, name, 0, 64, 64, sa=None, sb=None) == 0
+    assert call_dq(lib, name, 64, 0, 64, sa=None, sb=None) == 0
+    if name == "gemm_i4_dequant":
+        assert call_dq(lib, name, 64, 64, 63, lda=64, ldb=64) == c["PDGEMM_EINVAL_I4"]
+
+
+def test_dequant_cfg_errors(lib):
+    c = codes()
+    n = lib.pdgemm_num_configs()
+    args = (64, 64, 64, PA, 64, PB, 64, PSA, PSB, PC, 64, 0, None)
+    assert lib.pdgemm_dequant_cfg(0, 0, *args) == c["PDGEMM_EINVAL_CFG"]   # FP16 has no dequant
+    assert lib.pdgemm_dequant_cfg(1, n, *args) == c["PDGEMM_EINVAL_CFG"]
+    assert lib.pdgemm_dequant_cfg(2, -1, *args) == c["PDGEMM_EINVAL_CFG"]
+    assert lib.pdgemm_dequant_cfg(3, 0, *args) == c["PDGEMM_EINVAL_CFG"]
 
 
 def test_alignment_of_leading_dims_per_precision(lib):
@@ -153,3 +206,6 @@ def test_binding_imports_and_marshals_without_gpu():
         pd.gemm_i8(torch.zeros(4, 4, dtype=torch.float16), torch.zeros(4, 4, dtype=torch.int8))
     with pytest.raises(ValueError):
         pd.gemm_i8(torch.zeros(4, 4, dtype=torch.int8), torch.zeros(4, 4, dtype=torch.int8))  # CPU tensors
+    with pytest.raises(TypeError):
+        pd.gemm_i8_dequant(torch.zeros(4, 4, dtype=torch.float16), torch.zeros(4, 4, dtype=torch.int8),
+                           torch.ones(4), torch.ones(4))

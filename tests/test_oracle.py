@@ -304,6 +304,19 @@ def pin_dequant():
     Ch = oracle.dequant(Sm, sa * 1e-3, sb, half_out=True)
     wanth = ((Sm.astype(np.float32) * (sa * np.float32(1e-3))[:, None]) * sb[None, :]).astype(np.float16)
     assert Ch.dtype == np.float16 and np.array_equal(Ch.view(np.uint16), wanth.view(np.uint16))
+    # the elementwise form, with signed scales and zero sums (signed zeros are bit-exact)
+    n = 4000
+    Se = rng.integers(-2 ** 31, 2 ** 31, n, dtype=np.int64)
+    Se[::7] = 0
+    sae = (rng.uniform(-4, 4, n) * np.exp2(rng.integers(-30, 10, n))).astype(np.float32)
+    sbe = (rng.uniform(-4, 4, n) * np.exp2(rng.integers(-30, 10, n))).astype(np.float32)
+    want = (Se.astype(np.float32) * sae) * sbe
+    got = oracle.dequant_entries(Se, sae, sbe)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    goth = oracle.dequant_entries(Se, sae, sbe, half_out=True)
+    with np.errstate(over="ignore"):  # large products round to infinity, on both sides
+        wanth = want.astype(np.float16)
+    assert np.array_equal(goth.view(np.uint16), wanth.view(np.uint16))
 
 
 PINS = [pin_half_decoder, pin_mma_lab_f16, pin_mma_lab_integer, pin_closed_forms,
@@ -349,3 +362,15 @@ def test_synth_distributions():
     assert abs(n.mean()) < 0.02 and abs(n.std() - 1.0) < 0.02
     # pack order: low nibble holds the even k
     assert synth.pack_int4(np.array([[1, -1]], np.int8))[0, 0] == 0xF1
+
+
+def test_synth_scales():
+    s = synth.f32_scales(200000, 11, lo=-12, hi=-2)
+    assert s.dtype == np.float32 and np.all(s >= 2.0 ** -12) and np.all(s < 2.0 ** -2)
+    e = np.floor(np.log2(s.astype(np.float64))).astype(int)
+    counts = np.bincount(e + 12, minlength=10)
+    assert counts.size == 10 and np.all(np.abs(counts / s.size - 0.1) < 0.01)  # log-uniform
+    assert np.array_equal(s, synth.f32_scales(200000, 11, lo=-12, hi=-2))
+    assert not np.array_equal(s[:100], synth.f32_scales(100, 12))
+    with pytest.raises(ValueError):
+        synth.f32_scales(4, 0, lo=-130, hi=0)
