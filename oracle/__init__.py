@@ -12,7 +12,9 @@ arrays into it.  Arrays follow the library's operand contract:
     A   (M, lda)   row-major, K contiguous            (int4: (M, lda/2) uint8)
     Bt  (N, ldb)   column-major B stored as its rows  (int4: (N, ldb/2) uint8)
 
-and the first K elements of each row take part in the product.
+and the first K elements of each row take part in the product.  The *_rowb
+functions take B row-major instead, as a (K, ldb) array (int4: (K, ldb/2)
+bytes packed along N), of which the first N columns take part.
 """
 from __future__ import annotations
 
@@ -67,6 +69,16 @@ def _load():
         lib.oracle_dequant.restype = i32
         lib.oracle_dequant_entries.argtypes = [i64, p, p, p, p, i32]
         lib.oracle_dequant_entries.restype = i32
+        lib.oracle_gemm_f16_rowb.argtypes = lib.oracle_gemm_f16.argtypes
+        lib.oracle_gemm_i8_rowb.argtypes = lib.oracle_gemm_i8.argtypes
+        lib.oracle_gemm_i4_rowb.argtypes = lib.oracle_gemm_i4.argtypes
+        lib.oracle_entries_f16_rowb.argtypes = lib.oracle_entries_f16.argtypes
+        lib.oracle_entries_i8_rowb.argtypes = lib.oracle_entries_i8.argtypes
+        lib.oracle_entries_i4_rowb.argtypes = lib.oracle_entries_i4.argtypes
+        for f in (lib.oracle_gemm_f16_rowb, lib.oracle_gemm_i8_rowb, lib.oracle_gemm_i4_rowb,
+                  lib.oracle_entries_f16_rowb, lib.oracle_entries_i8_rowb,
+                  lib.oracle_entries_i4_rowb):
+            f.restype = i32
         for f in (lib.oracle_gemm_f16, lib.oracle_gemm_i8, lib.oracle_gemm_i4,
                   lib.oracle_entries_f16, lib.oracle_entries_i8, lib.oracle_entries_i4):
             f.restype = i32
@@ -217,3 +229,95 @@ def dequant_entries(S, scale_a, scale_b, half_out=False):
     _check(_load().oracle_dequant_entries(S.size, ps, pa, pb, C.ctypes.data_as(ctypes.c_void_p),
                                           1 if half_out else 0))
     return C.view(np.float16) if half_out else C
+
+
+# ---------------------------------------------------------------------------
+# B row-major: B is a (K, ldb) array (int4: (K, ldb/2) bytes packed along N)
+
+def _rowb_dims(A, B, N, K, packed):
+    width = 2 * B.shape[1] if packed else B.shape[1]
+    N = width if N is None else N
+    K = (2 * A.shape[1] if packed else A.shape[1]) if K is None else K
+    if N > width or K > B.shape[0]:
+        raise ValueError("B holds fewer than K rows or N columns")
+    return N, K, width
+
+
+def gemm_f16_rowb(A, B, N=None, K=None, threads=None):
+    """FP16 product with B row-major, in fp64: returns (R, S) as gemm_f16."""
+    A, pa = _c(A, np.float16)
+    B, pb = _c(B, np.float16)
+    N, K, ldb = _rowb_dims(A, B, N, K, False)
+    M = A.shape[0]
+    R = np.zeros((M, N), np.float64)
+    S = np.zeros((M, N), np.float64)
+    _check(_load().oracle_gemm_f16_rowb(M, N, K, pa, A.shape[1], pb, ldb,
+                                        R.ctypes.data_as(ctypes.c_void_p),
+                                        S.ctypes.data_as(ctypes.c_void_p), N,
+                                        threads or default_threads()))
+    return R, S
+
+
+def gemm_i8_rowb(A, B, N=None, K=None, threads=None):
+    """INT8 product with B row-major, exact, as int64 (M, N)."""
+    A, pa = _c(A, np.int8)
+    B, pb = _c(B, np.int8)
+    N, K, ldb = _rowb_dims(A, B, N, K, False)
+    C = np.zeros((A.shape[0], N), np.int64)
+    _check(_load().oracle_gemm_i8_rowb(A.shape[0], N, K, pa, A.shape[1], pb, ldb,
+                                       C.ctypes.data_as(ctypes.c_void_p), N,
+                                       threads or default_threads()))
+    return C
+
+
+def gemm_i4_rowb(Ap, Bp, N=None, K=None, threads=None):
+    """Packed INT4 product with B row-major (packed along N), exact, as int64 (M, N)."""
+    Ap, pa = _c(Ap, np.uint8)
+    Bp, pb = _c(Bp, np.uint8)
+    N, K, ldb = _rowb_dims(Ap, Bp, N, K, True)
+    C = np.zeros((Ap.shape[0], N), np.int64)
+    _check(_load().oracle_gemm_i4_rowb(Ap.shape[0], N, K, pa, 2 * Ap.shape[1], pb, ldb,
+                                       C.ctypes.data_as(ctypes.c_void_p), N,
+                                       threads or default_threads()))
+    return C
+
+
+def entries_f16_rowb(A, B, rows, cols, K=None):
+    A, pa = _c(A, np.float16)
+    B, pb = _c(B, np.float16)
+    r, c = _idx(rows, cols)
+    K = A.shape[1] if K is None else K
+    R = np.zeros(r.shape, np.float64)
+    S = np.zeros(r.shape, np.float64)
+    _check(_load().oracle_entries_f16_rowb(K, pa, A.shape[1], pb, B.shape[1], r.size,
+                                           r.ctypes.data_as(ctypes.c_void_p),
+                                           c.ctypes.data_as(ctypes.c_void_p),
+                                           R.ctypes.data_as(ctypes.c_void_p),
+                                           S.ctypes.data_as(ctypes.c_void_p)))
+    return R, S
+
+
+def entries_i8_rowb(A, B, rows, cols, K=None):
+    A, pa = _c(A, np.int8)
+    B, pb = _c(B, np.int8)
+    r, c = _idx(rows, cols)
+    K = A.shape[1] if K is None else K
+    C = np.zeros(r.shape, np.int64)
+    _check(_load().oracle_entries_i8_rowb(K, pa, A.shape[1], pb, B.shape[1], r.size,
+                                          r.ctypes.data_as(ctypes.c_void_p),
+                                          c.ctypes.data_as(ctypes.c_void_p),
+                                          C.ctypes.data_as(ctypes.c_void_p)))
+    return C
+
+
+def entries_i4_rowb(Ap, Bp, rows, cols, K=None):
+    Ap, pa = _c(Ap, np.uint8)
+    Bp, pb = _c(Bp, np.uint8)
+    r, c = _idx(rows, cols)
+    K = 2 * Ap.shape[1] if K is None else K
+    C = np.zeros(r.shape, np.int64)
+    _check(_load().oracle_entries_i4_rowb(K, pa, 2 * Ap.shape[1], pb, 2 * Bp.shape[1], r.size,
+                                          r.ctypes.data_as(ctypes.c_void_p),
+                                          c.ctypes.data_as(ctypes.c_void_p),
+                                          C.ctypes.data_as(ctypes.c_void_p)))
+    return C

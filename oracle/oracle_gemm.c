@@ -35,6 +35,12 @@
  * odd; lda/ldb count 4-bit elements (the pages do not give the nibble order;
  * low-nibble-first is the reading taken).
  *
+ * The *_rowb functions take B row-major instead: element (k, j) at
+ * B[k*ldb + j] with ldb >= N, the "transposed B" layout of the paper's
+ * Section IV-D loader ablation (Run 4), which it finds slower.  INT4 B then
+ * packs two values per byte along N: element j of row k sits in byte j/2 of
+ * that row, low nibble for even j.
+ *
  * Parallelism: output rows are split over POSIX threads; each element is the
  * same sequential k loop, so results do not depend on the thread count.
  */
@@ -73,6 +79,25 @@ static int s4_at(const uint8_t *row, int64_t k)
     return v < 8 ? v : v - 16;
 }
 
+/* Element (k, j) of B in either layout. */
+static double b_f16(const void *B, int64_t ldb, int rowmajor, int64_t k, int64_t j)
+{
+    const uint16_t *b = (const uint16_t *)B;
+    return oracle_half_to_double(rowmajor ? b[k * ldb + j] : b[j * ldb + k]);
+}
+
+static int64_t b_i8(const void *B, int64_t ldb, int rowmajor, int64_t k, int64_t j)
+{
+    const int8_t *b = (const int8_t *)B;
+    return rowmajor ? b[k * ldb + j] : b[j * ldb + k];
+}
+
+static int64_t b_i4(const void *B, int64_t ldb, int rowmajor, int64_t k, int64_t j)
+{
+    const uint8_t *b = (const uint8_t *)B;
+    return rowmajor ? s4_at(b + k * (ldb / 2), j) : s4_at(b + j * (ldb / 2), k);
+}
+
 /* ----------------------------------------------------------------------- */
 /* Full-matrix products, row-parallel.                                      */
 
@@ -85,6 +110,7 @@ struct job {
     int64_t lda;
     const void *B;
     int64_t ldb;
+    int b_rowmajor; /* B layout: 0 column-major (K contiguous), 1 row-major */
     void *C;        /* int64_t* (int) or double* R (f16) */
     double *S;      /* f16 only */
     int64_t ldc;
@@ -94,15 +120,15 @@ struct job {
 static void one_row(const struct job *jb, int64_t i)
 {
     int64_t j, k;
+    const int rm = jb->b_rowmajor;
     if (jb->p == P_F16) {
         const uint16_t *a = (const uint16_t *)jb->A + i * jb->lda;
         double *r = (double *)jb->C + i * jb->ldc;
         double *s = jb->S + i * jb->ldc;
         for (j = 0; j < jb->N; ++j) {
-            const uint16_t *b = (const uint16_t *)jb->B + j * jb->ldb;
             double acc = 0.0, mag = 0.0;
             for (k = 0; k < jb->K; ++k) {
-                double prod = oracle_half_to_double(a[k]) * oracle_half_to_double(b[k]);
+                double prod = oracle_half_to_double(a[k]) * b_f16(jb->B, jb->ldb, rm, k, j);
                 acc += prod;
                 mag += fabs(prod);
             }
@@ -113,20 +139,18 @@ static void one_row(const struct job *jb, int64_t i)
         const int8_t *a = (const int8_t *)jb->A + i * jb->lda;
         int64_t *c = (int64_t *)jb->C + i * jb->ldc;
         for (j = 0; j < jb->N; ++j) {
-            const int8_t *b = (const int8_t *)jb->B + j * jb->ldb;
             int64_t acc = 0;
             for (k = 0; k < jb->K; ++k)
-                acc += (int64_t)a[k] * (int64_t)b[k];
+                acc += (int64_t)a[k] * b_i8(jb->B, jb->ldb, rm, k, j);
             c[j] = acc;
         }
     } else {
         const uint8_t *a = (const uint8_t *)jb->A + i * (jb->lda / 2);
         int64_t *c = (int64_t *)jb->C + i * jb->ldc;
         for (j = 0; j < jb->N; ++j) {
-            const uint8_t *b = (const uint8_t *)jb->B + j * (jb->ldb / 2);
             int64_t acc = 0;
             for (k = 0; k < jb->K; ++k)
-                acc += (int64_t)s4_at(a, k) * (int64_t)s4_at(b, k);
+                acc += (int64_t)s4_at(a, k) * b_i4(jb->B, jb->ldb, rm, k, j);
             c[j] = acc;
         }
     }
@@ -177,7 +201,7 @@ int oracle_gemm_f16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t 
                     const uint16_t *B, int64_t ldb, double *R, double *S, int64_t ldr,
                     int nthreads)
 {
-    struct job jb = {P_F16, M, N, K, A, lda, B, ldb, R, S, ldr, 0, 0};
+    struct job jb = {P_F16, M, N, K, A, lda, B, ldb, 0, R, S, ldr, 0, 0};
     return run(jb, nthreads);
 }
 
@@ -185,7 +209,7 @@ int oracle_gemm_f16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t 
 int oracle_gemm_i8(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
                    const int8_t *B, int64_t ldb, int64_t *C, int64_t ldc, int nthreads)
 {
-    struct job jb = {P_I8, M, N, K, A, lda, B, ldb, C, NULL, ldc, 0, 0};
+    struct job jb = {P_I8, M, N, K, A, lda, B, ldb, 0, C, NULL, ldc, 0, 0};
     return run(jb, nthreads);
 }
 
@@ -195,7 +219,33 @@ int oracle_gemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t ld
 {
     if ((lda & 1) || (ldb & 1))
         return ORACLE_EINVAL;
-    struct job jb = {P_I4, M, N, K, A, lda, B, ldb, C, NULL, ldc, 0, 0};
+    struct job jb = {P_I4, M, N, K, A, lda, B, ldb, 0, C, NULL, ldc, 0, 0};
+    return run(jb, nthreads);
+}
+
+/* The same three products with B row-major (element (k, j) at B[k*ldb + j],
+ * ldb >= N; INT4 packed two per byte along N, ldb in 4-bit elements). */
+int oracle_gemm_f16_rowb(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                         const uint16_t *B, int64_t ldb, double *R, double *S, int64_t ldr,
+                         int nthreads)
+{
+    struct job jb = {P_F16, M, N, K, A, lda, B, ldb, 1, R, S, ldr, 0, 0};
+    return run(jb, nthreads);
+}
+
+int oracle_gemm_i8_rowb(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
+                        const int8_t *B, int64_t ldb, int64_t *C, int64_t ldc, int nthreads)
+{
+    struct job jb = {P_I8, M, N, K, A, lda, B, ldb, 1, C, NULL, ldc, 0, 0};
+    return run(jb, nthreads);
+}
+
+int oracle_gemm_i4_rowb(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+                        const uint8_t *B, int64_t ldb, int64_t *C, int64_t ldc, int nthreads)
+{
+    if ((lda & 1) || (ldb & 1))
+        return ORACLE_EINVAL;
+    struct job jb = {P_I4, M, N, K, A, lda, B, ldb, 1, C, NULL, ldc, 0, 0};
     return run(jb, nthreads);
 }
 
@@ -249,6 +299,55 @@ int oracle_entries_i4(int64_t K, const uint8_t *A, int64_t lda, const uint8_t *B
         int64_t acc = 0;
         for (int64_t k = 0; k < K; ++k)
             acc += (int64_t)s4_at(a, k) * (int64_t)s4_at(b, k);
+        C[t] = acc;
+    }
+    return ORACLE_OK;
+}
+
+/* Single entries with B row-major (layout as for the *_rowb products). */
+int oracle_entries_f16_rowb(int64_t K, const uint16_t *A, int64_t lda, const uint16_t *B,
+                            int64_t ldb, int64_t count, const int64_t *rows,
+                            const int64_t *cols, double *R, double *S)
+{
+    for (int64_t t = 0; t < count; ++t) {
+        const uint16_t *a = A + rows[t] * lda;
+        double acc = 0.0, mag = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double prod = oracle_half_to_double(a[k]) * b_f16(B, ldb, 1, k, cols[t]);
+            acc += prod;
+            mag += fabs(prod);
+        }
+        R[t] = acc;
+        S[t] = mag;
+    }
+    return ORACLE_OK;
+}
+
+int oracle_entries_i8_rowb(int64_t K, const int8_t *A, int64_t lda, const int8_t *B,
+                           int64_t ldb, int64_t count, const int64_t *rows,
+                           const int64_t *cols, int64_t *C)
+{
+    for (int64_t t = 0; t < count; ++t) {
+        const int8_t *a = A + rows[t] * lda;
+        int64_t acc = 0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += (int64_t)a[k] * b_i8(B, ldb, 1, k, cols[t]);
+        C[t] = acc;
+    }
+    return ORACLE_OK;
+}
+
+int oracle_entries_i4_rowb(int64_t K, const uint8_t *A, int64_t lda, const uint8_t *B,
+                           int64_t ldb, int64_t count, const int64_t *rows,
+                           const int64_t *cols, int64_t *C)
+{
+    if ((lda & 1) || (ldb & 1))
+        return ORACLE_EINVAL;
+    for (int64_t t = 0; t < count; ++t) {
+        const uint8_t *a = A + rows[t] * (lda / 2);
+        int64_t acc = 0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += (int64_t)s4_at(a, k) * b_i4(B, ldb, 1, k, cols[t]);
         C[t] = acc;
     }
     return ORACLE_OK;

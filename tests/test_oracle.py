@@ -319,9 +319,95 @@ def pin_dequant():
     assert np.array_equal(goth.view(np.uint16), wanth.view(np.uint16))
 
 
+def _exact_eval_rowb(prec, A, B, N, K):
+    """Independent evaluator for B row-major: B[k][j], Python ints / Fractions."""
+    M = A.shape[0]
+    if prec == "i4":
+        Au = synth.unpack_int4(A).astype(int).tolist()
+        Bu = synth.unpack_int4(B).astype(int).tolist()
+    elif prec == "i8":
+        Au, Bu = A.astype(int).tolist(), B.astype(int).tolist()
+    else:
+        Au = [[Fraction(float(v)) for v in row] for row in A]
+        Bu = [[Fraction(float(v)) for v in row] for row in B]
+    C = [[sum((Au[i][k] * Bu[k][j] for k in range(K)), 0) for j in range(N)] for i in range(M)]
+    S = [[sum((abs(Au[i][k] * Bu[k][j]) for k in range(K)), 0) for j in range(N)] for i in range(M)]
+    return C, S
+
+
+def pin_rowb():
+    """B row-major (element (k, j) at B[k*ldb + j]; INT4 packed along N)."""
+    # the PTX tutorial's worked example is stated with B as a K x N row-major matrix
+    g, A, Bmat = _lab_operands()
+    R, _ = oracle.gemm_f16_rowb(A.astype(np.float16), Bmat.astype(np.float16))
+    for r, c, v in g["printed_entries"]:
+        assert R[r, c] == v
+    _, Ar, _ = _lab_operands(reverse_rows=True)
+    R2, _ = oracle.gemm_f16_rowb(Ar.astype(np.float16), Bmat.astype(np.float16))
+    assert list(R2[0]) == g["row_reversed_A_first_row"]
+    M, N, K = g["M"], g["N"], g["K"]
+    B8 = np.array([[8 * r + c - 64 for c in range(N)] for r in range(K)], dtype=np.int8)
+    assert np.array_equal(oracle.gemm_i8_rowb(A.astype(np.int8), B8), B8.astype(np.int64))
+    B4 = np.array([[((8 * r + c) % 16) - 8 for c in range(N)] for r in range(K)], dtype=np.int8)
+    C4 = oracle.gemm_i4_rowb(synth.pack_int4(A.astype(np.int8)), synth.pack_int4(B4))
+    assert np.array_equal(C4, B4.astype(np.int64))
+    # INT4 nibble order along N: a one-hot A row picks one row of B, value by value
+    w = np.arange(-8, 8, dtype=np.int8)
+    Bw = synth.pack_int4(np.stack([w, np.zeros(16, np.int8), w[::-1]]))   # 3 rows x 16 columns
+    for k, want in ((0, w), (1, np.zeros(16)), (2, w[::-1])):
+        a = np.zeros((1, 4), np.int8)
+        a[0, k] = 1
+        assert np.array_equal(oracle.gemm_i4_rowb(synth.pack_int4(a), Bw, K=3)[0], want)
+    a = synth.pack_int4(np.array([[0, 0, -3, 0]], np.int8))
+    assert np.array_equal(oracle.gemm_i4_rowb(a, Bw, K=3)[0], -3 * w[::-1].astype(np.int64))
+    # brute force on tiny shapes; columns past N and rows past K hold poison
+    rng = np.random.default_rng(17)
+    for m, n, k in [(m, n, k) for m in (1, 2, 5) for n in range(1, 7) for k in range(1, 7)]:
+        b8 = rng.integers(-128, 128, (k, n), dtype=np.int8)
+        a8 = rng.integers(-128, 128, (m, k), dtype=np.int8)
+        b8p = np.vstack([_padded(b8, n + 3, 127), np.full((2, n + 3), -128, np.int8)])
+        C = oracle.gemm_i8_rowb(_padded(a8, k + 1, 127), b8p, N=n, K=k)
+        assert C.tolist() == _exact_eval_rowb("i8", a8, b8, n, k)[0], ("i8", m, n, k)
+        n4 = 2 * n
+        b4 = rng.integers(-8, 8, (k, n4), dtype=np.int8)
+        a4 = rng.integers(-8, 8, (m, 2 * k), dtype=np.int8)
+        b4p = np.vstack([_padded(synth.pack_int4(b4), n + 2, 0x77), np.full((2, n + 2), 0x88, np.uint8)])
+        C4 = oracle.gemm_i4_rowb(_padded(synth.pack_int4(a4), k + 1, 0x77), b4p, N=n4, K=k)
+        E4 = _exact_eval_rowb("i4", synth.pack_int4(a4), synth.pack_int4(b4), n4, k)[0]
+        assert C4.tolist() == E4, ("i4", m, n4, k)
+        if n4 > 1:   # odd N: the last byte's high nibble is outside
+            C4o = oracle.gemm_i4_rowb(_padded(synth.pack_int4(a4), k + 1, 0x77), b4p, N=n4 - 1, K=k)
+            assert C4o.tolist() == [row[:n4 - 1] for row in E4], ("i4 odd N", m, n4, k)
+        bh = rng.uniform(-2, 2, (k, n)).astype(np.float16)
+        ah = rng.uniform(-2, 2, (m, k)).astype(np.float16)
+        bhp = np.vstack([_padded(bh, n + 2, np.float16(np.inf)),
+                         np.full((1, n + 2), np.nan, np.float16)])
+        R, S = oracle.gemm_f16_rowb(_padded(ah, k + 2, np.float16(np.nan)), bhp, N=n, K=k)
+        Eh, Sh = _exact_eval_rowb("f16", ah, bh, n, k)
+        for i in range(m):
+            for j in range(n):
+                assert abs(Fraction(R[i, j]) - Eh[i][j]) <= Fraction(k, 2 ** 52) * Sh[i][j]
+                assert abs(Fraction(S[i, j]) - Sh[i][j]) <= Fraction(k, 2 ** 52) * Sh[i][j]
+    # entry-wise forms agree with the full products
+    A8, B8t = synth.operands("i8", 37, 45, 70, 3, 4)
+    B8r = np.ascontiguousarray(B8t.T)
+    full = oracle.gemm_i8_rowb(A8, B8r)
+    rows, cols = rng.integers(0, 37, 50), rng.integers(0, 45, 50)
+    assert np.array_equal(oracle.entries_i8_rowb(A8, B8r, rows, cols), full[rows, cols])
+    A4, _ = synth.operands("i4", 37, 45, 70, 5, 6)
+    B4r = synth.pack_int4(rng.integers(-8, 8, (70, 46), dtype=np.int8))
+    full4 = oracle.gemm_i4_rowb(A4, B4r)
+    assert np.array_equal(oracle.entries_i4_rowb(A4, B4r, rows, cols), full4[rows, cols])
+    Ah, Bht = synth.operands("f16", 37, 45, 70, 7, 8)
+    Bhr = np.ascontiguousarray(Bht.T)
+    Rf, Sf = oracle.gemm_f16_rowb(Ah, Bhr)
+    Re, Se = oracle.entries_f16_rowb(Ah, Bhr, rows, cols)
+    assert np.array_equal(Re, Rf[rows, cols]) and np.array_equal(Se, Sf[rows, cols])
+
+
 PINS = [pin_half_decoder, pin_mma_lab_f16, pin_mma_lab_integer, pin_closed_forms,
         pin_identities, pin_brute_force_tiny, pin_product_tables, pin_invariants,
-        pin_half_rounding, pin_dequant]
+        pin_half_rounding, pin_dequant, pin_rowb]
 
 
 # --------------------------------------------------------------------------

@@ -22,17 +22,20 @@ MUTANTS = {
     "subnormal_scale": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
     "exponent_bias": ("ldexp((double)(1024 + frac), expo - 25)", "ldexp((double)(1024 + frac), expo - 24)"),
     "hidden_bit": ("(double)(1024 + frac)", "(double)(frac)"),
-    "transposed_B_i8": ("acc += (int64_t)a[k] * (int64_t)b[k];\n            c[j] = acc;\n        }\n    } else {",
-                        "acc += (int64_t)a[k] * (int64_t)((const int8_t *)jb->B)[k * jb->ldb + j];\n"
-                        "            c[j] = acc;\n        }\n    } else {"),
-    "B_uses_lda": ("const int8_t *b = (const int8_t *)jb->B + j * jb->ldb;",
-                   "const int8_t *b = (const int8_t *)jb->B + j * jb->lda;"),
+    "transposed_B_i8": ("    return rowmajor ? b[k * ldb + j] : b[j * ldb + k];",
+                        "    return rowmajor ? b[k * ldb + j] : b[k * ldb + j];"),
+    "B_uses_lda": ("b_i8(jb->B, jb->ldb, rm, k, j)", "b_i8(jb->B, jb->lda, rm, k, j)"),
     "i4_byte_stride": ("const uint8_t *a = (const uint8_t *)jb->A + i * (jb->lda / 2);",
                        "const uint8_t *a = (const uint8_t *)jb->A + i * jb->lda;"),
     "magnitude_signed": ("mag += fabs(prod);\n            }\n            r[j]", "mag += prod;\n            }\n            r[j]"),
     "subtract_product": ("acc += prod;\n                mag", "acc -= prod;\n                mag"),
-    "f16_B_uses_lda": ("const uint16_t *b = (const uint16_t *)jb->B + j * jb->ldb;",
-                       "const uint16_t *b = (const uint16_t *)jb->B + j * jb->lda;"),
+    "f16_B_uses_lda": ("b_f16(jb->B, jb->ldb, rm, k, j)", "b_f16(jb->B, jb->lda, rm, k, j)"),
+    "rowb_f16_as_colmajor": ("oracle_half_to_double(rowmajor ? b[k * ldb + j] : b[j * ldb + k])",
+                             "oracle_half_to_double(rowmajor ? b[j * ldb + k] : b[j * ldb + k])"),
+    "rowb_i4_packed_along_k": ("rowmajor ? s4_at(b + k * (ldb / 2), j)", "rowmajor ? s4_at(b + j * (ldb / 2), k)"),
+    "rowb_i8_wrong_stride": ("    return rowmajor ? b[k * ldb + j] : b[j * ldb + k];",
+                             "    return rowmajor ? b[k * (ldb - 1) + j] : b[j * ldb + k];"),
+    "rowb_entries_colmajor": ("b_i8(B, ldb, 1, k, cols[t])", "b_i8(B, ldb, 0, k, cols[t])"),
     "dequant_swapped_scales": ("float c = dequant(S[i * lds + j], scale_a[i], scale_b[j]);",
                                "float c = dequant(S[i * lds + j], scale_a[j % M], scale_b[i % N]);"),
     "dequant_scale_product_first": ("    c = c * sa;\n    c = c * sb;", "    c = c * (sa * sb);"),
