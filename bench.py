@@ -18,6 +18,15 @@ HBM before the timed region starts.  The JSON line reports:
                 dequantizing epilogue, ((float)S * scale_a[i]) * scale_b[j]
                 rounded to binary16, timed back to back alternately with the
                 plain GEMM (medians of 3), with a bit-exact sampled parity check
+  layout        (outside the step) the N = 8192 GEMMs with B row-major (the
+                paper's "transposed B", read with transposing LDS loads), timed
+                back to back alternately with the column-major B kernel (medians
+                of 3), checked bit-equal to it and against the oracle
+  shapes        (outside the step) non-square inference shapes M x 8192 x 8192,
+                M in {16, 64, 256, 1024}: the first M rows of the sweep's
+                N = 8192 operands, timed back to back and placed on their own
+                roofline (HBM-bound below about M = 315 for f16 and i8, 157 for
+                i4), with a sampled parity check
 
 Usage: python bench.py [--steps K] [--warmup W] [--case f16:8192] [--calib-copy]
 """
@@ -68,6 +77,10 @@ def parse():
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--no-dequant", action="store_true",
                     help="skip the dequantizing-epilogue measurement")
+    ap.add_argument("--no-shapes", action="store_true",
+                    help="skip the non-square (small M) measurement")
+    ap.add_argument("--no-layout", action="store_true",
+                    help="skip the row-major-B measurement")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of C per GEMM for the CPU baseline (default 192)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -115,6 +128,26 @@ def trace_summary(path):
 
 def gemm_ops(n):
     return 2.0 * n * n * n
+
+
+SHAPE_MS = (16, 64, 256, 1024)   # rows of A for the non-square shapes M x 8192 x 8192
+
+
+def shape_roofline(prec, M, N, K, ms):
+    """Achieved rate of one M x N x K GEMM against the roof that bounds it: HBM for
+    algorithmic bytes / peak bandwidth above flops / peak MFMA, else MFMA."""
+    flops = 2.0 * M * N * K
+    nbytes = M * K * IN_BYTES[prec] + K * N * IN_BYTES[prec] + 4.0 * M * N
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (PEAK[prec] * 1e12)
+    tops = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    if t_hbm >= t_mfma:
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "tops": round(tops, 2)}
+    return {"bound": "mfma", "achieved": round(tops, 2), "peak": PEAK[prec],
+            "unit": "TFLOP/s" if prec == "f16" else "TOPS", "frac": round(tops / PEAK[prec], 4),
+            "gbs": round(gbs, 1)}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_n8192_hbm_counters.txt")
@@ -309,6 +342,87 @@ def main():
             log(f"[bench] dequant {prec} N={n}: {ms_d:.4f} ms (plain {ms_r:.4f} ms)")
             del Ch, sad, sbd
 
+    # ---- B row-major at N = 8192 (not part of the step) ----
+    layout = {}
+    if not args.no_layout:
+        for prec, n, Ad, Bd, C in work:
+            if n != 8192:
+                continue
+            A, Bt = host[(prec, n)]
+            if prec == "i4":
+                Brow = synth.pack_int4(np.ascontiguousarray(synth.unpack_int4(Bt).T))
+            else:
+                Brow = np.ascontiguousarray(Bt.T)
+            Brd = torch.from_numpy(Brow).to(dev)
+            Cr = torch.empty_like(C)
+            go = pd.prepare(prec, Ad, Brd, Cr, K=n, rowb=True)
+            launchers[(prec, n)]()
+            torch.cuda.synchronize()
+            entry = {"same_as_column_major": bool(torch.equal(Cr.view(torch.int32), C.view(torch.int32)))}
+            if not args.no_parity:
+                import oracle
+                rng = np.random.default_rng(n + 2)
+                rows, cols = rng.integers(0, n, 256), rng.integers(0, n, 256)
+                got = Cr.cpu().numpy()[rows, cols]
+                if prec == "f16":
+                    R, S = oracle.entries_f16_rowb(A, Brow, rows, cols)
+                    ok = bool(np.all(np.abs(got.astype(np.float64) - R) <= 1e-3 * S))
+                else:
+                    ref = (oracle.entries_i8_rowb if prec == "i8" else oracle.entries_i4_rowb)(
+                        A, Brow, rows, cols)
+                    ok = bool(np.array_equal(got.astype(np.int64), ref))
+                entry["parity"] = ok and entry["same_as_column_major"]
+                parity[f"{prec}:{n}:rowb"] = entry["parity"]
+            rs, cs = [], []
+            for _ in range(3):
+                rs.append(time_b2b(go, b2b[(prec, n)]))
+                cs.append(time_b2b(launchers[(prec, n)], b2b[(prec, n)]))
+            ms_r, ms_c = float(np.median(rs)), float(np.median(cs))
+            entry.update({
+                "ms_back_to_back": round(ms_r, 5),
+                "tops_back_to_back": round(gemm_ops(n) / (ms_r * 1e-3) / 1e12, 2),
+                "frac_of_peak": round(gemm_ops(n) / (ms_r * 1e-3) / 1e12 / PEAK[prec], 4),
+                "column_major_ms_back_to_back": round(ms_c, 5),
+                "time_vs_column_major": round(ms_r / ms_c, 4),
+            })
+            layout[f"{prec}:{n}"] = entry
+            log(f"[bench] row-major B {prec} N={n}: {ms_r:.4f} ms (column-major {ms_c:.4f} ms)")
+            del Brd, Cr
+
+    # ---- non-square inference shapes (not part of the step) ----
+    shapes = {}
+    if not args.no_shapes:
+        for prec, n, Ad, Bd, C in work:
+            if n != 8192:
+                continue
+            for M in SHAPE_MS:
+                Cm = torch.empty((M, n), dtype=C.dtype, device=dev)
+                go = pd.prepare(prec, Ad[:M], Bd, Cm, K=n)
+                torch.cuda.synchronize()
+                entry = {"M": M, "N": n, "K": n,
+                         "cfg": pd.pick_config({"f16": 0, "i8": 1, "i4": 2}[prec], M, n, n)}
+                if not args.no_parity:
+                    import oracle
+                    A, Bt = host[(prec, n)]
+                    rng = np.random.default_rng(M)
+                    rows, cols = rng.integers(0, M, 256), rng.integers(0, n, 256)
+                    got = Cm.cpu().numpy()[rows, cols]
+                    if prec == "f16":
+                        R, S = oracle.entries_f16(A, Bt, rows, cols)
+                        ok = bool(np.all(np.abs(got.astype(np.float64) - R) <= 1e-3 * S))
+                    else:
+                        ref = (oracle.entries_i8 if prec == "i8" else oracle.entries_i4)(A, Bt, rows, cols)
+                        ok = bool(np.array_equal(got.astype(np.int64), ref))
+                    entry["parity"] = ok
+                    parity[f"{prec}:{M}x{n}x{n}"] = ok
+                ms = time_b2b(go, 0.05)
+                entry["ms_back_to_back"] = round(ms, 5)
+                entry["roofline"] = shape_roofline(prec, M, n, n, ms)
+                shapes[f"{prec}:{M}x{n}x{n}"] = entry
+                log(f"[bench] shape {prec} {M}x{n}x{n}: {ms * 1e3:.1f} us "
+                    f"({entry['roofline']['bound']} {entry['roofline']['frac']:.3f})")
+                del Cm
+
     per = {}
     for (prec, n), pairs in ev.items():
         ms = float(np.mean([s.elapsed_time(e) for s, e in pairs])) if pairs else float("nan")
@@ -408,6 +522,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "dequant": dequant or None,
+        "layout": layout or None,
+        "shapes": shapes or None,
     }
     print(json.dumps(out), flush=True)
     if parity and not all(parity.values()):

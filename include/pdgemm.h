@@ -43,7 +43,11 @@
  * multiple of 16 bytes (f16: lda, ldb % 8 == 0; i8: % 16; i4: % 32); C
  * 4-byte aligned with any ldc >= N.  A row of A, B or C (lda, ldb, ldc
  * elements) may span at most 4 MiB.  M, N and K are otherwise arbitrary:
- * partial tiles are masked inside the kernels.
+ * partial tiles are masked inside the kernels.  Operands are read in
+ * 16-byte chunks: the chunk that holds the last element of a row may be read
+ * whole (it never crosses the 16-byte granule of the allocation, since bases
+ * and row spans are multiples of 16), and values outside the M x K and
+ * K x N extents never reach a stored result.
  *
  * Ownership and execution: every pointer is device memory owned by the
  * caller.  The library never allocates, frees, copies or synchronizes.  The
@@ -70,7 +74,7 @@ extern "C" {
 
 #define PDGEMM_OK 0
 #define PDGEMM_EINVAL_DIM (-1)  /* M, N or K negative, or gemm_i4 K > 131071 */
-#define PDGEMM_EINVAL_LD (-2)   /* lda < K, ldb < K, ldc < N, or a row of A, B or C above 4 MiB */
+#define PDGEMM_EINVAL_LD (-2)   /* lda < K, ldb < K (row-major B: ldb < N), ldc < N, or a row above 4 MiB */
 #define PDGEMM_ENULL (-3)       /* NULL pointer for an operand with nonzero extent */
 #define PDGEMM_EINVAL_I4 (-4)   /* gemm_i4: K, lda or ldb odd */
 #define PDGEMM_EALIGN (-5)      /* a pointer or leading dimension breaks the alignment rules */
@@ -116,6 +120,24 @@ int gemm_i4_dequant(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t l
                     const uint8_t *B, int64_t ldb, const float *scale_a, const float *scale_b,
                     void *C, int64_t ldc, int out_f16, void *stream);
 
+/* C = A * B with B row-major (N-contiguous): element (k, j) of B at
+ * B[k*ldb + j] with ldb >= N.  This is the "transposed B" layout of the
+ * paper's loader ablation (Section IV-D, Run 4), which it finds slower than
+ * the column-major B of the entry points above; here the kernels read it with
+ * gfx950's transposing LDS loads, so both layouts feed the same MFMAs.
+ * gemm_i4_rowb: B packs two signed 4-bit values per byte along N (element j
+ * of a row in byte j/2, low nibble for even j); ldb counts 4-bit elements and
+ * must be even, K must be even (A's packing), N may be odd.  Other
+ * arguments, alignment (ldb spans a multiple of 16 bytes), results and
+ * errors as gemm_f16 / gemm_i8 / gemm_i4, with ldb < N giving
+ * PDGEMM_EINVAL_LD. */
+int gemm_f16_rowb(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                  const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream);
+int gemm_i8_rowb(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
+                 const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream);
+int gemm_i4_rowb(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+                 const uint8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream);
+
 /* Precision ids and tile configurations, for the calls below. */
 #define PDGEMM_PREC_F16 0
 #define PDGEMM_PREC_I8 1
@@ -128,6 +150,11 @@ int gemm_i4_dequant(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t l
 int pdgemm_gemm_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K,
                     const void *A, int64_t lda, const void *B, int64_t ldb,
                     void *C, int64_t ldc, void *stream);
+
+/* The row-major-B GEMM with an explicit tile configuration. */
+int pdgemm_gemm_rowb_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K, const void *A,
+                         int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc,
+                         void *stream);
 
 /* The dequantizing GEMM with an explicit tile configuration (prec is
  * PDGEMM_PREC_I8 or PDGEMM_PREC_I4; FP16 returns PDGEMM_EINVAL_CFG). */

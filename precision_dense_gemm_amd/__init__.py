@@ -13,6 +13,9 @@ Operands are torch tensors on the GPU whose rows are contiguous in K:
          transpose (ldb = Bt.stride(0))
     out  (M, N) row-major (ldc = out.stride(0)); allocated when omitted
 
+With the *_rowb functions B is instead a (K, N) row-major tensor
+(ldb = B.stride(0)); INT4 packs it along N, (K, N/2) bytes.
+
 INT4 operands are uint8 tensors of packed bytes, (rows, K/2), two signed
 4-bit values per byte with the even k in the low nibble; K is passed
 explicitly and the leading dimensions are counted in 4-bit elements.
@@ -47,6 +50,11 @@ for _name in ("gemm_f16", "gemm_i8", "gemm_i4"):
 for _name in ("gemm_i8_dequant", "gemm_i4_dequant"):
     getattr(lib, _name).argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i64, _i, _p]
     getattr(lib, _name).restype = _i
+for _name in ("gemm_f16_rowb", "gemm_i8_rowb", "gemm_i4_rowb"):
+    getattr(lib, _name).argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+    getattr(lib, _name).restype = _i
+lib.pdgemm_gemm_rowb_cfg.argtypes = [_i, _i, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+lib.pdgemm_gemm_rowb_cfg.restype = _i
 lib.pdgemm_dequant_cfg.argtypes = [_i, _i, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i64,
                                    _i, _p]
 lib.pdgemm_dequant_cfg.restype = _i
@@ -123,13 +131,22 @@ def _scale(t: torch.Tensor, n: int, name: str) -> int:
     return t.data_ptr()
 
 
-def _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None):
+def _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None, N=None, rowb=False):
     """The C function and its argument tuple for one GEMM (dequantizing when
-    scales = (scale_a, scale_b) is given)."""
-    M, N = A.shape[0], Bt.shape[0]
+    scales = (scale_a, scale_b) is given; B row-major when rowb, with N given)."""
+    M = A.shape[0]
+    N = Bt.shape[0] if N is None else N
     ldc = _row_major_2d(out, "out")
     if tuple(out.shape) != (M, N):
         raise ValueError(f"out must have shape {(M, N)}")
+    if rowb:
+        if scales is not None:
+            raise ValueError("the dequantizing epilogue takes a column-major B")
+        args = (M, N, K, A.data_ptr(), lda, Bt.data_ptr(), ldb, out.data_ptr(), ldc,
+                _stream(stream))
+        if cfg is None:
+            return (lib.gemm_f16_rowb, lib.gemm_i8_rowb, lib.gemm_i4_rowb)[prec], args
+        return lib.pdgemm_gemm_rowb_cfg, (prec, cfg) + args
     if scales is None:
         args = (M, N, K, A.data_ptr(), lda, Bt.data_ptr(), ldb, out.data_ptr(), ldc,
                 _stream(stream))
@@ -148,8 +165,8 @@ def _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None):
     return lib.pdgemm_dequant_cfg, (prec, cfg) + args
 
 
-def _call(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None):
-    fn, args = _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales)
+def _call(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None, N=None, rowb=False):
+    fn, args = _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales, N, rowb)
     rc = fn(*args)
     if rc != 0:
         raise PdgemmError(rc)
@@ -205,6 +222,46 @@ def gemm_i4(A: torch.Tensor, Bt: torch.Tensor, K: int | None = None,
     return _call(PREC_I4, A, Bt, out, K, lda, ldb, stream, cfg)
 
 
+_DTYPES = {"f16": (torch.float16, torch.float32, PREC_F16), "i8": (torch.int8, torch.int32, PREC_I8),
+           "i4": (torch.uint8, torch.int32, PREC_I4)}
+
+
+def _gemm_rowb(prec, A, B, K, N, out, stream, cfg):
+    in_t, out_t, p = _DTYPES[prec]
+    if A.dtype != in_t or B.dtype != in_t:
+        raise TypeError(f"{prec} with row-major B takes {in_t} operands")
+    per = 2 if prec == "i4" else 1
+    K = per * A.shape[1] if K is None else K
+    N = per * B.shape[1] if N is None else N
+    if per * A.shape[1] < K or B.shape[0] < K or per * B.shape[1] < N:
+        raise ValueError("operands hold fewer than K values per row of A, K rows of B or N columns")
+    lda, ldb = per * _row_major_2d(A, "A"), per * _row_major_2d(B, "B")
+    if out is None:
+        out = torch.empty((A.shape[0], N), dtype=out_t, device=A.device)
+    elif out.dtype != out_t:
+        raise TypeError(f"{prec} writes a {out_t} output")
+    return _call(p, A, B, out, K, lda, ldb, stream, cfg, N=N, rowb=True)
+
+
+def gemm_f16_rowb(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None,
+                  stream=None, cfg: int | None = None) -> torch.Tensor:
+    """C = A * B for binary16 A (M, K) and row-major B (K, N); fp32 C (M, N)."""
+    return _gemm_rowb("f16", A, B, None, None, out, stream, cfg)
+
+
+def gemm_i8_rowb(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None,
+                 stream=None, cfg: int | None = None) -> torch.Tensor:
+    """C = A * B for int8 A (M, K) and row-major B (K, N); int32 C (M, N)."""
+    return _gemm_rowb("i8", A, B, None, None, out, stream, cfg)
+
+
+def gemm_i4_rowb(A: torch.Tensor, B: torch.Tensor, K: int | None = None, N: int | None = None,
+                 out: torch.Tensor | None = None, stream=None,
+                 cfg: int | None = None) -> torch.Tensor:
+    """C = A * B for packed INT4 A (M, K/2) and row-major B (K, N/2 bytes, packed along N)."""
+    return _gemm_rowb("i4", A, B, K, N, out, stream, cfg)
+
+
 def gemm_i8_dequant(A: torch.Tensor, Bt: torch.Tensor, scale_a: torch.Tensor,
                     scale_b: torch.Tensor, out: torch.Tensor | None = None,
                     out_dtype: torch.dtype = torch.float32, stream=None,
@@ -240,7 +297,7 @@ def gemm_i4_dequant(A: torch.Tensor, Bt: torch.Tensor, scale_a: torch.Tensor,
 
 
 def prepare(prec: str, A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor, K: int | None = None,
-            stream=None, cfg: int | None = None, scales=None):
+            stream=None, cfg: int | None = None, scales=None, rowb: bool = False):
     """Check and marshal one GEMM once; return a no-argument callable that
     enqueues it again (on the stream current now) through the C ABI.
 
@@ -248,7 +305,8 @@ def prepare(prec: str, A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor, K: 
     callable skips the per-call Python checks, so host time stays far below
     the kernel time even for small shapes.  The tensors must stay alive.
     With scales = (scale_a, scale_b) an INT8 / INT4 GEMM is the dequantizing
-    one, and out is float32 or float16.
+    one, and out is float32 or float16.  With rowb, Bt is a row-major B
+    (K, N) instead (INT4: packed along N) and N is out's column count.
     """
     integer_out = (torch.int32,) if scales is None else (torch.float32, torch.float16)
     if prec == "f16":
@@ -268,9 +326,15 @@ def prepare(prec: str, A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor, K: 
         lda, ldb, p = 2 * _row_major_2d(A, "A"), 2 * _row_major_2d(Bt, "Bt"), PREC_I4
     else:
         raise ValueError(f"unknown precision {prec!r}")
-    if A.shape[1] * (2 if prec == "i4" else 1) < K or Bt.shape[1] * (2 if prec == "i4" else 1) < K:
+    per = 2 if prec == "i4" else 1
+    N = out.shape[1]
+    if rowb:
+        if A.shape[1] * per < K or Bt.shape[0] < K or Bt.shape[1] * per < N:
+            raise ValueError("operands hold fewer than K values per row of A, K rows of B or N columns")
+    elif A.shape[1] * per < K or Bt.shape[1] * per < K:
         raise ValueError("operands hold fewer than K values per row")
-    fn, args = _marshal(p, A, Bt, out, K, lda, ldb, stream, cfg, scales)
+    fn, args = _marshal(p, A, Bt, out, K, lda, ldb, stream, cfg, scales, N=N if rowb else None,
+                        rowb=rowb)
     rc = fn(*args)  # validates the arguments once, and is a first launch
     if rc != 0:
         raise PdgemmError(rc)

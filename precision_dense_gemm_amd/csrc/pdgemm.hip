@@ -1,37 +1,42 @@
 // pdgemm.hip -- multi-precision dense GEMM kernels for gfx950 (MI355X) and the
 // C ABI declared in include/pdgemm.h.
 //
-// C = A * B with A row-major (M x K), B column-major (K x N) and C row-major,
-// in FP16 -> fp32, INT8 -> int32 and packed signed INT4 -> int32.
+// C = A * B with A row-major (M x K), B column-major or row-major (K x N) and
+// C row-major, in FP16 -> fp32, INT8 -> int32 and packed signed INT4 -> int32,
+// optionally followed (integer paths) by a dequantizing epilogue.
 //
 // The method is the tiled matrix-unit GEMM of "Hand-Written PTX Tensor-Core
 // GEMM Kernels: A Multi-Precision Study on NVIDIA L4": a block tile of C per
 // workgroup, a loop over K tiles that are staged from global memory into
-// double-buffered shared memory while the previous tile feeds the matrix
-// units (Section II-B, Listing 1), fragments read from shared memory into
-// registers (Listing 2), and the matrix multiply-accumulate itself
-// (Section II-A).  Its design targets the L4; this file keeps the structure
-// and re-derives every choice for CDNA4:
+// shared memory while earlier tiles feed the matrix units (Section II-B,
+// Listing 1), fragments read from shared memory into registers (Listing 2),
+// and the matrix multiply-accumulate itself (Section II-A).  Its design
+// targets the L4; this file keeps the structure and re-derives every choice
+// for CDNA4:
 //
 //  * Matrix units: v_mfma_f32_32x32x16_f16 and v_mfma_i32_32x32x32_i8.  Both
-//    consume, per lane, 16 contiguous bytes of one row of A and of one column
-//    of B (32 rows x 32 bytes of K per instruction), so FP16, INT8 and
-//    unpacked INT4 share one LDS geometry: a K tile is 128 bytes per row.
+//    take, per lane, 16 contiguous bytes of K of one row of A and of one
+//    column of B, so FP16, INT8 and packed INT4 share one LDS geometry: a K
+//    tile is 64 bytes of K per row of A (32 f16, 64 int8, 128 int4 values).
 //  * INT4: gfx950 has no signed 4-bit MFMA (the paper's m16n8k64.s4 path,
-//    Listing 2, has no equivalent here).  Each packed dword w is split in
-//    registers, on its way from global memory to LDS, into two int8 planes:
-//    (w << 4) & 0xF0F0F0F0 holds 16*a for the even k and w & 0xF0F0F0F0 holds
-//    16*a for the odd k, each as a signed byte.  A and B are split the same
-//    way, so the planes pair k with k; every product is 256*a*b and the int32
-//    sum is exactly 256*C (no overflow while 16384*K < 2^31, K <= 131071).
-//    The epilogue shifts right by 8, which is exact.
-//  * Staging: 16-byte global loads, coalesced along K (A rows and B columns
-//    are both K-contiguous: the paper's "non-transposed B", Section IV-D),
-//    into registers and then LDS, two LDS stages.  The 16-byte chunks of each
-//    128-byte LDS row are XOR-swizzled by the row index so that the fragment
-//    reads of consecutive rows fall in different banks (the paper pads shared
-//    rows for the same reason on its first page's coalescing discussion; a
-//    swizzle keeps rows dense).
+//    Listing 2, has no equivalent here).  INT4 stays packed in LDS; after a
+//    fragment read each packed dword w is split in registers into two int8
+//    planes: (w << 4) & 0xF0F0F0F0 holds 16*a for the even k and
+//    w & 0xF0F0F0F0 holds 16*a for the odd k, each as a signed byte.  A and B
+//    are split the same way, so the planes pair k with k; every product is
+//    256*a*b and the int32 sum is exactly 256*C (no overflow while
+//    16384*K < 2^31, K <= 131071).  The epilogue shifts right by 8 (exact).
+//  * Staging: buffer_load_dwordx4 ... lds, a direct global -> LDS copy in
+//    16-byte chunks, four stages deep.  The 16-byte chunks of each LDS row are
+//    XOR-swizzled by the row index so that fragment reads are free of bank
+//    conflicts (the paper pads shared rows for the same purpose; a swizzle
+//    keeps rows dense).
+//  * B layouts: K-contiguous (column-major, the paper's "non-transposed B"
+//    that its Section IV-D ablation finds fastest) is staged like A.
+//    N-contiguous (row-major, the "transposed B" of the same ablation) is
+//    staged as K rows of the tile and read with gfx950's transposing LDS reads
+//    (ds_read_b64_tr_b16 / _b8 / _b4), which hand each lane K-contiguous
+//    values of its own column: the same fragments, no transposition pass.
 //  * Tiles: a workgroup of 4 waves computes a BM x BN block of C, each wave a
 //    WM x WN sub-block made of (WM/32) x (WN/32) MFMA tiles held in
 //    accumulator registers for the whole K loop.
@@ -39,10 +44,12 @@
 //    XCDs, so the block id is remapped to give each XCD a contiguous range of
 //    tiles, and tiles are ordered in bands of GM block rows so that the
 //    workgroups resident on one XCD share A and B panels in its L2.
-//  * Ragged edges: rows of A / columns of B past M / N are clamped to the
-//    last valid one (their results are discarded); the last K tile loads
-//    only bytes below K and zero-fills the rest, so no access leaves the
-//    operands' valid extents.
+//  * Ragged edges: rows of A (and columns of a column-major B) past M / N are
+//    clamped to the last valid one, and the columns of a row-major B past N
+//    are read from its padding; their results are discarded.  The buffer
+//    range of each K tile ends at the last 16-byte chunk that holds valid
+//    data, so the hardware zero-fills everything beyond it, and the last K
+//    tile's fragments are masked below K.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -55,6 +62,7 @@ namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef int intx2_t __attribute__((ext_vector_type(2)));
 typedef int intx4_t __attribute__((ext_vector_type(4)));
 typedef int intx16_t __attribute__((ext_vector_type(16)));
 
@@ -143,6 +151,34 @@ constexpr int kDequantF32 = 1;
 constexpr int kDequantF16 = 2;
 
 template <int P, int E> struct OutOf { using type = typename Prec<P>::Out; };
+
+// B layouts: K-contiguous (column-major) or N-contiguous (row-major).
+constexpr int kBCol = 0;
+constexpr int kBRow = 1;
+
+// Row-major B in LDS.  A stage holds the tile's kKRows rows of B (the K
+// values of one 64-byte K tile: 32, 64 or 128 rows), each BN values wide
+// (kCpr 16-byte chunks).  A transposing read hands each lane R consecutive
+// rows of one column: the 16 lanes of a group read R rows (f16 4, i8 8,
+// i4 16) and Q = 16/R chunks of each, so a half-wave covers 16 chunk
+// positions.  Position p of row r holds logical chunk p ^ bswizzle(r);
+// bswizzle(r) = Q * ((r / V) % (min(kCpr, 16) / Q)) with V = max(1, 16/kCpr)
+// makes the 16 positions of a half-wave fall in 16 different 16-byte bank
+// groups (64 banks), so the reads are conflict-free.
+template <int P> struct RowB {
+    static constexpr int kKRows = P == kF16 ? 32 : (P == kI8 ? 64 : 128);  // rows per K tile
+    static constexpr int kR = P == kF16 ? 4 : (P == kI8 ? 8 : 16);         // rows per read
+    static constexpr int kQ = 16 / kR;                                      // chunks per row per read
+    static constexpr int kElemPerChunk = P == kF16 ? 8 : (P == kI8 ? 16 : 32);
+};
+
+template <int P, int BN>
+__device__ __forceinline__ int bswizzle(int r) {
+    constexpr int cpr = BN / RowB<P>::kElemPerChunk;
+    constexpr int v = cpr >= 16 ? 1 : 16 / cpr;
+    constexpr int span = (cpr < 16 ? cpr : 16) / RowB<P>::kQ;
+    return RowB<P>::kQ * ((r / v) % span);
+}
 template <int P> struct OutOf<P, kDequantF32> { using type = float; };
 template <int P> struct OutOf<P, kDequantF16> { using type = _Float16; };
 
@@ -165,7 +201,7 @@ template <int P> struct OutOf<P, kDequantF16> { using type = _Float16; };
 // only for its own DMA of tile t+1 (tiles t+2 .. t+kStages-1 stay in
 // flight), so after the barrier tile t+1 is complete in LDS and stage t is
 // free for tile t+kStages.
-template <int P, int BM, int BN, int WM, int WN, int GM, int E>
+template <int P, int BM, int BN, int WM, int WN, int GM, int E, int BR>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Args args) {
     // The body uses gfx950-only types (buffer resources), which the host
     // pass cannot type-check; the host pass only needs the launch stub.
@@ -173,6 +209,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     using Acc = typename Prec<P>::Acc;
     using Out = typename OutOf<P, E>::type;
     static_assert(E == kRaw || P != kF16, "the dequantizing epilogue is for the integer paths");
+    using RB = RowB<P>;
+    constexpr int kCpr = BN / RB::kElemPerChunk;   // row-major B: 16-byte chunks per row of B
+    static_assert(BR == kBCol || (kCpr >= 2 && (kCpr & (kCpr - 1)) == 0), "row-major B tile width");
     constexpr int kWavesN = BN / WN;
     constexpr int NW = (BM / WM) * kWavesN;
     constexpr int kRows = BM + BN;           // LDS rows per stage
@@ -228,9 +267,18 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     const int n_tiles = (valid + kRowBytes - 1) / kRowBytes;
     const int valid16 = (valid + 15) & ~15;
     const uint8_t *a_base = args.A + (int64_t)m0 * args.lda_bytes;
-    const uint8_t *b_base = args.B + (int64_t)n0 * args.ldb_bytes;
     const int a_end = (int)((min(BM, M - m0) - 1) * args.lda_bytes) + valid16;
-    const int b_end = (int)((min(BN, N - n0) - 1) * args.ldb_bytes) + valid16;
+    // column-major B: like A, BN rows of K.  Row-major B: the tile's columns
+    // start n0 values into every row of B; the range ends at the last chunk
+    // of row K-1 that holds a column below N, so rows past K read as zeros.
+    const int64_t b_col_bytes = (int64_t)n0 * (P == kF16 ? 2 : 1) / (P == kI4 ? 2 : 1);
+    const uint8_t *b_base = args.B + (BR == kBRow ? b_col_bytes : (int64_t)n0 * args.ldb_bytes);
+    // bytes of the last row of B that hold columns n0 .. N-1 (INT4: an odd
+    // count of columns ends inside a byte, which still counts)
+    const int64_t b_row_valid = ((int64_t)min(BN, N - n0) * (P == kF16 ? 16 : (P == kI8 ? 8 : 4)) + 7) / 8;
+    const int64_t b_end = BR == kBRow ? (int64_t)(K - 1) * args.ldb_bytes + ((b_row_valid + 15) & ~int64_t(15))
+                                      : (int64_t)(min(BN, N - n0) - 1) * args.ldb_bytes + valid16;
+    const int64_t b_tile_bytes = BR == kBRow ? (int64_t)RB::kKRows * args.ldb_bytes : kRowBytes;
     const int lrow = lane >> 2;              // row within the 16-row group
     const int lpos = lane & 3;               // LDS position written by this lane
     uint32_t voff[kDma];
@@ -238,10 +286,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     for (int j = 0; j < kDma; ++j) {
         const int cr = (j * NW + wave) * 16 + lrow;  // row within the stage
         const int lchunk = lpos ^ swizzle(cr);       // logical chunk this lane fetches
-        if (j < kDmaA)
+        if (j < kDmaA) {
             voff[j] = (uint32_t)((min(m0 + cr, M - 1) - m0) * args.lda_bytes) + lchunk * 16;
-        else
+        } else if (BR == kBCol) {
             voff[j] = (uint32_t)((min(n0 + cr - BM, N - 1) - n0) * args.ldb_bytes) + lchunk * 16;
+        } else {
+            // flat chunk f of the B part: row f / kCpr, position f % kCpr
+            const int f = (cr - BM) * kChunks + lpos;
+            const int krow = f / kCpr;
+            const int gchunk = (f % kCpr) ^ bswizzle<P, BN>(krow);
+            voff[j] = (uint32_t)(krow * args.ldb_bytes) + gchunk * 16;
+        }
     }
 
     auto stage = [&](int t, Stage &buf) __attribute__((always_inline)) {
@@ -249,8 +304,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
         const bool live = t < n_tiles;
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(a_base + kb), (short)0, live ? a_end - kb : 0, kRsrcWord3);
+        const int64_t bt = (int64_t)t * b_tile_bytes;
+        // a row-major tile spans kKRows rows of B; the range never exceeds it
+        const int b_range = !live ? 0
+                            : BR == kBRow ? (int)min(b_end - bt, (int64_t)RB::kKRows * args.ldb_bytes)
+                                          : (int)(b_end - bt);
         const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(b_base + kb), (short)0, live ? b_end - kb : 0, kRsrcWord3);
+            (void *)(b_base + bt), (short)0, b_range, kRsrcWord3);
 #pragma unroll
         for (int j = 0; j < kDma; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kDmaA ? ra : rb,
@@ -263,12 +323,54 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     const int frow = lane & 31;              // fragment row (A) / column (B) of this lane
     const int fhalf = lane >> 5;             // which 16-byte half of a 32-byte k-step
 
+    // Row-major B: lane i of a 16-lane group points its transposing read at
+    // row kb + i / Q, bytes 8 * (i % Q) of its Q chunks, and receives the R
+    // values of column (group base + i) in rows kb .. kb + R - 1; two reads
+    // make one 16-byte fragment.  Per lane constants:
+    const int tr_i = lane & 15;
+    const int tr_row = tr_i / RB::kQ;                 // row within a read
+    const int tr_byte = 8 * (tr_i % RB::kQ);          // byte within the lane's chunks
+    const int tr_col_bytes = (16 * ((lane >> 4) & 1)) * (P == kF16 ? 2 : 1) / (P == kI4 ? 2 : 1);
+    auto read_b_rowmajor = [&](const Stage &buf, int s, int j) __attribute__((always_inline)) {
+        const char *bpart = reinterpret_cast<const char *>(&buf[BM][0]);
+        // bytes of K per k-step are 32: 16 f16, 32 int8 or 64 int4 rows, half per lane half
+        constexpr int kStepRows = RB::kKRows / 2;
+        const int col_bytes = ((wn0 + j * 32) * (P == kF16 ? 2 : 1) / (P == kI4 ? 2 : 1)) + tr_col_bytes + tr_byte;
+        uint32_t w[4];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int krow = s * kStepRows + fhalf * (kStepRows / 2) + r * RB::kR + tr_row;
+            const int pos = (col_bytes >> 4) ^ bswizzle<P, BN>(krow);
+            const char *p = bpart + (krow * kCpr + pos) * 16 + (col_bytes & 15);
+            if constexpr (P == kF16) {
+                typedef short v4s __attribute__((ext_vector_type(4)));
+                const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4s *)(p));
+                __builtin_memcpy(&w[2 * r], &v, 8);
+            } else if constexpr (P == kI8) {
+                const intx2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) intx2_t *)(p));
+                __builtin_memcpy(&w[2 * r], &v, 8);
+            } else {
+                const intx2_t v = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+                    (__attribute__((address_space(3))) intx2_t *)(p));
+                __builtin_memcpy(&w[2 * r], &v, 8);
+            }
+        }
+        return make_uint4(w[0], w[1], w[2], w[3]);
+    };
+
     auto read_frags = [&](const Stage &buf, int s, uint4 (&fa)[FM], uint4 (&fb)[FN]) __attribute__((always_inline)) {
         const int ch = (2 * s + fhalf) ^ swizzle(frow);  // fragment rows start at multiples of 32
 #pragma unroll
         for (int i = 0; i < FM; ++i) fa[i] = buf[wm0 + i * 32 + frow][ch];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) fb[j] = buf[BM + wn0 + j * 32 + frow][ch];
+        for (int j = 0; j < FN; ++j) {
+            if constexpr (BR == kBCol)
+                fb[j] = buf[BM + wn0 + j * 32 + frow][ch];
+            else
+                fb[j] = read_b_rowmajor(buf, s, j);
+        }
     };
 
     // Zero the bytes of this lane's fragments of K tile t, k-step s, that lie
@@ -341,9 +443,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     // after the barrier, the DMA of a later tile) slotted one by one between
     // them, so that no burst of memory instructions holds up MFMA issue.
     constexpr int kMfma = FM * FN * (P == kI4 ? 2 : 1);   // MFMAs per k-step
-    constexpr int kReads = FM + FN;                       // fragment reads per k-step
-    // INT4 plane split: 3 VALU per packed dword, 12 per fragment
-    constexpr int kValu = P == kI4 ? (12 * kReads + kMfma - 1) / kMfma : 0;
+    constexpr int kReads = FM + FN * (BR == kBRow ? 2 : 1);   // LDS reads per k-step
+    // VALU per k-step: the INT4 plane split (3 per packed dword, 12 per
+    // fragment) and the row-major B read addresses (about 3 per read)
+    constexpr int kValuWork = (P == kI4 ? 12 * (FM + FN) : 0) + (BR == kBRow ? 6 * FN : 0);
+    constexpr int kValu = (kValuWork + kMfma - 1) / kMfma;
     auto interleave = [&](int dma) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < kMfma; ++i) {
@@ -528,31 +632,42 @@ constexpr Config kConfigs[] = {
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
-template <int P, int C, int E>
+template <int P, int C, int E, int BR>
 const void *kernel_for() {
     constexpr Config c = kConfigs[C];
-    return reinterpret_cast<const void *>(&gemm_kernel<P, c.bm, c.bn, c.wm, c.wn, c.gm, E>);
+    return reinterpret_cast<const void *>(&gemm_kernel<P, c.bm, c.bn, c.wm, c.wn, c.gm, E, BR>);
 }
 
-template <int P, int E>
+template <int P, int E, int BR>
 const void *kernel_ptr(int cfg) {
     switch (cfg) {
-    case 0: return kernel_for<P, 0, E>();
-    case 1: return kernel_for<P, 1, E>();
-    case 2: return kernel_for<P, 2, E>();
+    case 0: return kernel_for<P, 0, E, BR>();
+    case 1: return kernel_for<P, 1, E, BR>();
+    case 2: return kernel_for<P, 2, E, BR>();
     default: return nullptr;
     }
 }
 
-const void *kernel_ptr(int prec, int cfg, int epi) {
+// Instantiated: every precision with either B layout; the dequantizing
+// epilogues with column-major B.
+const void *kernel_ptr(int prec, int cfg, int epi, int br) {
+    if (br == kBRow) {
+        if (epi != kRaw) return nullptr;
+        switch (prec) {
+        case kF16: return kernel_ptr<kF16, kRaw, kBRow>(cfg);
+        case kI8: return kernel_ptr<kI8, kRaw, kBRow>(cfg);
+        case kI4: return kernel_ptr<kI4, kRaw, kBRow>(cfg);
+        default: return nullptr;
+        }
+    }
     switch (prec * 3 + epi) {
-    case kF16 * 3 + kRaw: return kernel_ptr<kF16, kRaw>(cfg);
-    case kI8 * 3 + kRaw: return kernel_ptr<kI8, kRaw>(cfg);
-    case kI8 * 3 + kDequantF32: return kernel_ptr<kI8, kDequantF32>(cfg);
-    case kI8 * 3 + kDequantF16: return kernel_ptr<kI8, kDequantF16>(cfg);
-    case kI4 * 3 + kRaw: return kernel_ptr<kI4, kRaw>(cfg);
-    case kI4 * 3 + kDequantF32: return kernel_ptr<kI4, kDequantF32>(cfg);
-    case kI4 * 3 + kDequantF16: return kernel_ptr<kI4, kDequantF16>(cfg);
+    case kF16 * 3 + kRaw: return kernel_ptr<kF16, kRaw, kBCol>(cfg);
+    case kI8 * 3 + kRaw: return kernel_ptr<kI8, kRaw, kBCol>(cfg);
+    case kI8 * 3 + kDequantF32: return kernel_ptr<kI8, kDequantF32, kBCol>(cfg);
+    case kI8 * 3 + kDequantF16: return kernel_ptr<kI8, kDequantF16, kBCol>(cfg);
+    case kI4 * 3 + kRaw: return kernel_ptr<kI4, kRaw, kBCol>(cfg);
+    case kI4 * 3 + kDequantF32: return kernel_ptr<kI4, kDequantF32, kBCol>(cfg);
+    case kI4 * 3 + kDequantF16: return kernel_ptr<kI4, kDequantF16, kBCol>(cfg);
     default: return nullptr;
     }
 }
@@ -580,13 +695,14 @@ int pick(int prec, int64_t M, int64_t N, int64_t K) {
     return kNumConfigs - 1;
 }
 
-int validate(int prec, int epi, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
-             const void *B, int64_t ldb, const void *C, int64_t ldc, const float *scale_a,
-             const float *scale_b) {
+int validate(int prec, int epi, int br, int64_t M, int64_t N, int64_t K, const void *A,
+             int64_t lda, const void *B, int64_t ldb, const void *C, int64_t ldc,
+             const float *scale_a, const float *scale_b) {
     if (M < 0 || N < 0 || K < 0) return PDGEMM_EINVAL_DIM;
     if (M > INT32_MAX || N > INT32_MAX || K > (int64_t(1) << 30)) return PDGEMM_EINVAL_DIM;
     if (prec == kI4 && K > PDGEMM_I4_MAX_K) return PDGEMM_EINVAL_DIM;
-    if (lda < K || ldb < K || ldc < N) return PDGEMM_EINVAL_LD;
+    // a row of B holds K values (column-major) or N values (row-major)
+    if (lda < K || ldb < (br == kBRow ? N : K) || ldc < N) return PDGEMM_EINVAL_LD;
     if (prec == kI4 && ((K & 1) || (lda & 1) || (ldb & 1))) return PDGEMM_EINVAL_I4;
     if (M == 0 || N == 0) return PDGEMM_OK;
     if (!C || (K > 0 && (!A || !B))) return PDGEMM_ENULL;
@@ -603,12 +719,12 @@ int validate(int prec, int epi, int64_t M, int64_t N, int64_t K, const void *A, 
     return PDGEMM_OK;
 }
 
-int launch(int prec, int cfg, int epi, int64_t M, int64_t N, int64_t K, const void *A,
+int launch(int prec, int cfg, int epi, int br, int64_t M, int64_t N, int64_t K, const void *A,
            int64_t lda, const void *B, int64_t ldb, const float *scale_a, const float *scale_b,
            void *C, int64_t ldc, void *stream) {
     if (prec < 0 || prec > 2 || cfg < 0 || cfg >= kNumConfigs) return PDGEMM_EINVAL_CFG;
     if (epi != kRaw && prec == kF16) return PDGEMM_EINVAL_CFG;
-    int rc = validate(prec, epi, M, N, K, A, lda, B, ldb, C, ldc, scale_a, scale_b);
+    int rc = validate(prec, epi, br, M, N, K, A, lda, B, ldb, C, ldc, scale_a, scale_b);
     if (rc != PDGEMM_OK) return rc;
     if (M == 0 || N == 0) return PDGEMM_OK;
 
@@ -632,7 +748,8 @@ int launch(int prec, int cfg, int epi, int64_t M, int64_t N, int64_t K, const vo
     const int64_t blocks = (int64_t)args.tiles_m * args.tiles_n;
     if (blocks > INT32_MAX) return PDGEMM_EINVAL_DIM;
 
-    const void *fn = kernel_ptr(prec, cfg, epi);
+    const void *fn = kernel_ptr(prec, cfg, epi, br);
+    if (!fn) return PDGEMM_EINVAL_CFG;
     const int threads = (c.bm / c.wm) * (c.bn / c.wn) * kWave;
     void *kargs[] = {&args};
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -651,48 +768,73 @@ extern "C" {
 
 int gemm_f16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
              const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream) {
-    return launch(kF16, pick(kF16, M, N, K), kRaw, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
+    return launch(kF16, pick(kF16, M, N, K), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
                   stream);
 }
 
 int gemm_i8(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
             const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
-    return launch(kI8, pick(kI8, M, N, K), kRaw, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
+    return launch(kI8, pick(kI8, M, N, K), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
                   stream);
 }
 
 int gemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
             const uint8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
-    return launch(kI4, pick(kI4, M, N, K), kRaw, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
+    return launch(kI4, pick(kI4, M, N, K), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
                   stream);
 }
 
 int gemm_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
                     const int8_t *B, int64_t ldb, const float *scale_a, const float *scale_b,
                     void *C, int64_t ldc, int out_f16, void *stream) {
-    return launch(kI8, pick(kI8, M, N, K), out_f16 ? kDequantF16 : kDequantF32, M, N, K, A, lda, B,
+    return launch(kI8, pick(kI8, M, N, K), out_f16 ? kDequantF16 : kDequantF32, kBCol, M, N, K, A, lda, B,
                   ldb, scale_a, scale_b, C, ldc, stream);
 }
 
 int gemm_i4_dequant(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
                     const uint8_t *B, int64_t ldb, const float *scale_a, const float *scale_b,
                     void *C, int64_t ldc, int out_f16, void *stream) {
-    return launch(kI4, pick(kI4, M, N, K), out_f16 ? kDequantF16 : kDequantF32, M, N, K, A, lda, B,
+    return launch(kI4, pick(kI4, M, N, K), out_f16 ? kDequantF16 : kDequantF32, kBCol, M, N, K, A, lda, B,
                   ldb, scale_a, scale_b, C, ldc, stream);
 }
 
 int pdgemm_gemm_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K, const void *A,
                     int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc,
                     void *stream) {
-    return launch(prec, cfg, kRaw, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc, stream);
+    return launch(prec, cfg, kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc, stream);
 }
 
 int pdgemm_dequant_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K, const void *A,
                        int64_t lda, const void *B, int64_t ldb, const float *scale_a,
                        const float *scale_b, void *C, int64_t ldc, int out_f16, void *stream) {
     if (prec == kF16) return PDGEMM_EINVAL_CFG;
-    return launch(prec, cfg, out_f16 ? kDequantF16 : kDequantF32, M, N, K, A, lda, B, ldb, scale_a,
+    return launch(prec, cfg, out_f16 ? kDequantF16 : kDequantF32, kBCol, M, N, K, A, lda, B, ldb, scale_a,
                   scale_b, C, ldc, stream);
+}
+
+int gemm_f16_rowb(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                  const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream) {
+    return launch(kF16, pick(kF16, M, N, K), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
+                  C, ldc, stream);
+}
+
+int gemm_i8_rowb(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
+                 const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
+    return launch(kI8, pick(kI8, M, N, K), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
+                  C, ldc, stream);
+}
+
+int gemm_i4_rowb(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+                 const uint8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
+    return launch(kI4, pick(kI4, M, N, K), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
+                  C, ldc, stream);
+}
+
+int pdgemm_gemm_rowb_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K, const void *A,
+                         int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc,
+                         void *stream) {
+    return launch(prec, cfg, kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
+                  stream);
 }
 
 int pdgemm_num_configs(void) { return kNumConfigs; }
@@ -718,7 +860,7 @@ const char *pdgemm_strerror(int code) {
     switch (code) {
     case PDGEMM_OK: return "success";
     case PDGEMM_EINVAL_DIM: return "invalid dimension (negative, too large, or INT4 K above 131071)";
-    case PDGEMM_EINVAL_LD: return "leading dimension smaller than the row length";
+    case PDGEMM_EINVAL_LD: return "leading dimension smaller than the row length, or a row above 4 MiB";
     case PDGEMM_ENULL: return "null pointer for an operand with nonzero extent";
     case PDGEMM_EINVAL_I4: return "INT4 K, lda and ldb must be even";
     case PDGEMM_EALIGN: return "A and B must be 16-byte aligned, A and B rows must span a multiple of 16 bytes, C and the scales must be element-aligned";

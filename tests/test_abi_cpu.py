@@ -40,6 +40,11 @@ def lib():
     for name in ("gemm_i8_dequant", "gemm_i4_dequant"):
         getattr(L, name).argtypes = [i64, i64, i64, p, i64, p, i64, p, p, p, i64, i, p]
         getattr(L, name).restype = i
+    for name in ("gemm_f16_rowb", "gemm_i8_rowb", "gemm_i4_rowb"):
+        getattr(L, name).argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+        getattr(L, name).restype = i
+    L.pdgemm_gemm_rowb_cfg.argtypes = [i, i, i64, i64, i64, p, i64, p, i64, p, i64, p]
+    L.pdgemm_gemm_rowb_cfg.restype = i
     L.pdgemm_dequant_cfg.argtypes = [i, i, i64, i64, i64, p, i64, p, i64, p, p, p, i64, i, p]
     L.pdgemm_dequant_cfg.restype = i
     L.pdgemm_gemm_cfg.argtypes = [i, i, i64, i64, i64, p, i64, p, i64, p, i64, p]
@@ -54,6 +59,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("gemm_f16", "gemm_i8", "gemm_i4", "gemm_i8_dequant", "gemm_i4_dequant",
+              "gemm_f16_rowb", "gemm_i8_rowb", "gemm_i4_rowb", "pdgemm_gemm_rowb_cfg",
               "pdgemm_gemm_cfg", "pdgemm_dequant_cfg", "pdgemm_strerror", "pdgemm_version"):
         assert n in names
 
@@ -141,6 +147,25 @@ def test_dequant_argument_errors(lib, name):
     assert call_dq(lib, name, 64, 0, 64, sa=None, sb=None) == 0
     if name == "gemm_i4_dequant":
         assert call_dq(lib, name, 64, 64, 63, lda=64, ldb=64) == c["PDGEMM_EINVAL_I4"]
+
+
+@pytest.mark.parametrize("name", ["gemm_f16_rowb", "gemm_i8_rowb", "gemm_i4_rowb"])
+def test_rowb_argument_errors(lib, name):
+    c = codes()
+    # a row of row-major B holds N values: ldb >= N, independent of K
+    assert call(lib, name, 64, 96, 64, ldb=64) == c["PDGEMM_EINVAL_LD"]
+    assert call(lib, name, 64, 64, 96, ldb=64) != c["PDGEMM_EINVAL_LD"]
+    assert call(lib, name, 64, 64, 64, lda=32) == c["PDGEMM_EINVAL_LD"]
+    assert call(lib, name, -1, 64, 64) == c["PDGEMM_EINVAL_DIM"]
+    assert call(lib, name, 64, 64, 64, B=None) == c["PDGEMM_ENULL"]
+    assert call(lib, name, 64, 64, 64, B=PB + 8) == c["PDGEMM_EALIGN"]
+    assert call(lib, name, 64, 60, 64, ldb=60) == c["PDGEMM_EALIGN"]  # rows of B span 16-byte multiples
+    assert call(lib, name, 0, 64, 64) == 0
+    if name == "gemm_i4_rowb":
+        assert call(lib, name, 64, 64, 64, ldb=65) == c["PDGEMM_EINVAL_I4"]
+        assert call(lib, name, 64, 64, 63, lda=64, ldb=64) == c["PDGEMM_EINVAL_I4"]
+    n = lib.pdgemm_num_configs()
+    assert lib.pdgemm_gemm_rowb_cfg(0, n, 64, 64, 64, PA, 64, PB, 64, PC, 64, None) == c["PDGEMM_EINVAL_CFG"]
 
 
 def test_dequant_cfg_errors(lib):

@@ -51,3 +51,103 @@ def test_xcd_locality_at_8192():
     tiles = 32
     first = [remap(b, tiles * tiles, tiles, tiles, 4) for b in range(0, 8 * 32, 8)]
     assert len({m for m, _ in first}) == 4 and len({n for _, n in first}) == 8
+
+
+# --------------------------------------------------------------------------
+# Row-major B: DMA placement, transposing reads and banks (restated from the
+# kernel source; the read semantics are those measured for gfx950's
+# ds_read_b64_tr_b16 / _b8 / _b4: in a 16-lane group, result element e of
+# lane i comes from the 8 bytes addressed by source lane j at element p, with
+# (j, p) = (i//4 + 4e, i%4) for b16, (i//8 + 2e, i%8) for b8, (e, i) for b4).
+
+import pytest  # noqa: E402
+
+ROWB = {  # precision: (rows per K tile, rows per read R, elements per 16-byte chunk, bits)
+    "f16": (32, 4, 8, 16),
+    "i8": (64, 8, 16, 8),
+    "i4": (128, 16, 32, 4),
+}
+CONFIGS = [(256, 256, 128, 128), (128, 128, 64, 64), (64, 64, 32, 32)]
+
+
+def bswizzle(prec, bn, r):
+    _, R, epc, _ = ROWB[prec]
+    Q = 16 // R
+    cpr = bn // epc
+    v = 1 if cpr >= 16 else 16 // cpr
+    span = min(cpr, 16) // Q
+    return Q * ((r // v) % span)
+
+
+def tr_source(prec, i, e):
+    """(source lane, element within its 8 bytes) of result element e of group lane i."""
+    if prec == "f16":
+        return i // 4 + 4 * e, i % 4
+    if prec == "i8":
+        return i // 8 + 2 * e, i % 8
+    return e, i
+
+
+@pytest.mark.parametrize("prec", ["f16", "i8", "i4"])
+@pytest.mark.parametrize("cfg", CONFIGS, ids=["256", "128", "64"])
+def test_rowmajor_b_layout(prec, cfg):
+    BM, BN, WM, WN = cfg
+    krows, R, epc, bits = ROWB[prec]
+    Q = 16 // R
+    cpr = BN // epc
+    NW = (BM // WM) * (BN // WN)
+    kdma = (BM + BN) // 16 // NW
+    kdma_a = BM // 16 // NW
+    # DMA: every LDS chunk slot of the B part receives one distinct (row, chunk) of the tile
+    slot_src = {}
+    for wave in range(NW):
+        for j in range(kdma_a, kdma):
+            for lane in range(64):
+                cr = (j * NW + wave) * 16 + lane // 4
+                f = (cr - BM) * 4 + lane % 4
+                krow, pos = f // cpr, f % cpr
+                g = pos ^ bswizzle(prec, BN, krow)
+                assert 0 <= krow < krows and 0 <= g < cpr
+                slot_src[f] = (krow, g)
+    assert sorted(slot_src) == list(range(krows * cpr))
+    assert len(set(slot_src.values())) == krows * cpr
+
+    def element_at(byte_addr, elem):
+        """(k, n) of element `elem` of the 8 bytes at LDS byte address byte_addr of the B part."""
+        f, inb = byte_addr // 16, byte_addr % 16
+        krow, g = slot_src[f]
+        col_byte = g * 16 + inb
+        return krow, col_byte * 8 // bits + elem
+
+    steprows = krows // 2
+    for wave in range(NW):
+        wn0 = (wave % (BN // WN)) * WN
+        for s in range(2):
+            for jj in range(WN // 32):
+                lane_bytes = {}   # LDS byte address of each lane, per read
+                for r in range(2):
+                    addrs = []
+                    for lane in range(64):
+                        i, grp, half = lane % 16, (lane >> 4) & 1, lane >> 5
+                        col_bytes = (wn0 + jj * 32) * bits // 8 + (16 * grp) * bits // 8 + 8 * (i % Q)
+                        krow = s * steprows + half * (steprows // 2) + r * R + i // Q
+                        pos = (col_bytes >> 4) ^ bswizzle(prec, BN, krow)
+                        addr = (krow * cpr + pos) * 16 + (col_bytes & 15)
+                        assert 0 <= addr and addr + 8 <= krows * cpr * 16
+                        addrs.append(addr)
+                    lane_bytes[r] = addrs
+                    # banks: each half-wave touches 64 distinct 4-byte banks
+                    for hw in (0, 32):
+                        banks = [(a // 4 + w) % 64 for a in addrs[hw:hw + 32] for w in (0, 1)]
+                        assert len(set(banks)) == 64, (prec, cfg, s, jj, r)
+                # the fragment each lane assembles: K-contiguous values of its own column
+                per_read = 64 // bits     # elements per 8 bytes
+                for lane in range(64):
+                    grp0 = lane - lane % 16
+                    i, half = lane % 16, lane >> 5
+                    for r in range(2):
+                        for e in range(per_read):
+                            src, p = tr_source(prec, i, e)
+                            k, n = element_at(lane_bytes[r][grp0 + src], p)
+                            want_k = s * steprows + half * (steprows // 2) + r * per_read + e
+                            assert (k, n) == (want_k, wn0 + jj * 32 + lane % 32), (prec, cfg, lane, r, e)
