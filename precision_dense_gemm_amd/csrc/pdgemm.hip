@@ -201,8 +201,8 @@ template <int P> struct OutOf<P, kDequantF16> { using type = _Float16; };
 // only for its own DMA of tile t+1 (tiles t+2 .. t+kStages-1 stay in
 // flight), so after the barrier tile t+1 is complete in LDS and stage t is
 // free for tile t+kStages.
-template <int P, int BM, int BN, int WM, int WN, int GM, int E, int BR>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Args args) {
+template <int P, int BM, int BN, int WM, int WN, int GM, int E, int BR, int KS>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kernel(Args args) {
     // The body uses gfx950-only types (buffer resources), which the host
     // pass cannot type-check; the host pass only needs the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -212,14 +212,23 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     using RB = RowB<P>;
     constexpr int kCpr = BN / RB::kElemPerChunk;   // row-major B: 16-byte chunks per row of B
     static_assert(BR == kBCol || (kCpr >= 2 && (kCpr & (kCpr - 1)) == 0), "row-major B tile width");
+    // KS > 1 splits K over the waves: each of the KS waves computes the whole
+    // BM x BN tile over its own 64-byte quarter (KS = 4) of every K tile,
+    // from its own slice of each stage, and the partial tiles are summed
+    // through LDS in wave order at the end.
     constexpr int kWavesN = BN / WN;
-    constexpr int NW = (BM / WM) * kWavesN;
-    constexpr int kRows = BM + BN;           // LDS rows per stage
-    constexpr int kDma = kRows / 16 / NW;    // 1 KB DMA instructions per wave per stage
-    constexpr int kDmaA = BM / 16 / NW;      // ... of which fill A rows
+    constexpr int NT = (BM / WM) * kWavesN;  // waves tiling the block
+    constexpr int NW = NT * KS;              // waves in the workgroup
+    constexpr int kSub = BM + BN;            // LDS rows of one K slice of a stage
+    constexpr int kRows = KS * kSub;         // LDS rows per stage
+    constexpr int kDma = KS > 1 ? kSub / 16 : kRows / 16 / NW;  // 1 KB DMA instructions per wave per stage
+    constexpr int kDmaA = KS > 1 ? BM / 16 : BM / 16 / NW;      // ... of which fill A rows
+    constexpr int kTileBytes = kRowBytes * KS;                  // bytes of K per row per K tile
     constexpr int FM = WM / 32;
     constexpr int FN = WN / 32;
-    static_assert((BM / 16) % NW == 0 && (BN / 16) % NW == 0, "stage rows must split evenly over waves");
+    static_assert(KS > 1 || ((BM / 16) % NW == 0 && (BN / 16) % NW == 0), "stage rows must split evenly over waves");
+    static_assert(KS == 1 || (NT == 1 && FM == 1 && FN == 1 && E == kRaw && BR == kBCol && 16 % KS == 0),
+                  "the K-split variant computes one 32 x 32 tile per wave, plain epilogue, column-major B");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(kStages == 4, "the main loop is unrolled for four stages");
     static_assert((kStages - 2) * kDma <= 63, "vmcnt holds at most 63 outstanding loads");
@@ -235,6 +244,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int slice = KS > 1 ? wave : 0;     // this wave's K slice
+    const int twave = KS > 1 ? 0 : wave;     // this wave's place in the block tile
     const int M = args.M, N = args.N, K = args.K;
 
     // ---- block id -> tile, XCD-aware and banded by GM block rows ----
@@ -264,7 +275,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     // it without touching memory, so no DMA reads past an operand.  A range
     // of zero turns a stage past the last K tile into a no-op.
     const int valid = (P == kF16) ? 2 * K : (P == kI8 ? K : K / 2);  // data bytes per row
-    const int n_tiles = (valid + kRowBytes - 1) / kRowBytes;
+    const int n_tiles = (valid + kTileBytes - 1) / kTileBytes;
     const int valid16 = (valid + 15) & ~15;
     const uint8_t *a_base = args.A + (int64_t)m0 * args.lda_bytes;
     const int a_end = (int)((min(BM, M - m0) - 1) * args.lda_bytes) + valid16;
@@ -278,18 +289,21 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     const int64_t b_row_valid = ((int64_t)min(BN, N - n0) * (P == kF16 ? 16 : (P == kI8 ? 8 : 4)) + 7) / 8;
     const int64_t b_end = BR == kBRow ? (int64_t)(K - 1) * args.ldb_bytes + ((b_row_valid + 15) & ~int64_t(15))
                                       : (int64_t)(min(BN, N - n0) - 1) * args.ldb_bytes + valid16;
-    const int64_t b_tile_bytes = BR == kBRow ? (int64_t)RB::kKRows * args.ldb_bytes : kRowBytes;
+    const int64_t b_tile_bytes = BR == kBRow ? (int64_t)RB::kKRows * args.ldb_bytes : kTileBytes;
     const int lrow = lane >> 2;              // row within the 16-row group
     const int lpos = lane & 3;               // LDS position written by this lane
     uint32_t voff[kDma];
 #pragma unroll
     for (int j = 0; j < kDma; ++j) {
-        const int cr = (j * NW + wave) * 16 + lrow;  // row within the stage
+        // row within the stage (KS > 1: within this wave's slice, which
+        // starts a multiple of 16 rows in, so the swizzle is the same)
+        const int cr = KS > 1 ? j * 16 + lrow : (j * NW + wave) * 16 + lrow;
         const int lchunk = lpos ^ swizzle(cr);       // logical chunk this lane fetches
+        const int kofs = slice * kRowBytes;          // this wave's bytes of the K tile
         if (j < kDmaA) {
-            voff[j] = (uint32_t)((min(m0 + cr, M - 1) - m0) * args.lda_bytes) + lchunk * 16;
+            voff[j] = (uint32_t)((min(m0 + cr, M - 1) - m0) * args.lda_bytes) + lchunk * 16 + kofs;
         } else if (BR == kBCol) {
-            voff[j] = (uint32_t)((min(n0 + cr - BM, N - 1) - n0) * args.ldb_bytes) + lchunk * 16;
+            voff[j] = (uint32_t)((min(n0 + cr - BM, N - 1) - n0) * args.ldb_bytes) + lchunk * 16 + kofs;
         } else {
             // flat chunk f of the B part: row f / kCpr, position f % kCpr
             const int f = (cr - BM) * kChunks + lpos;
@@ -300,7 +314,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     }
 
     auto stage = [&](int t, Stage &buf) __attribute__((always_inline)) {
-        const int kb = t * kRowBytes;
+        const int kb = t * kTileBytes;
         const bool live = t < n_tiles;
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(a_base + kb), (short)0, live ? a_end - kb : 0, kRsrcWord3);
@@ -314,12 +328,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
 #pragma unroll
         for (int j = 0; j < kDma; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kDmaA ? ra : rb,
-                                                     LDS_PTR(&buf[(j * NW + wave) * 16][0]),
+                                                     LDS_PTR(&buf[KS > 1 ? slice * kSub + j * 16
+                                                                          : (j * NW + wave) * 16][0]),
                                                      16, voff[j], 0, 0, 0);
     };
 
-    const int wm0 = (wave / kWavesN) * WM;   // wave's first row / column in the block tile
-    const int wn0 = (wave % kWavesN) * WN;
+    const int wm0 = (twave / kWavesN) * WM;  // wave's first row / column in the block tile
+    const int wn0 = (twave % kWavesN) * WN;
+    const int srow = slice * kSub;           // first LDS row of this wave's K slice
     const int frow = lane & 31;              // fragment row (A) / column (B) of this lane
     const int fhalf = lane >> 5;             // which 16-byte half of a 32-byte k-step
 
@@ -363,11 +379,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     auto read_frags = [&](const Stage &buf, int s, uint4 (&fa)[FM], uint4 (&fb)[FN]) __attribute__((always_inline)) {
         const int ch = (2 * s + fhalf) ^ swizzle(frow);  // fragment rows start at multiples of 32
 #pragma unroll
-        for (int i = 0; i < FM; ++i) fa[i] = buf[wm0 + i * 32 + frow][ch];
+        for (int i = 0; i < FM; ++i) fa[i] = buf[srow + wm0 + i * 32 + frow][ch];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             if constexpr (BR == kBCol)
-                fb[j] = buf[BM + wn0 + j * 32 + frow][ch];
+                fb[j] = buf[srow + BM + wn0 + j * 32 + frow][ch];
             else
                 fb[j] = read_b_rowmajor(buf, s, j);
         }
@@ -377,7 +393,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
     // at or beyond K (the last tile may be partial; what DMA left there is
     // either zeros or bytes of the row's padding).
     auto mask_frags = [&](int t, int s, uint4 (&fa)[FM], uint4 (&fb)[FN]) __attribute__((always_inline)) {
-        const int nb = valid - (t * kRowBytes + (2 * s + fhalf) * 16);
+        const int nb = valid - (t * kTileBytes + slice * kRowBytes + (2 * s + fhalf) * 16);
         uint32_t m[4];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -468,7 +484,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
         // this wave's DMA of tile t+1 has landed (only tiles t+2 .. t+3 may
         // still be in flight) and its reads of `cur` are done; after the
         // barrier the same holds for every wave
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((kStages - 2) * kDma) : "memory");
+        // (KS > 1: every wave reads only its own slice, so its own waits suffice)
+        if constexpr (KS > 1)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((kStages - 2) * kDma) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((kStages - 2) * kDma) : "memory");
         stage(t + kStages, cur);
         read_frags(next, 0, fa0, fb0);
         mma(fa1, fb1);
@@ -510,7 +530,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
 #pragma unroll
         for (int x = 0; x < kScaleLoads; ++x)
             if (tid + x * kThreads < BM + BN) lds_scale[tid + x * kThreads] = scale_v[x];
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((kStages - 1) * kDma) : "memory");
+        if constexpr (KS > 1)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 1) * kDma) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((kStages - 1) * kDma) : "memory");
         read_frags(lds0, 0, fa0, fb0);
         int t = 0;
         for (; t + kStages < n_tiles; t += kStages) {
@@ -539,12 +562,44 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
         __syncthreads();
     }
 
+    // ---- K-split epilogue: sum the partial tiles, then store ----
+    // Stage 0 is free once every wave has drained its own DMAs.  Each wave
+    // writes its 16 accumulators per lane there; wave w then sums registers
+    // kPer*w .. kPer*w + kPer-1 over the KS partials in wave order (a fixed
+    // order, so fp32 results do not vary between runs) and stores them: with
+    // KS = 4 that is rows 8w .. 8w+7 of the 32 x 32 tile.
+    if constexpr (KS > 1) {
+        using Sc = typename Prec<P>::Out;
+        constexpr int kPer = 16 / KS;
+        static_assert(sizeof(lds0) >= KS * 16 * kWave * sizeof(Sc), "partials fit in one stage");
+        Sc *const part = reinterpret_cast<Sc *>(&lds0[0][0]);
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 16; ++e) part[(wave * 16 + e) * kWave + lane] = acc[0][0][e];
+        __syncthreads();
+        const int rows_left = M - m0 - 4 * fhalf;
+        const bool col_ok = frow < N - n0;
+        char *const c_lane = reinterpret_cast<char *>(args.C) +
+                             ((int64_t)(m0 + 4 * fhalf) * args.ldc + n0 + frow) * (int64_t)sizeof(Sc);
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int e = wave * kPer + u;
+            Sc v = part[e * kWave + lane];
+#pragma unroll
+            for (int w = 1; w < KS; ++w) v += part[(w * 16 + e) * kWave + lane];
+            if constexpr (P == kI4) v >>= 8;
+            const int r = 8 * (e >> 2) + (e & 3);   // row in the tile, less 4*(l/32)
+            if (col_ok && r < rows_left)
+                *reinterpret_cast<Sc *>(c_lane + (int64_t)r * args.ldc * (int64_t)sizeof(Sc)) = v;
+        }
+    }
+
     // ---- epilogue: 32x32 MFMA result layout -> row-major C ----
     // Register e of lane l in MFMA block (i, j) holds row
     // i*32 + 8*(e/4) + 4*(l/32) + e%4 and column j*32 + l%32 of the wave's
     // tile.  Row offsets are wave-uniform (scalar registers); each lane adds
     // one 32-bit offset, so a store costs no vector address arithmetic.
-    {
+    if constexpr (KS == 1) {
         char *const wave_c = reinterpret_cast<char *>(args.C) +
                              ((int64_t)(m0 + wm0) * args.ldc + n0 + wn0) * (int64_t)sizeof(Out);
         const int64_t row_bytes = args.ldc * (int64_t)sizeof(Out);
@@ -622,20 +677,24 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Arg
 // host side
 
 struct Config {
-    int bm, bn, wm, wn, gm;
+    int bm, bn, wm, wn, gm, ks;
 };
 
 constexpr Config kConfigs[] = {
-    {256, 256, 128, 128, 4},  // 0: large shapes
-    {128, 128, 64, 64, 8},    // 1: medium
-    {64, 64, 32, 32, 8},      // 2: small
+    {256, 256, 128, 128, 4, 1},  // 0: large shapes
+    {128, 128, 64, 64, 8, 1},    // 1: medium
+    {64, 64, 32, 32, 8, 1},      // 2: small
+    {32, 32, 32, 32, 8, 4},      // 3: few tiles (small M or N): K split over 4 waves
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
 template <int P, int C, int E, int BR>
 const void *kernel_for() {
     constexpr Config c = kConfigs[C];
-    return reinterpret_cast<const void *>(&gemm_kernel<P, c.bm, c.bn, c.wm, c.wn, c.gm, E, BR>);
+    if constexpr (c.ks > 1 && (E != kRaw || BR != kBCol))
+        return nullptr;   // the K-split tile has the plain epilogue and column-major B only
+    else
+        return reinterpret_cast<const void *>(&gemm_kernel<P, c.bm, c.bn, c.wm, c.wn, c.gm, E, BR, c.ks>);
 }
 
 template <int P, int E, int BR>
@@ -644,6 +703,7 @@ const void *kernel_ptr(int cfg) {
     case 0: return kernel_for<P, 0, E, BR>();
     case 1: return kernel_for<P, 1, E, BR>();
     case 2: return kernel_for<P, 2, E, BR>();
+    case 3: return kernel_for<P, 3, E, BR>();
     default: return nullptr;
     }
 }
@@ -686,13 +746,17 @@ bool sync_check_enabled() {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-int pick(int prec, int64_t M, int64_t N, int64_t K) {
+// The largest tile that still gives every CU (256) at least one workgroup.
+// When even the 64 x 64 tile leaves CUs idle (small M or N), the K-split
+// 32 x 32 tile, where it applies (plain epilogue, column-major B), puts 4
+// waves on each of 4 times as many tiles.
+int pick(int prec, int64_t M, int64_t N, int64_t K, bool ksplit_ok) {
     (void)prec;
     (void)K;
-    // the largest tile that still gives every CU (256) at least one workgroup
-    for (int c = 0; c < kNumConfigs; ++c)
+    constexpr int kLast = 2;   // the smallest tile without K split
+    for (int c = 0; c <= kLast; ++c)
         if (cdiv(M, kConfigs[c].bm) * cdiv(N, kConfigs[c].bn) >= 256) return c;
-    return kNumConfigs - 1;
+    return ksplit_ok ? 3 : kLast;
 }
 
 int validate(int prec, int epi, int br, int64_t M, int64_t N, int64_t K, const void *A,
@@ -750,7 +814,7 @@ int launch(int prec, int cfg, int epi, int br, int64_t M, int64_t N, int64_t K, 
 
     const void *fn = kernel_ptr(prec, cfg, epi, br);
     if (!fn) return PDGEMM_EINVAL_CFG;
-    const int threads = (c.bm / c.wm) * (c.bn / c.wn) * kWave;
+    const int threads = (c.bm / c.wm) * (c.bn / c.wn) * c.ks * kWave;
     void *kargs[] = {&args};
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), kargs, 0, s);
@@ -768,33 +832,33 @@ extern "C" {
 
 int gemm_f16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
              const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream) {
-    return launch(kF16, pick(kF16, M, N, K), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
+    return launch(kF16, pick(kF16, M, N, K, true), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
                   stream);
 }
 
 int gemm_i8(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
             const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
-    return launch(kI8, pick(kI8, M, N, K), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
+    return launch(kI8, pick(kI8, M, N, K, true), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
                   stream);
 }
 
 int gemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
             const uint8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
-    return launch(kI4, pick(kI4, M, N, K), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
+    return launch(kI4, pick(kI4, M, N, K, true), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
                   stream);
 }
 
 int gemm_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
                     const int8_t *B, int64_t ldb, const float *scale_a, const float *scale_b,
                     void *C, int64_t ldc, int out_f16, void *stream) {
-    return launch(kI8, pick(kI8, M, N, K), out_f16 ? kDequantF16 : kDequantF32, kBCol, M, N, K, A, lda, B,
+    return launch(kI8, pick(kI8, M, N, K, false), out_f16 ? kDequantF16 : kDequantF32, kBCol, M, N, K, A, lda, B,
                   ldb, scale_a, scale_b, C, ldc, stream);
 }
 
 int gemm_i4_dequant(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
                     const uint8_t *B, int64_t ldb, const float *scale_a, const float *scale_b,
                     void *C, int64_t ldc, int out_f16, void *stream) {
-    return launch(kI4, pick(kI4, M, N, K), out_f16 ? kDequantF16 : kDequantF32, kBCol, M, N, K, A, lda, B,
+    return launch(kI4, pick(kI4, M, N, K, false), out_f16 ? kDequantF16 : kDequantF32, kBCol, M, N, K, A, lda, B,
                   ldb, scale_a, scale_b, C, ldc, stream);
 }
 
@@ -814,19 +878,19 @@ int pdgemm_dequant_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K, const
 
 int gemm_f16_rowb(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
                   const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream) {
-    return launch(kF16, pick(kF16, M, N, K), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
+    return launch(kF16, pick(kF16, M, N, K, false), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
                   C, ldc, stream);
 }
 
 int gemm_i8_rowb(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
                  const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
-    return launch(kI8, pick(kI8, M, N, K), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
+    return launch(kI8, pick(kI8, M, N, K, false), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
                   C, ldc, stream);
 }
 
 int gemm_i4_rowb(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
                  const uint8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
-    return launch(kI4, pick(kI4, M, N, K), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
+    return launch(kI4, pick(kI4, M, N, K, false), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
                   C, ldc, stream);
 }
 
@@ -841,7 +905,7 @@ int pdgemm_num_configs(void) { return kNumConfigs; }
 
 int pdgemm_pick_config(int prec, int64_t M, int64_t N, int64_t K) {
     if (prec < 0 || prec > 2) return -1;
-    return pick(prec, M, N, K);
+    return pick(prec, M, N, K, true);
 }
 
 int pdgemm_config_info(int cfg, int *block_m, int *block_n, int *wave_m, int *wave_n,
@@ -852,7 +916,7 @@ int pdgemm_config_info(int cfg, int *block_m, int *block_n, int *wave_m, int *wa
     if (block_n) *block_n = c.bn;
     if (wave_m) *wave_m = c.wm;
     if (wave_n) *wave_n = c.wn;
-    if (threads) *threads = (c.bm / c.wm) * (c.bn / c.wn) * kWave;
+    if (threads) *threads = (c.bm / c.wm) * (c.bn / c.wn) * c.ks * kWave;
     return PDGEMM_OK;
 }
 

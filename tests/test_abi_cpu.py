@@ -176,6 +176,20 @@ def test_dequant_cfg_errors(lib):
     assert lib.pdgemm_dequant_cfg(1, n, *args) == c["PDGEMM_EINVAL_CFG"]
     assert lib.pdgemm_dequant_cfg(2, -1, *args) == c["PDGEMM_EINVAL_CFG"]
     assert lib.pdgemm_dequant_cfg(3, 0, *args) == c["PDGEMM_EINVAL_CFG"]
+    # the K-split tile has the plain epilogue and column-major B only
+    ks = [cfg for cfg in range(n) if _k_split(lib, cfg) > 1]
+    assert ks, "no K-split configuration"
+    for cfg in ks:
+        assert lib.pdgemm_dequant_cfg(1, cfg, *args) == c["PDGEMM_EINVAL_CFG"]
+        assert lib.pdgemm_gemm_rowb_cfg(1, cfg, 64, 64, 64, PA, 64, PB, 64, PC, 64, None) == c["PDGEMM_EINVAL_CFG"]
+
+
+def _k_split(lib, cfg):
+    """Waves per output wave tile: threads / (waves tiling the block * 64)."""
+    vals = [ctypes.c_int() for _ in range(5)]
+    assert lib.pdgemm_config_info(cfg, *[ctypes.byref(v) for v in vals]) == 0
+    bm, bn, wm, wn, threads = (v.value for v in vals)
+    return threads // ((bm // wm) * (bn // wn) * 64)
 
 
 def test_alignment_of_leading_dims_per_precision(lib):
@@ -206,7 +220,8 @@ def test_config_errors_and_info(lib):
         assert lib.pdgemm_config_info(cfg, *[ctypes.byref(v) for v in vals]) == 0
         bm, bn, wm, wn, threads = (v.value for v in vals)
         assert bm % wm == 0 and bn % wn == 0 and wm % 32 == 0 and wn % 32 == 0
-        assert threads == (bm // wm) * (bn // wn) * 64
+        # waves tile the block, times the K split (4 waves share one 32 x 32 tile)
+        assert threads in ((bm // wm) * (bn // wn) * 64, (bm // wm) * (bn // wn) * 64 * 4)
     assert lib.pdgemm_config_info(n, None, None, None, None, None) == c["PDGEMM_EINVAL_CFG"]
     for prec in (0, 1, 2):
         for size in (1, 512, 2048, 8192):

@@ -222,6 +222,22 @@ def test_f16_output_two_byte_aligned(pd, dev):
     assert_bits_equal(C[:, 1:], oracle_dequant("i8", A, Bt, K, sa, sb, "f16"), "odd ldc")
 
 
+def test_ksplit_config_is_rejected(pd, dev):
+    gu.note("[case] dequant with the K-split configuration")
+    A = torch.zeros((8, 32), dtype=torch.int8, device=dev)
+    s8 = torch.ones(8, device=dev)
+    with pytest.raises(pd.PdgemmError) as e:
+        pd.gemm_i8_dequant(A, A, s8, s8, cfg=3)
+    assert e.value.code == -6
+
+
+def test_small_m_uses_a_plain_tile(pd, dev):
+    # the entry points never pick the K-split tile for the dequantizing epilogue
+    M, N, K = 16, 520, 300
+    A, Bt, sa, sb, C = run_case(pd, dev, "i8", M, N, K, 12, "f32")
+    assert_bits_equal(C, oracle_dequant("i8", A, Bt, K, sa, sb, "f32"), "small M dequant")
+
+
 def test_scale_vector_errors(pd, dev):
     gu.note("[case] dequant binding errors")
     A = torch.zeros((8, 32), dtype=torch.int8, device=dev)

@@ -106,7 +106,7 @@ CFG_SHAPES = [(520, 600, 520), (300, 260, 1030), (64, 700, 130)]
 
 
 @pytest.mark.parametrize("prec", PRECS)
-@pytest.mark.parametrize("cfg", [0, 1, 2])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
 @pytest.mark.parametrize("shape", CFG_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in CFG_SHAPES])
 def test_every_config(pd, dev, prec, cfg, shape):
     if cfg >= pd.num_configs():
@@ -305,3 +305,53 @@ def test_prepared_launch_matches_plain_call(pd, dev, prec):
         go()
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# the K-split 32 x 32 tile (four waves per tile, each on its own quarter of
+# every K tile, partials summed in wave order): small M or N
+
+KSPLIT_SHAPES = [(1, 1000, 3000), (16, 1000, 1030), (33, 700, 4100), (64, 257, 258), (16, 96, 64),
+                 (5, 64, 2)]
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("shape", KSPLIT_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in KSPLIT_SHAPES])
+def test_ksplit_small_m(pd, dev, prec, shape):
+    M, N, K = shape
+    pnum = {"f16": 0, "i8": 1, "i4": 2}[prec]
+    assert pd.pick_config(pnum, M, N, K) == 3, "small M should take the K-split tile"
+    A, Bt, C = run_case(pd, dev, prec, M, N, K, 4000 + M + N + K)
+    check_full(prec, A, Bt, K, C, f"ksplit {prec} {shape}")
+
+
+def test_ksplit_f16_is_deterministic(pd, dev):
+    M, N, K = 16, 2048, 4096
+    gu.note("[case] ksplit f16 determinism")
+    A, Bt = synth.operands("f16", M, N, K, 41, 42)
+    Ad, Bd = torch.from_numpy(A).to(dev), torch.from_numpy(Bt).to(dev)
+    ref = pd.gemm_f16(Ad, Bd, cfg=3)
+    for _ in range(3):
+        assert torch.equal(pd.gemm_f16(Ad, Bd, cfg=3).view(torch.int32), ref.view(torch.int32))
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("M", [16, 64])
+def test_inference_shape_full_size(pd, dev, prec, M):
+    """M x 8192 x 8192 in the launch the benchmark times: sampled entries and Freivalds."""
+    n = 8192
+    sa = synth.config_seed(7, n, synth.OPERAND_A)
+    sb = synth.config_seed(7, n, synth.OPERAND_B)
+    gu.note(f"[case] inference {prec} {M}x{n}x{n}")
+    A, Bt = synth.operands(prec, M, n, n, sa, sb)
+    Ad, Bd = torch.from_numpy(A).to(dev), torch.from_numpy(Bt).to(dev)
+    C = torch.empty((M, n), dtype=torch.float32 if prec == "f16" else torch.int32, device=dev)
+    pd.prepare(prec, Ad, Bd, C, K=n)
+    torch.cuda.synchronize()
+    C = C.cpu().numpy()
+    rows, cols = gu.sample_positions(M, n, 1024, seed=M)
+    gu.check_sampled(prec, A, Bt, n, C, rows, cols, f"inference {prec} {M}")
+    if prec == "f16":
+        gu.freivalds_f16(A, Bt, n, C, seed=M)
+    else:
+        gu.freivalds_int(prec, A, Bt, n, C, seed=M)
