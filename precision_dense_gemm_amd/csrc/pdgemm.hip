@@ -685,7 +685,12 @@ constexpr Config kConfigs[] = {
     {128, 128, 64, 64, 8, 1},    // 1: medium
     {64, 64, 32, 32, 8, 1},      // 2: small
     {32, 32, 32, 32, 8, 4},      // 3: few tiles (small M or N): K split over 4 waves
+    {256, 128, 128, 64, 4, 1},   // 4: between 0 and 1 (e.g. M = 1024 of a wide product)
+    {128, 64, 64, 32, 8, 1},     // 5: between 1 and 2 (e.g. M = 256)
 };
+
+// Tiles without K split, largest first: the order in which pick() tries them.
+constexpr int kPickOrder[] = {0, 4, 1, 5, 2};
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
 template <int P, int C, int E, int BR>
@@ -704,6 +709,8 @@ const void *kernel_ptr(int cfg) {
     case 1: return kernel_for<P, 1, E, BR>();
     case 2: return kernel_for<P, 2, E, BR>();
     case 3: return kernel_for<P, 3, E, BR>();
+    case 4: return kernel_for<P, 4, E, BR>();
+    case 5: return kernel_for<P, 5, E, BR>();
     default: return nullptr;
     }
 }
@@ -746,17 +753,21 @@ bool sync_check_enabled() {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// The largest tile that still gives every CU (256) at least one workgroup.
+// The largest tile (in kPickOrder) that still gives every CU (256) at least
+// one workgroup.
 // When even the 64 x 64 tile leaves CUs idle (small M or N), the K-split
 // 32 x 32 tile, where it applies (plain epilogue, column-major B), puts 4
 // waves on each of 4 times as many tiles.
+// INT4 skips the 256 x 128 tile: its in-register unpack costs more VALU per
+// MFMA on the narrower wave tile, and two 128 x 128 workgroups per CU hide
+// it better (measured at M = 1024, N = K = 8192).
 int pick(int prec, int64_t M, int64_t N, int64_t K, bool ksplit_ok) {
-    (void)prec;
     (void)K;
-    constexpr int kLast = 2;   // the smallest tile without K split
-    for (int c = 0; c <= kLast; ++c)
+    for (int c : kPickOrder) {
+        if (prec == kI4 && c == 4) continue;
         if (cdiv(M, kConfigs[c].bm) * cdiv(N, kConfigs[c].bn) >= 256) return c;
-    return ksplit_ok ? 3 : kLast;
+    }
+    return ksplit_ok ? 3 : 2;
 }
 
 int validate(int prec, int epi, int br, int64_t M, int64_t N, int64_t K, const void *A,

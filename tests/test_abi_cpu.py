@@ -249,3 +249,28 @@ def test_binding_imports_and_marshals_without_gpu():
     with pytest.raises(TypeError):
         pd.gemm_i8_dequant(torch.zeros(4, 4, dtype=torch.float16), torch.zeros(4, 4, dtype=torch.int8),
                            torch.ones(4), torch.ones(4))
+
+
+def test_pick_prefers_large_tiles_that_fill_the_chip(lib):
+    # square sizes of the sweep keep their tiles; a wide product with few rows takes
+    # the intermediate tiles, and small M the K-split tile
+    info = {}
+    for cfg in range(lib.pdgemm_num_configs()):
+        vals = [ctypes.c_int() for _ in range(5)]
+        assert lib.pdgemm_config_info(cfg, *[ctypes.byref(v) for v in vals]) == 0
+        info[cfg] = tuple(v.value for v in vals)
+    def tile(m, n, k=8192):
+        c = lib.pdgemm_pick_config(1, m, n, k)
+        return info[c][:2], c
+    assert tile(8192, 8192)[0] == (256, 256)
+    assert tile(4096, 4096)[0] == (256, 256)
+    assert tile(2048, 2048)[0] == (128, 128)
+    assert tile(1024, 1024)[0] == (64, 64)
+    assert tile(1024, 8192)[0] == (256, 128)
+    assert tile(256, 8192)[0] == (128, 64)
+    assert tile(16, 8192)[0] == (32, 32) and _k_split(lib, tile(16, 8192)[1]) == 4
+    for m, n in ((1024, 8192), (256, 8192), (16, 8192), (8192, 8192), (512, 512)):
+        bm, bn = tile(m, n)[0]
+        assert -(-m // bm) * -(-n // bn) >= 256
+    # INT4 takes 128 x 128 rather than 256 x 128
+    assert info[lib.pdgemm_pick_config(2, 1024, 8192, 8192)][:2] == (128, 128)
