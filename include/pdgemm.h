@@ -73,7 +73,7 @@ extern "C" {
 #endif
 
 #define PDGEMM_OK 0
-#define PDGEMM_EINVAL_DIM (-1)  /* M, N or K negative, or gemm_i4 K > 131071 */
+#define PDGEMM_EINVAL_DIM (-1)  /* M, N or K negative or too large (K > 2^30, over 2^32 work-items), or gemm_i4 K > 131071 */
 #define PDGEMM_EINVAL_LD (-2)   /* lda < K, ldb < K (row-major B: ldb < N), ldc < N, or a row above 4 MiB */
 #define PDGEMM_ENULL (-3)       /* NULL pointer for an operand with nonzero extent */
 #define PDGEMM_EINVAL_I4 (-4)   /* gemm_i4: K, lda or ldb odd */

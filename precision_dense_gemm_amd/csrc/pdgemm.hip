@@ -821,11 +821,12 @@ int launch(int prec, int cfg, int epi, int br, int64_t M, int64_t N, int64_t K, 
     args.tiles_m = (int)cdiv(M, c.bm);
     args.tiles_n = (int)cdiv(N, c.bn);
     const int64_t blocks = (int64_t)args.tiles_m * args.tiles_n;
-    if (blocks > INT32_MAX) return PDGEMM_EINVAL_DIM;
+    const int threads = (c.bm / c.wm) * (c.bn / c.wn) * c.ks * kWave;
+    // a launch counts its work-items in 32 bits
+    if (blocks * threads > (int64_t)UINT32_MAX) return PDGEMM_EINVAL_DIM;
 
     const void *fn = kernel_ptr(prec, cfg, epi, br);
     if (!fn) return PDGEMM_EINVAL_CFG;
-    const int threads = (c.bm / c.wm) * (c.bn / c.wn) * c.ks * kWave;
     void *kargs[] = {&args};
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), kargs, 0, s);

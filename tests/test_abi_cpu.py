@@ -192,6 +192,14 @@ def _k_split(lib, cfg):
     return threads // ((bm // wm) * (bn // wn) * 64)
 
 
+def test_grid_beyond_32_bit_work_items_is_rejected(lib):
+    c = codes()
+    # 2^20 x 2^20 outputs on 64 x 64 tiles: 2^28 workgroups of 256 work-items
+    big = 1 << 20
+    assert lib.pdgemm_gemm_cfg(1, 2, big, big, 64, PA, 64, PB, 64, PC, big, None) == c["PDGEMM_EINVAL_DIM"]
+    assert lib.pdgemm_gemm_cfg(1, 2, 64, 64, 1 << 31, PA, 1 << 31, PB, 1 << 31, PC, 64, None) == c["PDGEMM_EINVAL_DIM"]
+
+
 def test_alignment_of_leading_dims_per_precision(lib):
     c = codes()
     # f16 rows must span multiples of 8 elements, i8 of 16, i4 of 32
