@@ -154,16 +154,26 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_n8192_hbm_counters.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "precision_dense_gemm_amd", "csrc", "pdgemm.hip")
 
 
+def kernel_source_sha(source=KERNEL_SOURCE):
+    """sha256 of what decides the code a launch runs: the device part of the kernel source
+    (everything before its host-side section) and the host's tile table, instantiation and
+    tile choice (from the Config struct to the argument checks)."""
+    import hashlib
+    text = open(source, encoding="utf-8").read()
+    device = text[:text.index("// host side")]
+    tiles = text[text.index("struct Config {"):text.index("int validate(")]
+    return hashlib.sha256((device + tiles).encode()).hexdigest()
+
+
 def measured_traffic(path=TRAFFIC_FILE, source=KERNEL_SOURCE):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
-    keyed "prec:N"; empty when the summary is missing or was taken on another kernel
-    source (its sha256 differs from the current one)."""
-    import hashlib
+    keyed "prec:N"; empty when the summary is missing or was taken on other kernels
+    (its recorded kernel_source_sha differs from the current one)."""
     import re
     try:
         text = open(path).read()
-        sha = hashlib.sha256(open(source, "rb").read()).hexdigest()
-    except OSError:
+        sha = kernel_source_sha(source)
+    except (OSError, ValueError):
         return {}
     m = re.search(r"^source_sha256 = ([0-9a-f]{64})$", text, flags=re.M)
     if not m or m.group(1) != sha:
