@@ -227,8 +227,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     constexpr int FM = WM / 32;
     constexpr int FN = WN / 32;
     static_assert(KS > 1 || ((BM / 16) % NW == 0 && (BN / 16) % NW == 0), "stage rows must split evenly over waves");
-    static_assert(KS == 1 || (NT == 1 && FM == 1 && FN == 1 && E == kRaw && BR == kBCol && 16 % KS == 0),
-                  "the K-split variant computes one 32 x 32 tile per wave, plain epilogue, column-major B");
+    static_assert(KS == 1 || (NT == 1 && E == kRaw && BR == kBCol && 16 % KS == 0),
+                  "the K-split variant computes the whole block tile per wave, plain epilogue, column-major B");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(kStages == 4, "the main loop is unrolled for four stages");
     static_assert((kStages - 2) * kDma <= 63, "vmcnt holds at most 63 outstanding loads");
@@ -563,34 +563,42 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     }
 
     // ---- K-split epilogue: sum the partial tiles, then store ----
-    // Stage 0 is free once every wave has drained its own DMAs.  Each wave
-    // writes its 16 accumulators per lane there; wave w then sums registers
-    // kPer*w .. kPer*w + kPer-1 over the KS partials in wave order (a fixed
-    // order, so fp32 results do not vary between runs) and stores them: with
-    // KS = 4 that is rows 8w .. 8w+7 of the 32 x 32 tile.
+    // Stage 0 is free once every wave has drained its own DMAs.  One 32 x 32
+    // MFMA block at a time, each wave writes its 16 accumulators per lane
+    // there; wave w then sums registers kPer*w .. kPer*w + kPer-1 over the KS
+    // partials in wave order (a fixed order, so fp32 results do not vary
+    // between runs) and stores them: with KS = 4 that is rows 8w .. 8w+7 of
+    // the block.
     if constexpr (KS > 1) {
         using Sc = typename Prec<P>::Out;
         constexpr int kPer = 16 / KS;
-        static_assert(sizeof(lds0) >= KS * 16 * kWave * sizeof(Sc), "partials fit in one stage");
+        static_assert(sizeof(lds0) >= KS * 16 * kWave * sizeof(Sc), "partials of a block fit in one stage");
         Sc *const part = reinterpret_cast<Sc *>(&lds0[0][0]);
-        __syncthreads();
 #pragma unroll
-        for (int e = 0; e < 16; ++e) part[(wave * 16 + e) * kWave + lane] = acc[0][0][e];
-        __syncthreads();
-        const int rows_left = M - m0 - 4 * fhalf;
-        const bool col_ok = frow < N - n0;
-        char *const c_lane = reinterpret_cast<char *>(args.C) +
-                             ((int64_t)(m0 + 4 * fhalf) * args.ldc + n0 + frow) * (int64_t)sizeof(Sc);
+        for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-            const int e = wave * kPer + u;
-            Sc v = part[e * kWave + lane];
+            for (int j = 0; j < FN; ++j) {
+                __syncthreads();   // stage 0 free: main loop, or the previous block, done
 #pragma unroll
-            for (int w = 1; w < KS; ++w) v += part[(w * 16 + e) * kWave + lane];
-            if constexpr (P == kI4) v >>= 8;
-            const int r = 8 * (e >> 2) + (e & 3);   // row in the tile, less 4*(l/32)
-            if (col_ok && r < rows_left)
-                *reinterpret_cast<Sc *>(c_lane + (int64_t)r * args.ldc * (int64_t)sizeof(Sc)) = v;
+                for (int e = 0; e < 16; ++e) part[(wave * 16 + e) * kWave + lane] = acc[i][j][e];
+                __syncthreads();
+                const int rows_left = M - m0 - i * 32 - 4 * fhalf;
+                const bool col_ok = j * 32 + frow < N - n0;
+                char *const c_lane = reinterpret_cast<char *>(args.C) +
+                                     ((int64_t)(m0 + i * 32 + 4 * fhalf) * args.ldc + n0 + j * 32 + frow) *
+                                         (int64_t)sizeof(Sc);
+#pragma unroll
+                for (int u = 0; u < kPer; ++u) {
+                    const int e = wave * kPer + u;
+                    Sc v = part[e * kWave + lane];
+#pragma unroll
+                    for (int w = 1; w < KS; ++w) v += part[(w * 16 + e) * kWave + lane];
+                    if constexpr (P == kI4) v >>= 8;
+                    const int r = 8 * (e >> 2) + (e & 3);   // row in the block, less 4*(l/32)
+                    if (col_ok && r < rows_left)
+                        *reinterpret_cast<Sc *>(c_lane + (int64_t)r * args.ldc * (int64_t)sizeof(Sc)) = v;
+                }
+            }
         }
     }
 
@@ -687,6 +695,7 @@ constexpr Config kConfigs[] = {
     {32, 32, 32, 32, 8, 4},      // 3: few tiles (small M or N): K split over 4 waves
     {256, 128, 128, 64, 4, 1},   // 4: between 0 and 1 (e.g. M = 1024 of a wide product)
     {128, 64, 64, 32, 8, 1},     // 5: between 1 and 2 (e.g. M = 256)
+    {64, 32, 64, 32, 8, 4},      // 6: K split over 4 waves, 64 rows (e.g. M = 64 of a wide product)
 };
 
 // Tiles without K split, largest first: the order in which pick() tries them.
@@ -711,6 +720,7 @@ const void *kernel_ptr(int cfg) {
     case 3: return kernel_for<P, 3, E, BR>();
     case 4: return kernel_for<P, 4, E, BR>();
     case 5: return kernel_for<P, 5, E, BR>();
+    case 6: return kernel_for<P, 6, E, BR>();
     default: return nullptr;
     }
 }
@@ -754,7 +764,7 @@ bool sync_check_enabled() {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // The largest tile (in kPickOrder) that still gives every CU (256) at least
-// one workgroup.
+// one workgroup; failing that, a K-split tile.
 // When even the 64 x 64 tile leaves CUs idle (small M or N), the K-split
 // 32 x 32 tile, where it applies (plain epilogue, column-major B), puts 4
 // waves on each of 4 times as many tiles.
@@ -767,7 +777,11 @@ int pick(int prec, int64_t M, int64_t N, int64_t K, bool ksplit_ok) {
         if (prec == kI4 && c == 4) continue;
         if (cdiv(M, kConfigs[c].bm) * cdiv(N, kConfigs[c].bn) >= 256) return c;
     }
-    return ksplit_ok ? 3 : 2;
+    if (!ksplit_ok) return 2;
+    // K split: 64 x 32 when more than 32 rows still fill the chip (each B
+    // panel is then staged once rather than once per 32 rows), else 32 x 32
+    if (M > 32 && cdiv(M, 64) * cdiv(N, 32) >= 256) return 6;
+    return 3;
 }
 
 int validate(int prec, int epi, int br, int64_t M, int64_t N, int64_t K, const void *A,

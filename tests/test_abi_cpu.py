@@ -277,6 +277,8 @@ def test_pick_prefers_large_tiles_that_fill_the_chip(lib):
     assert tile(1024, 8192)[0] == (256, 128)
     assert tile(256, 8192)[0] == (128, 64)
     assert tile(16, 8192)[0] == (32, 32) and _k_split(lib, tile(16, 8192)[1]) == 4
+    assert tile(64, 8192)[0] == (64, 32) and _k_split(lib, tile(64, 8192)[1]) == 4
+    assert tile(512, 512)[0] == (32, 32)
     for m, n in ((1024, 8192), (256, 8192), (16, 8192), (8192, 8192), (512, 512)):
         bm, bn = tile(m, n)[0]
         assert -(-m // bm) * -(-n // bn) >= 256

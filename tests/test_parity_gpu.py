@@ -106,7 +106,7 @@ CFG_SHAPES = [(520, 600, 520), (300, 260, 1030), (64, 700, 130)]
 
 
 @pytest.mark.parametrize("prec", PRECS)
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("shape", CFG_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in CFG_SHAPES])
 def test_every_config(pd, dev, prec, cfg, shape):
     if cfg >= pd.num_configs():
@@ -311,16 +311,18 @@ def test_prepared_launch_matches_plain_call(pd, dev, prec):
 # the K-split 32 x 32 tile (four waves per tile, each on its own quarter of
 # every K tile, partials summed in wave order): small M or N
 
-KSPLIT_SHAPES = [(1, 1000, 3000), (16, 1000, 1030), (33, 700, 4100), (64, 257, 258), (16, 96, 64),
-                 (5, 64, 2)]
+# (shape, the K-split tile the entry points pick: 3 = 32 x 32, 6 = 64 x 32)
+KSPLIT_SHAPES = [((1, 1000, 3000), 3), ((16, 1000, 1030), 3), ((33, 700, 4100), 3), ((64, 257, 258), 3),
+                 ((16, 96, 64), 3), ((5, 64, 2), 3), ((50, 8200, 700), 6), ((64, 8192, 1030), 6),
+                 ((33, 8250, 130), 6)]
 
 
 @pytest.mark.parametrize("prec", PRECS)
-@pytest.mark.parametrize("shape", KSPLIT_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in KSPLIT_SHAPES])
-def test_ksplit_small_m(pd, dev, prec, shape):
+@pytest.mark.parametrize("shape,cfg", KSPLIT_SHAPES, ids=[f"{m}x{n}x{k}" for (m, n, k), _ in KSPLIT_SHAPES])
+def test_ksplit_small_m(pd, dev, prec, shape, cfg):
     M, N, K = shape
     pnum = {"f16": 0, "i8": 1, "i4": 2}[prec]
-    assert pd.pick_config(pnum, M, N, K) == 3, "small M should take the K-split tile"
+    assert pd.pick_config(pnum, M, N, K) == cfg, "small M should take this K-split tile"
     A, Bt, C = run_case(pd, dev, prec, M, N, K, 4000 + M + N + K)
     check_full(prec, A, Bt, K, C, f"ksplit {prec} {shape}")
 
