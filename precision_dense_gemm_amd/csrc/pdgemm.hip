@@ -151,6 +151,8 @@ constexpr int kDequantF32 = 1;
 constexpr int kDequantF16 = 2;
 
 template <int P, int E> struct OutOf { using type = typename Prec<P>::Out; };
+template <int P> struct OutOf<P, kDequantF32> { using type = float; };
+template <int P> struct OutOf<P, kDequantF16> { using type = _Float16; };
 
 // B layouts: K-contiguous (column-major) or N-contiguous (row-major).
 constexpr int kBCol = 0;
@@ -179,8 +181,6 @@ __device__ __forceinline__ int bswizzle(int r) {
     constexpr int span = (cpr < 16 ? cpr : 16) / RowB<P>::kQ;
     return RowB<P>::kQ * ((r / v) % span);
 }
-template <int P> struct OutOf<P, kDequantF32> { using type = float; };
-template <int P> struct OutOf<P, kDequantF16> { using type = _Float16; };
 
 // One workgroup computes a BM x BN block of C with (BM/WM) x (BN/WN) waves.
 //
@@ -190,7 +190,9 @@ template <int P> struct OutOf<P, kDequantF16> { using type = _Float16; };
 // at position c ^ swizzle(r).  A stage is filled by buffer_load_dwordx4 ...
 // lds: each instruction of a wave writes 1 KB = 16 whole rows, lane l landing
 // in row l/4 at position l%4, so lane l fetches logical chunk
-// (l%4) ^ swizzle(row) of its row.
+// (l%4) ^ swizzle(row) of its row.  (A row-major B fills the B part of a
+// stage with K rows instead, see RowB; with a K split (KS > 1) a K tile is
+// KS x 64 bytes and a stage holds one such A-then-B slice per wave.)
 //
 // Tile t lives in stage t % kStages and is fetched kStages tiles before it
 // is consumed.  Per tile a wave runs two k-steps; a k-step reads one 16-byte
@@ -269,8 +271,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     // ---- stage geometry ----
     // Each lane has one 32-bit offset per DMA instruction: its row (clamped to
     // the last valid row of A or B) times the leading dimension, plus its
-    // chunk.  K tile t is addressed by a buffer resource based t*64 bytes
-    // further on, whose range ends at the last 16-byte chunk that holds data
+    // chunk (and, with a K split, its wave's 64-byte slice).  K tile t is
+    // addressed by a buffer resource based t * kTileBytes bytes further on
+    // (row-major B: t * kKRows rows), whose range ends at the last 16-byte
+    // chunk that holds data
     // of the last valid row: the hardware returns zeros for offsets outside
     // it without touching memory, so no DMA reads past an operand.  A range
     // of zero turns a stage past the last K tile into a no-op.
