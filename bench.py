@@ -428,6 +428,16 @@ def main():
                 ms = time_b2b(go, 0.05)
                 entry["ms_back_to_back"] = round(ms, 5)
                 entry["roofline"] = shape_roofline(prec, M, n, n, ms)
+                if prec != "f16":
+                    # the same product with the dequantizing epilogue to binary16 (the
+                    # scales of the dequant section, first M rows)
+                    sah = synth.f32_scales(n, synth.config_seed(SWEEP_CFG_ID, n, synth.OPERAND_A) + 2)[:M]
+                    sbh = synth.f32_scales(n, synth.config_seed(SWEEP_CFG_ID, n, synth.OPERAND_B) + 3)
+                    Ch = torch.empty((M, n), dtype=torch.float16, device=dev)
+                    scl = (torch.from_numpy(sah).to(dev), torch.from_numpy(sbh).to(dev))
+                    god = pd.prepare(prec, Ad[:M], Bd, Ch, K=n, scales=scl)
+                    entry["dequant_f16_ms_back_to_back"] = round(time_b2b(god, 0.05), 5)
+                    del Ch, scl
                 shapes[f"{prec}:{M}x{n}x{n}"] = entry
                 log(f"[bench] shape {prec} {M}x{n}x{n}: {ms * 1e3:.1f} us "
                     f"({entry['roofline']['bound']} {entry['roofline']['frac']:.3f})")

@@ -229,8 +229,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     constexpr int FM = WM / 32;
     constexpr int FN = WN / 32;
     static_assert(KS > 1 || ((BM / 16) % NW == 0 && (BN / 16) % NW == 0), "stage rows must split evenly over waves");
-    static_assert(KS == 1 || (NT == 1 && E == kRaw && BR == kBCol && 16 % KS == 0),
-                  "the K-split variant computes the whole block tile per wave, plain epilogue, column-major B");
+    static_assert(KS == 1 || (NT == 1 && BR == kBCol && 16 % KS == 0),
+                  "the K-split variant computes the whole block tile per wave, column-major B");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(kStages == 4, "the main loop is unrolled for four stages");
     static_assert((kStages - 2) * kDma <= 63, "vmcnt holds at most 63 outstanding loads");
@@ -574,7 +574,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     // between runs) and stores them: with KS = 4 that is rows 8w .. 8w+7 of
     // the block.
     if constexpr (KS > 1) {
-        using Sc = typename Prec<P>::Out;
+        using Sc = typename Prec<P>::Out;    // the sums (int32 or fp32)
         constexpr int kPer = 16 / KS;
         static_assert(sizeof(lds0) >= KS * 16 * kWave * sizeof(Sc), "partials of a block fit in one stage");
         Sc *const part = reinterpret_cast<Sc *>(&lds0[0][0]);
@@ -590,7 +590,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
                 const bool col_ok = j * 32 + frow < N - n0;
                 char *const c_lane = reinterpret_cast<char *>(args.C) +
                                      ((int64_t)(m0 + i * 32 + 4 * fhalf) * args.ldc + n0 + j * 32 + frow) *
-                                         (int64_t)sizeof(Sc);
+                                         (int64_t)sizeof(Out);
 #pragma unroll
                 for (int u = 0; u < kPer; ++u) {
                     const int e = wave * kPer + u;
@@ -599,8 +599,20 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
                     for (int w = 1; w < KS; ++w) v += part[(w * 16 + e) * kWave + lane];
                     if constexpr (P == kI4) v >>= 8;
                     const int r = 8 * (e >> 2) + (e & 3);   // row in the block, less 4*(l/32)
+                    Out o;
+                    if constexpr (E != kRaw) {
+                        // ((float)sum * scale_a) * scale_b, one rounding per step,
+                        // then (binary16 output) narrowed as a separate step
+                        float c = (float)v;
+                        c = c * lds_scale[i * 32 + r + 4 * fhalf];
+                        c = c * lds_scale[BM + j * 32 + frow];
+                        if constexpr (E == kDequantF16) asm("" : "+v"(c));
+                        o = (Out)c;
+                    } else {
+                        o = v;
+                    }
                     if (col_ok && r < rows_left)
-                        *reinterpret_cast<Sc *>(c_lane + (int64_t)r * args.ldc * (int64_t)sizeof(Sc)) = v;
+                        *reinterpret_cast<Out *>(c_lane + (int64_t)r * args.ldc * (int64_t)sizeof(Out)) = o;
                 }
             }
         }
@@ -709,8 +721,8 @@ constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 template <int P, int C, int E, int BR>
 const void *kernel_for() {
     constexpr Config c = kConfigs[C];
-    if constexpr (c.ks > 1 && (E != kRaw || BR != kBCol))
-        return nullptr;   // the K-split tile has the plain epilogue and column-major B only
+    if constexpr (c.ks > 1 && BR != kBCol)
+        return nullptr;   // the K-split tiles take column-major B only
     else
         return reinterpret_cast<const void *>(&gemm_kernel<P, c.bm, c.bn, c.wm, c.wn, c.gm, E, BR, c.ks>);
 }
@@ -768,10 +780,9 @@ bool sync_check_enabled() {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // The largest tile (in kPickOrder) that still gives every CU (256) at least
-// one workgroup; failing that, a K-split tile.
-// When even the 64 x 64 tile leaves CUs idle (small M or N), the K-split
-// 32 x 32 tile, where it applies (plain epilogue, column-major B), puts 4
-// waves on each of 4 times as many tiles.
+// one workgroup.  When even the 64 x 64 tile leaves CUs idle (small M or N),
+// a K-split tile (where it applies: column-major B) puts 4 waves on each of
+// up to 4 times as many tiles.
 // INT4 skips the 256 x 128 tile: its in-register unpack costs more VALU per
 // MFMA on the narrower wave tile, and two 128 x 128 workgroups per CU hide
 // it better (measured at M = 1024, N = K = 8192).
@@ -881,14 +892,14 @@ int gemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
 int gemm_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
                     const int8_t *B, int64_t ldb, const float *scale_a, const float *scale_b,
                     void *C, int64_t ldc, int out_f16, void *stream) {
-    return launch(kI8, pick(kI8, M, N, K, false), out_f16 ? kDequantF16 : kDequantF32, kBCol, M, N, K, A, lda, B,
+    return launch(kI8, pick(kI8, M, N, K, true), out_f16 ? kDequantF16 : kDequantF32, kBCol, M, N, K, A, lda, B,
                   ldb, scale_a, scale_b, C, ldc, stream);
 }
 
 int gemm_i4_dequant(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
                     const uint8_t *B, int64_t ldb, const float *scale_a, const float *scale_b,
                     void *C, int64_t ldc, int out_f16, void *stream) {
-    return launch(kI4, pick(kI4, M, N, K, false), out_f16 ? kDequantF16 : kDequantF32, kBCol, M, N, K, A, lda, B,
+    return launch(kI4, pick(kI4, M, N, K, true), out_f16 ? kDequantF16 : kDequantF32, kBCol, M, N, K, A, lda, B,
                   ldb, scale_a, scale_b, C, ldc, stream);
 }
 

@@ -136,7 +136,7 @@ CFG_SHAPES = [(520, 600, 520), (300, 260, 1030)]
 
 @pytest.mark.parametrize("out", OUTS)
 @pytest.mark.parametrize("prec", INT_PRECS)
-@pytest.mark.parametrize("cfg", [0, 1, 2, 4, 5])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("shape", CFG_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in CFG_SHAPES])
 def test_every_config(pd, dev, prec, out, cfg, shape):
     if cfg >= pd.num_configs():
@@ -222,20 +222,18 @@ def test_f16_output_two_byte_aligned(pd, dev):
     assert_bits_equal(C[:, 1:], oracle_dequant("i8", A, Bt, K, sa, sb, "f16"), "odd ldc")
 
 
-def test_ksplit_config_is_rejected(pd, dev):
-    gu.note("[case] dequant with the K-split configuration")
-    A = torch.zeros((8, 32), dtype=torch.int8, device=dev)
-    s8 = torch.ones(8, device=dev)
-    with pytest.raises(pd.PdgemmError) as e:
-        pd.gemm_i8_dequant(A, A, s8, s8, cfg=3)
-    assert e.value.code == -6
+# small M: the entry points pick the K-split tiles (3 = 32 x 32, 6 = 64 x 32)
+KSPLIT = [((16, 520, 300), 3), ((1, 1000, 1030), 3), ((40, 8200, 260), 6), ((64, 8192, 130), 6)]
 
 
-def test_small_m_uses_a_plain_tile(pd, dev):
-    # the entry points never pick the K-split tile for the dequantizing epilogue
-    M, N, K = 16, 520, 300
-    A, Bt, sa, sb, C = run_case(pd, dev, "i8", M, N, K, 12, "f32")
-    assert_bits_equal(C, oracle_dequant("i8", A, Bt, K, sa, sb, "f32"), "small M dequant")
+@pytest.mark.parametrize("out", OUTS)
+@pytest.mark.parametrize("prec", INT_PRECS)
+@pytest.mark.parametrize("shape,cfg", KSPLIT, ids=[f"{m}x{n}x{k}" for (m, n, k), _ in KSPLIT])
+def test_small_m_ksplit(pd, dev, prec, out, shape, cfg):
+    M, N, K = shape
+    assert pd.pick_config({"i8": 1, "i4": 2}[prec], M, N, K) == cfg
+    A, Bt, sa, sb, C = run_case(pd, dev, prec, M, N, K, 12 + M, out)
+    assert_bits_equal(C, oracle_dequant(prec, A, Bt, K, sa, sb, out), f"{prec}->{out} small M {shape}")
 
 
 def test_scale_vector_errors(pd, dev):
@@ -281,22 +279,25 @@ def test_unit_scales_match_plain_gemm(pd, dev, prec):
 
 @pytest.mark.parametrize("prec", INT_PRECS)
 @pytest.mark.parametrize("out", OUTS)
-def test_full_size_sampled(pd, dev, prec, out):
+@pytest.mark.parametrize("M", [16, 64, 8192])
+def test_full_size_sampled(pd, dev, prec, out, M):
+    """M x 8192 x 8192 (the first M rows of the 8192^3 operands) in the launch the
+    benchmark times; sampled entries bit for bit."""
     n = 8192
     sa_seed = synth.config_seed(5, n, synth.OPERAND_A)
     sb_seed = synth.config_seed(5, n, synth.OPERAND_B)
-    gu.note(f"[case] dequant {prec}->{out} {n}^3 seeds {sa_seed:#x}/{sb_seed:#x}")
-    A, Bt = synth.operands(prec, n, n, n, sa_seed, sb_seed)
-    sa, sb = synth.f32_scales(n, sa_seed + 2), synth.f32_scales(n, sb_seed + 3)
+    gu.note(f"[case] dequant {prec}->{out} {M}x{n}x{n} seeds {sa_seed:#x}/{sb_seed:#x}")
+    A, Bt = synth.operands(prec, M, n, n, sa_seed, sb_seed)
+    sa, sb = synth.f32_scales(M, sa_seed + 2), synth.f32_scales(n, sb_seed + 3)
     Ad, Bd = torch.from_numpy(A).to(dev), torch.from_numpy(Bt).to(dev)
     sad, sbd = torch.from_numpy(sa).to(dev), torch.from_numpy(sb).to(dev)
-    outv = torch.empty((n, n), dtype=torch.float32 if out == "f32" else torch.float16, device=dev)
+    outv = torch.empty((M, n), dtype=torch.float32 if out == "f32" else torch.float16, device=dev)
     go = pd.prepare(prec, Ad, Bd, outv, K=n, scales=(sad, sbd))
     go()
     torch.cuda.synchronize()
     C = outv.cpu().numpy()
     del Ad, Bd, outv
-    rows, cols = gu.sample_positions(n, n, 1024, seed=n + 1)
+    rows, cols = gu.sample_positions(M, n, 1024, seed=n + M)
     S = oracle.entries_i8(A, Bt, rows, cols) if prec == "i8" else oracle.entries_i4(A, Bt, rows, cols)
     want = oracle.dequant_entries(S, sa[rows], sb[cols], half_out=(out == "f16"))
-    assert_bits_equal(C[rows, cols], want, f"{prec}->{out} {n}^3 sampled")
+    assert_bits_equal(C[rows, cols], want, f"{prec}->{out} {M}x{n}x{n} sampled")
