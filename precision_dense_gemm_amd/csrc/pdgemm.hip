@@ -811,13 +811,14 @@ int validate(int prec, int epi, int br, int64_t M, int64_t N, int64_t K, const v
     if (M == 0 || N == 0) return PDGEMM_OK;
     if (!C || (K > 0 && (!A || !B))) return PDGEMM_ENULL;
     if (epi != kRaw && (!scale_a || !scale_b)) return PDGEMM_ENULL;
+    // operand tiles are addressed with 32-bit offsets from the tile's first
+    // row; the limit is checked in elements, before any byte count is formed
+    const int64_t c_size = epi == kDequantF16 ? 2 : 4;
+    const int64_t max_ld = kMaxRowBytes * 8 / elem_bits(prec);
+    if (lda > max_ld || ldb > max_ld || ldc > kMaxRowBytes / c_size) return PDGEMM_EINVAL_LD;
     const int64_t lda_bytes = lda * elem_bits(prec) / 8;
     const int64_t ldb_bytes = ldb * elem_bits(prec) / 8;
-    const int64_t c_size = epi == kDequantF16 ? 2 : 4;
     if ((lda_bytes & 15) || (ldb_bytes & 15)) return PDGEMM_EALIGN;
-    // operand tiles are addressed with 32-bit offsets from the tile's first row
-    if (lda_bytes > kMaxRowBytes || ldb_bytes > kMaxRowBytes || ldc * c_size > kMaxRowBytes)
-        return PDGEMM_EINVAL_LD;
     if (((uintptr_t)A & 15) || ((uintptr_t)B & 15) || ((uintptr_t)C & (c_size - 1))) return PDGEMM_EALIGN;
     if (epi != kRaw && (((uintptr_t)scale_a & 3) || ((uintptr_t)scale_b & 3))) return PDGEMM_EALIGN;
     return PDGEMM_OK;
