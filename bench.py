@@ -7,8 +7,9 @@ HBM before the timed region starts.  The JSON line reports:
 
   value         whole-step throughput in TOPS (2*M*N*K per GEMM, summed over
                 the sweep, divided by the wall time of a step)
-  per_gemm      per (precision, N): mean kernel time from HIP events on the
-                launch stream over the timed steps, TOPS, fraction of peak; and
+  per_gemm      per (precision, N): mean (also median and minimum) kernel time from
+                HIP events on the launch stream over the timed steps, TOPS, fraction
+                of peak; and
                 the same GEMM timed over back-to-back launches after the steps
   roofline      the GEMM that takes the largest share of a step, against the
                 MFMA peak of its own precision
@@ -445,12 +446,15 @@ def main():
 
     per = {}
     for (prec, n), pairs in ev.items():
-        ms = float(np.mean([s.elapsed_time(e) for s, e in pairs])) if pairs else float("nan")
+        times = [s.elapsed_time(e) for s, e in pairs]
+        ms = float(np.mean(times)) if times else float("nan")
         tops = gemm_ops(n) / (ms * 1e-3) / 1e12
         hbm_bytes = n * n * (2 * IN_BYTES[prec] + 4)
         ms_b = b2b[(prec, n)]
         per[f"{prec}:{n}"] = {
             "ms": round(ms, 5),
+            "ms_median": round(float(np.median(times)), 5) if times else None,
+            "ms_min": round(float(np.min(times)), 5) if times else None,
             "tops": round(tops, 2),
             "frac_of_peak": round(tops / PEAK[prec], 4),
             "ms_back_to_back": round(ms_b, 5),
