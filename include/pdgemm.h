@@ -50,7 +50,8 @@
  * K x N extents never reach a stored result.
  *
  * Ownership and execution: every pointer is device memory owned by the
- * caller.  The library never allocates, frees, copies or synchronizes.  The
+ * caller, on the device the stream belongs to.  C must not overlap A, B or
+ * the scales (the result is then undefined).  The library never allocates, frees, copies or synchronizes.  The
  * call enqueues work on `stream` (a hipStream_t passed as void*; NULL is the
  * default stream) and returns once it is enqueued.  Entry points are
  * thread-safe and keep no state between calls.

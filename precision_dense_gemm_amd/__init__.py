@@ -137,6 +137,9 @@ def _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None, N=None, ro
     M = A.shape[0]
     N = Bt.shape[0] if N is None else N
     ldc = _row_major_2d(out, "out")
+    tensors = [A, Bt, out] + ([] if scales is None else list(scales))
+    if any(isinstance(t, torch.Tensor) and t.device != out.device for t in tensors):
+        raise ValueError("operands, scales and out must be on the same GPU")
     if tuple(out.shape) != (M, N):
         raise ValueError(f"out must have shape {(M, N)}")
     if rowb:
