@@ -79,7 +79,9 @@ extern "C" {
 #define PDGEMM_ENULL (-3)       /* NULL pointer for an operand with nonzero extent */
 #define PDGEMM_EINVAL_I4 (-4)   /* gemm_i4: K, lda or ldb odd */
 #define PDGEMM_EALIGN (-5)      /* a pointer or leading dimension breaks the alignment rules */
-#define PDGEMM_EINVAL_CFG (-6)  /* unknown precision or tile configuration; dequantizing FP16 */
+#define PDGEMM_EINVAL_CFG (-6)  /* unknown precision or tile configuration, dequantizing FP16, or a
+                                   configuration without the variant (row-major B on a K-split tile);
+                                   reported before any other check */
 
 #define PDGEMM_I4_MAX_K 131071
 

@@ -829,6 +829,8 @@ int launch(int prec, int cfg, int epi, int br, int64_t M, int64_t N, int64_t K, 
            void *C, int64_t ldc, void *stream) {
     if (prec < 0 || prec > 2 || cfg < 0 || cfg >= kNumConfigs) return PDGEMM_EINVAL_CFG;
     if (epi != kRaw && prec == kF16) return PDGEMM_EINVAL_CFG;
+    const void *fn = kernel_ptr(prec, cfg, epi, br);   // null: no such kernel (e.g. K split, row-major B)
+    if (!fn) return PDGEMM_EINVAL_CFG;
     int rc = validate(prec, epi, br, M, N, K, A, lda, B, ldb, C, ldc, scale_a, scale_b);
     if (rc != PDGEMM_OK) return rc;
     if (M == 0 || N == 0) return PDGEMM_OK;
@@ -855,8 +857,6 @@ int launch(int prec, int cfg, int epi, int br, int64_t M, int64_t N, int64_t K, 
     // a launch counts its work-items in 32 bits
     if (blocks * threads > (int64_t)UINT32_MAX) return PDGEMM_EINVAL_DIM;
 
-    const void *fn = kernel_ptr(prec, cfg, epi, br);
-    if (!fn) return PDGEMM_EINVAL_CFG;
     void *kargs[] = {&args};
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), kargs, 0, s);

@@ -21,11 +21,14 @@ BITS = {0: 16, 1: 8, 2: 4}
 MAX_ROW = 1 << 22
 
 
-def model(prec, cfg, epi, rowb, M, N, K, A, lda, B, ldb, C, ldc, sa, sb, ksplit_cfgs, ncfg):
-    """Expected return code, or None when the call would reach the GPU."""
+def model(prec, cfg, epi, rowb, M, N, K, A, lda, B, ldb, C, ldc, sa, sb, ksplit_cfgs, ncfg, tiles=None):
+    """Expected return code, or None when the call would reach the GPU.  tiles maps a
+    configuration to (block rows, block cols, threads) for the work-item limit."""
     if not (0 <= prec <= 2) or not (0 <= cfg < ncfg):
         return ECFG
     if epi and prec == 0:
+        return ECFG
+    if rowb and cfg in ksplit_cfgs:
         return ECFG
     if M < 0 or N < 0 or K < 0 or M > 2 ** 31 - 1 or N > 2 ** 31 - 1 or K > 2 ** 30:
         return EDIM
@@ -50,8 +53,10 @@ def model(prec, cfg, epi, rowb, M, N, K, A, lda, B, ldb, C, ldc, sa, sb, ksplit_
         return EALIGN
     if epi and (sa % 4 or sb % 4):
         return EALIGN
-    if rowb and cfg in ksplit_cfgs:
-        return ECFG
+    if tiles is not None:
+        bm, bn, threads = tiles[cfg]
+        if -(-M // bm) * -(-N // bn) * threads > 2 ** 32 - 1:
+            return EDIM
     return None
 
 
@@ -64,14 +69,15 @@ def lib():
     L.pdgemm_dequant_cfg.argtypes = [i, i, i64, i64, i64, p, i64, p, i64, p, p, p, i64, i, p]
     L.pdgemm_config_info.argtypes = [i] + [ctypes.POINTER(i)] * 5
     n = L.pdgemm_num_configs()
-    ks = set()
+    ks, tiles = set(), {}
     for c in range(n):
         v = [ctypes.c_int() for _ in range(5)]
         L.pdgemm_config_info(c, *[ctypes.byref(x) for x in v])
         bm, bn, wm, wn, th = (x.value for x in v)
+        tiles[c] = (bm, bn, th)
         if th > (bm // wm) * (bn // wn) * 64:
             ks.add(c)
-    return L, n, ks
+    return L, n, ks, tiles
 
 
 def weighted(common, rare, pct_rare):
@@ -98,9 +104,9 @@ combos = weighted(st.sampled_from(VALID), st.sampled_from(INVALID), 10)
        sa=ptrs, sb=ptrs)
 def test_argument_checks_follow_the_documented_rules(lib, combo, M, N, K, A, lda, B, ldb, C, ldc,
                                                      sa, sb):
-    L, ncfg, ks = lib
+    L, ncfg, ks, tiles = lib
     prec, cfg, epi, rowb = combo
-    want = model(prec, cfg, epi, rowb, M, N, K, A, lda, B, ldb, C, ldc, sa, sb, ks, ncfg)
+    want = model(prec, cfg, epi, rowb, M, N, K, A, lda, B, ldb, C, ldc, sa, sb, ks, ncfg, tiles)
     if want is None:
         return   # a valid call: it would launch on the GPU
     if epi:
