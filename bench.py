@@ -27,7 +27,8 @@ HBM before the timed region starts.  The JSON line reports:
                 M in {16, 64, 256, 1024}: the first M rows of the sweep's
                 N = 8192 operands, timed back to back and placed on their own
                 roofline (HBM-bound below about M = 315 for f16 and i8, 157 for
-                i4), with a sampled parity check
+                i4), with a sampled parity check; also timed with the
+                dequantizing epilogue (i8, i4) and with B row-major
 
 Usage: python bench.py [--steps K] [--warmup W] [--case f16:8192] [--calib-copy]
 """
@@ -355,6 +356,7 @@ def main():
 
     # ---- B row-major at N = 8192 (not part of the step) ----
     layout = {}
+    brow_dev = {}   # the row-major B of each precision, reused by the shape section
     if not args.no_layout:
         for prec, n, Ad, Bd, C in work:
             if n != 8192:
@@ -398,7 +400,8 @@ def main():
             })
             layout[f"{prec}:{n}"] = entry
             log(f"[bench] row-major B {prec} N={n}: {ms_r:.4f} ms (column-major {ms_c:.4f} ms)")
-            del Brd, Cr
+            brow_dev[prec] = Brd
+            del Cr
 
     # ---- non-square inference shapes (not part of the step) ----
     shapes = {}
@@ -439,6 +442,10 @@ def main():
                     god = pd.prepare(prec, Ad[:M], Bd, Ch, K=n, scales=scl)
                     entry["dequant_f16_ms_back_to_back"] = round(time_b2b(god, 0.05), 5)
                     del Ch, scl
+                if prec in brow_dev:
+                    # the same product with B row-major
+                    gor = pd.prepare(prec, Ad[:M], brow_dev[prec], Cm, K=n, rowb=True)
+                    entry["rowb_ms_back_to_back"] = round(time_b2b(gor, 0.05), 5)
                 shapes[f"{prec}:{M}x{n}x{n}"] = entry
                 log(f"[bench] shape {prec} {M}x{n}x{n}: {ms * 1e3:.1f} us "
                     f"({entry['roofline']['bound']} {entry['roofline']['frac']:.3f})")

@@ -213,7 +213,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     static_assert(E == kRaw || P != kF16, "the dequantizing epilogue is for the integer paths");
     using RB = RowB<P>;
     constexpr int kCpr = BN / RB::kElemPerChunk;   // row-major B: 16-byte chunks per row of B
-    static_assert(BR == kBCol || (kCpr >= 2 && (kCpr & (kCpr - 1)) == 0), "row-major B tile width");
+    static_assert(BR == kBCol || (kCpr >= 1 && (kCpr & (kCpr - 1)) == 0), "row-major B tile width");
     // KS > 1 splits K over the waves: each of the KS waves computes the whole
     // BM x BN tile over its own 64-byte quarter (KS = 4) of every K tile,
     // from its own slice of each stage, and the partial tiles are summed
@@ -229,8 +229,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     constexpr int FM = WM / 32;
     constexpr int FN = WN / 32;
     static_assert(KS > 1 || ((BM / 16) % NW == 0 && (BN / 16) % NW == 0), "stage rows must split evenly over waves");
-    static_assert(KS == 1 || (NT == 1 && BR == kBCol && 16 % KS == 0),
-                  "the K-split variant computes the whole block tile per wave, column-major B");
+    static_assert(KS == 1 || (NT == 1 && 16 % KS == 0), "the K-split variant computes the whole block tile per wave");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(kStages == 4, "the main loop is unrolled for four stages");
     static_assert((kStages - 2) * kDma <= 63, "vmcnt holds at most 63 outstanding loads");
@@ -293,7 +292,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     const int64_t b_row_valid = ((int64_t)min(BN, N - n0) * (P == kF16 ? 16 : (P == kI8 ? 8 : 4)) + 7) / 8;
     const int64_t b_end = BR == kBRow ? (int64_t)(K - 1) * args.ldb_bytes + ((b_row_valid + 15) & ~int64_t(15))
                                       : (int64_t)(min(BN, N - n0) - 1) * args.ldb_bytes + valid16;
-    const int64_t b_tile_bytes = BR == kBRow ? (int64_t)RB::kKRows * args.ldb_bytes : kTileBytes;
+    // row-major B: a K tile is KS slices of kKRows rows of B
+    const int64_t b_tile_bytes = BR == kBRow ? (int64_t)KS * RB::kKRows * args.ldb_bytes : kTileBytes;
     const int lrow = lane >> 2;              // row within the 16-row group
     const int lpos = lane & 3;               // LDS position written by this lane
     uint32_t voff[kDma];
@@ -310,10 +310,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
             voff[j] = (uint32_t)((min(n0 + cr - BM, N - 1) - n0) * args.ldb_bytes) + lchunk * 16 + kofs;
         } else {
             // flat chunk f of the B part: row f / kCpr, position f % kCpr
+            // (K split: of this wave's slice, kKRows rows further on per slice)
             const int f = (cr - BM) * kChunks + lpos;
             const int krow = f / kCpr;
             const int gchunk = (f % kCpr) ^ bswizzle<P, BN>(krow);
-            voff[j] = (uint32_t)(krow * args.ldb_bytes) + gchunk * 16;
+            voff[j] = (uint32_t)((slice * RB::kKRows + krow) * args.ldb_bytes) + gchunk * 16;
         }
     }
 
@@ -323,9 +324,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(a_base + kb), (short)0, live ? a_end - kb : 0, kRsrcWord3);
         const int64_t bt = (int64_t)t * b_tile_bytes;
-        // a row-major tile spans kKRows rows of B; the range never exceeds it
+        // a row-major tile spans KS * kKRows rows of B; the range never
+        // exceeds it (nor 2^31 - 1: every offset a lane forms is below that)
         const int b_range = !live ? 0
-                            : BR == kBRow ? (int)min(b_end - bt, (int64_t)RB::kKRows * args.ldb_bytes)
+                            : BR == kBRow ? (int)min(min(b_end - bt, b_tile_bytes), (int64_t)INT32_MAX)
                                           : (int)(b_end - bt);
         const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(b_base + bt), (short)0, b_range, kRsrcWord3);
@@ -352,7 +354,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     const int tr_byte = 8 * (tr_i % RB::kQ);          // byte within the lane's chunks
     const int tr_col_bytes = (16 * ((lane >> 4) & 1)) * (P == kF16 ? 2 : 1) / (P == kI4 ? 2 : 1);
     auto read_b_rowmajor = [&](const Stage &buf, int s, int j) __attribute__((always_inline)) {
-        const char *bpart = reinterpret_cast<const char *>(&buf[BM][0]);
+        const char *bpart = reinterpret_cast<const char *>(&buf[srow + BM][0]);
         // bytes of K per k-step are 32: 16 f16, 32 int8 or 64 int4 rows, half per lane half
         constexpr int kStepRows = RB::kKRows / 2;
         const int col_bytes = ((wn0 + j * 32) * (P == kF16 ? 2 : 1) / (P == kI4 ? 2 : 1)) + tr_col_bytes + tr_byte;
@@ -721,10 +723,7 @@ constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 template <int P, int C, int E, int BR>
 const void *kernel_for() {
     constexpr Config c = kConfigs[C];
-    if constexpr (c.ks > 1 && BR != kBCol)
-        return nullptr;   // the K-split tiles take column-major B only
-    else
-        return reinterpret_cast<const void *>(&gemm_kernel<P, c.bm, c.bn, c.wm, c.wn, c.gm, E, BR, c.ks>);
+    return reinterpret_cast<const void *>(&gemm_kernel<P, c.bm, c.bn, c.wm, c.wn, c.gm, E, BR, c.ks>);
 }
 
 template <int P, int E, int BR>
@@ -781,18 +780,16 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // The largest tile (in kPickOrder) that still gives every CU (256) at least
 // one workgroup.  When even the 64 x 64 tile leaves CUs idle (small M or N),
-// a K-split tile (where it applies: column-major B) puts 4 waves on each of
-// up to 4 times as many tiles.
+// a K-split tile puts 4 waves on each of up to 4 times as many tiles.
 // INT4 skips the 256 x 128 tile: its in-register unpack costs more VALU per
 // MFMA on the narrower wave tile, and two 128 x 128 workgroups per CU hide
 // it better (measured at M = 1024, N = K = 8192).
-int pick(int prec, int64_t M, int64_t N, int64_t K, bool ksplit_ok) {
+int pick(int prec, int64_t M, int64_t N, int64_t K) {
     (void)K;
     for (int c : kPickOrder) {
         if (prec == kI4 && c == 4) continue;
         if (cdiv(M, kConfigs[c].bm) * cdiv(N, kConfigs[c].bn) >= 256) return c;
     }
-    if (!ksplit_ok) return 2;
     // K split: 64 x 32 when more than 32 rows still fill the chip (each B
     // panel is then staged once rather than once per 32 rows), else 32 x 32
     if (M > 32 && cdiv(M, 64) * cdiv(N, 32) >= 256) return 6;
@@ -874,33 +871,33 @@ extern "C" {
 
 int gemm_f16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
              const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream) {
-    return launch(kF16, pick(kF16, M, N, K, true), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
+    return launch(kF16, pick(kF16, M, N, K), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
                   stream);
 }
 
 int gemm_i8(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
             const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
-    return launch(kI8, pick(kI8, M, N, K, true), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
+    return launch(kI8, pick(kI8, M, N, K), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
                   stream);
 }
 
 int gemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
             const uint8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
-    return launch(kI4, pick(kI4, M, N, K, true), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
+    return launch(kI4, pick(kI4, M, N, K), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
                   stream);
 }
 
 int gemm_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
                     const int8_t *B, int64_t ldb, const float *scale_a, const float *scale_b,
                     void *C, int64_t ldc, int out_f16, void *stream) {
-    return launch(kI8, pick(kI8, M, N, K, true), out_f16 ? kDequantF16 : kDequantF32, kBCol, M, N, K, A, lda, B,
+    return launch(kI8, pick(kI8, M, N, K), out_f16 ? kDequantF16 : kDequantF32, kBCol, M, N, K, A, lda, B,
                   ldb, scale_a, scale_b, C, ldc, stream);
 }
 
 int gemm_i4_dequant(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
                     const uint8_t *B, int64_t ldb, const float *scale_a, const float *scale_b,
                     void *C, int64_t ldc, int out_f16, void *stream) {
-    return launch(kI4, pick(kI4, M, N, K, true), out_f16 ? kDequantF16 : kDequantF32, kBCol, M, N, K, A, lda, B,
+    return launch(kI4, pick(kI4, M, N, K), out_f16 ? kDequantF16 : kDequantF32, kBCol, M, N, K, A, lda, B,
                   ldb, scale_a, scale_b, C, ldc, stream);
 }
 
@@ -920,19 +917,19 @@ int pdgemm_dequant_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K, const
 
 int gemm_f16_rowb(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
                   const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream) {
-    return launch(kF16, pick(kF16, M, N, K, false), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
+    return launch(kF16, pick(kF16, M, N, K), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
                   C, ldc, stream);
 }
 
 int gemm_i8_rowb(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
                  const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
-    return launch(kI8, pick(kI8, M, N, K, false), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
+    return launch(kI8, pick(kI8, M, N, K), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
                   C, ldc, stream);
 }
 
 int gemm_i4_rowb(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
                  const uint8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
-    return launch(kI4, pick(kI4, M, N, K, false), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
+    return launch(kI4, pick(kI4, M, N, K), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
                   C, ldc, stream);
 }
 
@@ -947,7 +944,7 @@ int pdgemm_num_configs(void) { return kNumConfigs; }
 
 int pdgemm_pick_config(int prec, int64_t M, int64_t N, int64_t K) {
     if (prec < 0 || prec > 2) return -1;
-    return pick(prec, M, N, K, true);
+    return pick(prec, M, N, K);
 }
 
 int pdgemm_config_info(int cfg, int *block_m, int *block_n, int *wave_m, int *wave_n,

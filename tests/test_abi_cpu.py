@@ -176,12 +176,11 @@ def test_dequant_cfg_errors(lib):
     assert lib.pdgemm_dequant_cfg(1, n, *args) == c["PDGEMM_EINVAL_CFG"]
     assert lib.pdgemm_dequant_cfg(2, -1, *args) == c["PDGEMM_EINVAL_CFG"]
     assert lib.pdgemm_dequant_cfg(3, 0, *args) == c["PDGEMM_EINVAL_CFG"]
-    # the K-split tiles take column-major B only (the dequantizing epilogue is fine)
+    # every variant exists on the K-split tiles; argument errors are found before any HIP call
     ks = [cfg for cfg in range(n) if _k_split(lib, cfg) > 1]
     assert ks, "no K-split configuration"
     for cfg in ks:
-        assert lib.pdgemm_gemm_rowb_cfg(1, cfg, 64, 64, 64, PA, 64, PB, 64, PC, 64, None) == c["PDGEMM_EINVAL_CFG"]
-        # argument errors are still found first, before any HIP call
+        assert lib.pdgemm_gemm_rowb_cfg(1, cfg, 64, 64, 64, PA, 64, None, 64, PC, 64, None) == c["PDGEMM_ENULL"]
         assert lib.pdgemm_dequant_cfg(1, cfg, 64, 64, 64, PA, 64, PB, 64, None, PSB, PC, 64, 0,
                                       None) == c["PDGEMM_ENULL"]
 

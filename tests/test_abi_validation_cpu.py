@@ -28,8 +28,6 @@ def model(prec, cfg, epi, rowb, M, N, K, A, lda, B, ldb, C, ldc, sa, sb, ksplit_
         return ECFG
     if epi and prec == 0:
         return ECFG
-    if rowb and cfg in ksplit_cfgs:
-        return ECFG
     if M < 0 or N < 0 or K < 0 or M > 2 ** 31 - 1 or N > 2 ** 31 - 1 or K > 2 ** 30:
         return EDIM
     if prec == 2 and K > 131071:

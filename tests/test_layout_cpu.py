@@ -67,7 +67,9 @@ ROWB = {  # precision: (rows per K tile, rows per read R, elements per 16-byte c
     "i8": (64, 8, 16, 8),
     "i4": (128, 16, 32, 4),
 }
-CONFIGS = [(256, 256, 128, 128), (128, 128, 64, 64), (64, 64, 32, 32), (256, 128, 128, 64), (128, 64, 64, 32)]
+# the tiles without K split, and one K slice of the K-split tiles (32 x 32, 64 x 32)
+CONFIGS = [(256, 256, 128, 128), (128, 128, 64, 64), (64, 64, 32, 32), (256, 128, 128, 64), (128, 64, 64, 32),
+           (32, 32, 32, 32), (64, 32, 64, 32)]
 
 
 def bswizzle(prec, bn, r):
@@ -89,7 +91,7 @@ def tr_source(prec, i, e):
 
 
 @pytest.mark.parametrize("prec", ["f16", "i8", "i4"])
-@pytest.mark.parametrize("cfg", CONFIGS, ids=["256", "128", "64", "256x128", "128x64"])
+@pytest.mark.parametrize("cfg", CONFIGS, ids=["256", "128", "64", "256x128", "128x64", "ks32x32", "ks64x32"])
 def test_rowmajor_b_layout(prec, cfg):
     BM, BN, WM, WN = cfg
     krows, R, epc, bits = ROWB[prec]

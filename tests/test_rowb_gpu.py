@@ -113,12 +113,26 @@ CFG_SHAPES = [(520, 600, 520), (300, 260, 1030), (64, 700, 130)]
 
 
 @pytest.mark.parametrize("prec", PRECS)
-@pytest.mark.parametrize("cfg", [0, 1, 2, 4, 5])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("shape", CFG_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in CFG_SHAPES])
 def test_every_config(pd, dev, prec, cfg, shape):
     M, N, K = shape
     A, B, C = run_case(pd, dev, prec, M, N, K, 300 + cfg, cfg=cfg)
     check(prec, C, oracle_rowb(prec, A, B, N, K), f"rowb {prec} cfg{cfg} {shape}")
+
+
+# small M: the K-split tiles (3 = 32 x 32, 6 = 64 x 32), each wave on its own
+# slice of K rows of B
+KSPLIT = [((16, 700, 1030), 3), ((1, 96, 258), 3), ((50, 8200, 260), 6), ((64, 8192, 130), 6)]
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("shape,cfg", KSPLIT, ids=[f"{m}x{n}x{k}" for (m, n, k), _ in KSPLIT])
+def test_small_m_ksplit(pd, dev, prec, shape, cfg):
+    M, N, K = shape
+    assert pd.pick_config({"f16": 0, "i8": 1, "i4": 2}[prec], M, N, K) == cfg
+    A, B, C = run_case(pd, dev, prec, M, N, K, 900 + M)
+    check(prec, C, oracle_rowb(prec, A, B, N, K), f"rowb {prec} small M {shape}")
 
 
 def test_mma_lab_example_with_row_major_b(pd, dev):
