@@ -27,7 +27,12 @@
 //    256*a*b and the int32 sum is exactly 256*C (no overflow while
 //    16384*K < 2^31, K <= 131071).  The epilogue shifts right by 8 (exact).
 //  * Staging: buffer_load_dwordx4 ... lds, a direct global -> LDS copy in
-//    16-byte chunks, four stages deep.  The 16-byte chunks of each LDS row are
+//    16-byte chunks.  With column-major B and no K split a stage holds 128
+//    bytes of K per row, so that every DMA instruction requests whole
+//    128-byte lines (the L2 returns whole lines: staging 64-byte pieces of
+//    them doubles the L2 -> CU traffic), two or three stages deep; the other
+//    variants stage 64 bytes per row, four stages deep.  The 16-byte chunks
+//    of each LDS row are
 //    XOR-swizzled by the row index so that fragment reads are free of bank
 //    conflicts (the paper pads shared rows for the same purpose; a swizzle
 //    keeps rows dense).
@@ -55,6 +60,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+#include <type_traits>
 
 #include "pdgemm.h"
 
@@ -102,6 +109,13 @@ constexpr int kRsrcWord3 = 0x00020000;
 // any 8 consecutive rows have distinct pairs (r%2, p).
 // ((r >> 1) & 3) ^ ((r >> 3) & 1) satisfies both.
 __device__ __forceinline__ int swizzle(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
+// The same for rows of 128 bytes (eight chunks), where row r's position p
+// covers banks 32*(r%2) + 4p .. +3 of 64: the 16 lanes of a quarter-wave
+// are conflict-free iff the pairs (r%2, p) are all distinct, and with 32
+// banks iff any 8 consecutive rows have distinct p.  (r & 7) ^ ((r >> 3) & 1)
+// satisfies both.
+__device__ __forceinline__ int swizzle8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 __device__ __forceinline__ floatx16_t mfma_f16(const uint4 &a, const uint4 &b, const floatx16_t &c) {
     half8_t av, bv;
@@ -203,7 +217,16 @@ __device__ __forceinline__ int bswizzle(int r) {
 // only for its own DMA of tile t+1 (tiles t+2 .. t+kStages-1 stay in
 // flight), so after the barrier tile t+1 is complete in LDS and stage t is
 // free for tile t+kStages.
-template <int P, int BM, int BN, int WM, int WN, int GM, int E, int BR, int KS>
+//
+// Whole-line staging (LS > 0, column-major B, no K split): a stage holds two
+// K tiles, 128 bytes per row in eight 16-byte chunks, logical chunk c of row
+// r at position c ^ swizzle8(r); each DMA instruction of a wave writes 1 KB =
+// 8 whole rows, lane l landing in row l/8 at position l%8, so each
+// instruction reads whole 128-byte lines.  LS stages: stage s is fetched LS
+// stages before it is consumed, four k-steps per stage, and the one barrier
+// of a stage comes after its last fragments are in registers, once this
+// wave's DMA of stage s+1 has landed (stages s+2 .. s+LS-1 stay in flight).
+template <int P, int BM, int BN, int WM, int WN, int GM, int E, int BR, int KS, int LS>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kernel(Args args) {
     // The body uses gfx950-only types (buffer resources), which the host
     // pass cannot type-check; the host pass only needs the launch stub.
@@ -233,14 +256,26 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(kStages == 4, "the main loop is unrolled for four stages");
     static_assert((kStages - 2) * kDma <= 63, "vmcnt holds at most 63 outstanding loads");
+    // whole-line staging: 8 rows of 128 bytes per DMA instruction
+    constexpr bool kLine = LS > 0 && BR == kBCol && KS == 1;
+    constexpr int kDmaL = kRows / 8 / NW;    // DMA instructions per wave per stage
+    constexpr int kDmaLA = BM / 8 / NW;      // ... of which fill A rows
+    static_assert(!kLine || (BM % (8 * NW) == 0 && BN % (8 * NW) == 0), "stage rows must split evenly over waves");
+    static_assert(!kLine || (LS == 2 || LS == 3), "the whole-line loop is unrolled for two or three stages");
+    static_assert(!kLine || (LS - 1) * kDmaL <= 63, "vmcnt holds at most 63 outstanding loads");
 
     // The stages are separate objects so that the compiler can tell a DMA
-    // into one from fragment reads of another (no false waits).
-    __shared__ uint4 lds0[kRows][kChunks];
-    __shared__ uint4 lds1[kRows][kChunks];
-    __shared__ uint4 lds2[kRows][kChunks];
-    __shared__ uint4 lds3[kRows][kChunks];
+    // into one from fragment reads of another (no false waits).  Only one of
+    // the two sets is used.
+    __shared__ uint4 lds0[kLine ? 1 : kRows][kChunks];
+    __shared__ uint4 lds1[kLine ? 1 : kRows][kChunks];
+    __shared__ uint4 lds2[kLine ? 1 : kRows][kChunks];
+    __shared__ uint4 lds3[kLine ? 1 : kRows][kChunks];
+    __shared__ uint4 ln0[kLine ? kRows : 1][2 * kChunks];
+    __shared__ uint4 ln1[kLine ? kRows : 1][2 * kChunks];
+    __shared__ uint4 ln2[kLine && LS > 2 ? kRows : 1][2 * kChunks];
     using Stage = uint4[kRows][kChunks];
+    using LStage = uint4[kLine ? kRows : 1][2 * kChunks];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -470,15 +505,20 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     // fragment) and the row-major B read addresses (about 3 per read)
     constexpr int kValuWork = (P == kI4 ? 12 * (FM + FN) : 0) + (BR == kBRow ? 6 * FN : 0);
     constexpr int kValu = (kValuWork + kMfma - 1) / kMfma;
-    auto interleave = [&](int dma) __attribute__((always_inline)) {
+    // (whole-line staging issues a stage's DMA after its last barrier,
+    // several per MFMA when there are more DMAs than MFMAs)
+    auto interleave = [&](auto dma_count) __attribute__((always_inline)) {
+        constexpr int dma = decltype(dma_count)::value;
+        constexpr int per = kLine && dma > kMfma ? (dma + kMfma - 1) / kMfma : 1;
 #pragma unroll
         for (int i = 0; i < kMfma; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // 1 MFMA
             if (i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-            if (i < dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // 1 VMEM (DMA)
+            if (i * per < dma) __builtin_amdgcn_sched_group_barrier(0x020, per, 0);  // VMEM (DMA)
             if (kValu) __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU (planes)
         }
     };
+    using NoDma = std::integral_constant<int, 0>;
 
     // K tile t (not the last) from stage `cur`, whose first fragments are in
     // fa0/fb0; refills `cur` with tile t+kStages (a no-op past the last tile)
@@ -486,7 +526,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     auto tile = [&](Stage &cur, const Stage &next, int t) __attribute__((always_inline)) {
         read_frags(cur, 1, fa1, fb1);
         mma(fa0, fb0);
-        interleave(0);
+        interleave(NoDma{});
         // this wave's DMA of tile t+1 has landed (only tiles t+2 .. t+3 may
         // still be in flight) and its reads of `cur` are done; after the
         // barrier the same holds for every wave
@@ -498,7 +538,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
         stage(t + kStages, cur);
         read_frags(next, 0, fa0, fb0);
         mma(fa1, fb1);
-        interleave(kDma);
+        interleave(std::integral_constant<int, kDma>{});
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -528,44 +568,184 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
             scale_v[x] = idx < BM ? args.scale_a[min(m0 + idx, M - 1)] : args.scale_b[min(n0 + idx - BM, N - 1)];
     }
 
-    if (n_tiles > 0) {
-        stage(0, lds0);
-        stage(1, lds1);
-        stage(2, lds2);
-        stage(3, lds3);
+    if constexpr (kLine) {
+        // ---- whole-line staging ----
+        constexpr int kLineBytes = 2 * kRowBytes;
+        const int n_st = (valid + kLineBytes - 1) / kLineBytes;   // stages of two K tiles
+        // lane offsets: instruction j of this wave fills rows
+        // (j*NW + wave)*8 .. +7; lane l fetches logical chunk
+        // (l%8) ^ swizzle8(row) of row (l/8), rows clamped as above
+        uint32_t voffl[kDmaL];
 #pragma unroll
-        for (int x = 0; x < kScaleLoads; ++x)
-            if (tid + x * kThreads < BM + BN) lds_scale[tid + x * kThreads] = scale_v[x];
-        if constexpr (KS > 1)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 1) * kDma) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((kStages - 1) * kDma) : "memory");
-        read_frags(lds0, 0, fa0, fb0);
-        int t = 0;
-        for (; t + kStages < n_tiles; t += kStages) {
-            tile(lds0, lds1, t);
-            tile(lds1, lds2, t + 1);
-            tile(lds2, lds3, t + 2);
-            tile(lds3, lds0, t + 3);
+        for (int j = 0; j < kDmaL; ++j) {
+            const int cr = (j * NW + wave) * 8 + (lane >> 3);
+            const int lchunk = (lane & 7) ^ swizzle8(cr);
+            if (j < kDmaLA)
+                voffl[j] = (uint32_t)((min(m0 + cr, M - 1) - m0) * args.lda_bytes) + lchunk * 16;
+            else
+                voffl[j] = (uint32_t)((min(n0 + cr - BM, N - 1) - n0) * args.ldb_bytes) + lchunk * 16;
         }
-        // 1 to 4 tiles remain, the first of them in lds0
-        if (t + 1 < n_tiles) {
-            tile(lds0, lds1, t++);
-            if (t + 1 < n_tiles) {
-                tile(lds1, lds2, t++);
-                if (t + 1 < n_tiles) tile(lds2, lds3, t++);
+        auto stage_l = [&](int st, LStage &buf) __attribute__((always_inline)) {
+            const int kb = st * kLineBytes;
+            const bool live = st < n_st;
+            const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(a_base + kb), (short)0, live ? a_end - kb : 0, kRsrcWord3);
+            const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(b_base + kb), (short)0, live ? (int)(b_end - kb) : 0, kRsrcWord3);
+#pragma unroll
+            for (int j = 0; j < kDmaL; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kDmaLA ? ra : rb,
+                                                         LDS_PTR(&buf[(j * NW + wave) * 8][0]), 16, voffl[j], 0, 0, 0);
+        };
+        // fragments of k-step q (0..3) of a stage: logical chunk 2q + half
+        auto read_l = [&](const LStage &buf, int q, uint4 (&fa)[FM], uint4 (&fb)[FN]) __attribute__((always_inline)) {
+            const int ch = (2 * q + fhalf) ^ swizzle8(frow);   // fragment rows start at multiples of 32
+#pragma unroll
+            for (int i = 0; i < FM; ++i) fa[i] = buf[wm0 + i * 32 + frow][ch];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) fb[j] = buf[BM + wn0 + j * 32 + frow][ch];
+        };
+        // zero the bytes of k-step q of stage st at or beyond K
+        auto mask_l = [&](int st, int q, uint4 (&fa)[FM], uint4 (&fb)[FN]) __attribute__((always_inline)) {
+            const int nb = valid - (st * kLineBytes + (2 * q + fhalf) * 16);
+            uint32_t m[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int r = nb - 4 * d;
+                m[d] = r >= 4 ? 0xFFFFFFFFu : (r <= 0 ? 0u : (1u << (8 * r)) - 1u);
             }
-        }
-        const int last = t & 3;
-        last_tile(last == 0 ? lds0 : last == 1 ? lds1 : last == 2 ? lds2 : lds3, t);
-        // no DMA may still be writing this workgroup's LDS when it exits
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    } else if constexpr (E != kRaw) {
-        // K == 0: no main loop, so stage the scales here
 #pragma unroll
-        for (int x = 0; x < kScaleLoads; ++x)
-            if (tid + x * kThreads < BM + BN) lds_scale[tid + x * kThreads] = scale_v[x];
-        __syncthreads();
+            for (int i = 0; i < FM; ++i) {
+                fa[i].x &= m[0];
+                fa[i].y &= m[1];
+                fa[i].z &= m[2];
+                fa[i].w &= m[3];
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                fb[j].x &= m[0];
+                fb[j].y &= m[1];
+                fb[j].z &= m[2];
+                fb[j].w &= m[3];
+            }
+        };
+        // stage st (not the last) from `cur`, whose first fragments are in
+        // fa0/fb0; refills `cur` with stage st+LS and reads the first
+        // fragments of stage st+1 from `nxt`
+        auto full_stage = [&](LStage &cur, const LStage &nxt, int st) __attribute__((always_inline)) {
+            read_l(cur, 1, fa1, fb1);
+            mma(fa0, fb0);
+            interleave(NoDma{});
+            read_l(cur, 2, fa0, fb0);
+            mma(fa1, fb1);
+            interleave(NoDma{});
+            read_l(cur, 3, fa1, fb1);
+            mma(fa0, fb0);
+            interleave(NoDma{});
+            // this wave's DMA of stage st+1 has landed and its reads of `cur`
+            // are done; after the barrier the same holds for every wave
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((LS - 2) * kDmaL) : "memory");
+            stage_l(st + LS, cur);
+            read_l(nxt, 0, fa0, fb0);
+            mma(fa1, fb1);
+            interleave(std::integral_constant<int, kDmaL>{});
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // the last stage, with the bytes at or beyond K masked off
+        auto last_stage = [&](const LStage &cur, int st) __attribute__((always_inline)) {
+            read_l(cur, 1, fa1, fb1);
+            mask_l(st, 0, fa0, fb0);
+            mma(fa0, fb0);
+            read_l(cur, 2, fa0, fb0);
+            mask_l(st, 1, fa1, fb1);
+            mma(fa1, fb1);
+            read_l(cur, 3, fa1, fb1);
+            mask_l(st, 2, fa0, fb0);
+            mma(fa0, fb0);
+            mask_l(st, 3, fa1, fb1);
+            mma(fa1, fb1);
+        };
+        if (n_st > 0) {
+            stage_l(0, ln0);
+            stage_l(1, ln1);
+            if constexpr (LS > 2) stage_l(2, ln2);
+#pragma unroll
+            for (int x = 0; x < kScaleLoads; ++x)
+                if (tid + x * kThreads < BM + BN) lds_scale[tid + x * kThreads] = scale_v[x];
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((LS - 1) * kDmaL) : "memory");
+            read_l(ln0, 0, fa0, fb0);
+            int st = 0;
+            if constexpr (LS == 2) {
+                for (; st + 2 < n_st; st += 2) {
+                    full_stage(ln0, ln1, st);
+                    full_stage(ln1, ln0, st + 1);
+                }
+                if (st + 1 < n_st) full_stage(ln0, ln1, st++);
+                last_stage((st & 1) ? ln1 : ln0, st);
+            } else {
+                for (; st + 3 < n_st; st += 3) {
+                    full_stage(ln0, ln1, st);
+                    full_stage(ln1, ln2, st + 1);
+                    full_stage(ln2, ln0, st + 2);
+                }
+                // 1 to 3 stages remain, the first of them in ln0
+                if (st + 1 < n_st) {
+                    full_stage(ln0, ln1, st++);
+                    if (st + 1 < n_st) full_stage(ln1, ln2, st++);
+                }
+                const int r = st % 3;
+                last_stage(r == 0 ? ln0 : r == 1 ? ln1 : ln2, st);
+            }
+            // no DMA may still be writing this workgroup's LDS when it exits
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        } else if constexpr (E != kRaw) {
+            // K == 0: no main loop, so stage the scales here
+#pragma unroll
+            for (int x = 0; x < kScaleLoads; ++x)
+                if (tid + x * kThreads < BM + BN) lds_scale[tid + x * kThreads] = scale_v[x];
+            __syncthreads();
+        }
+    } else {
+        if (n_tiles > 0) {
+            stage(0, lds0);
+            stage(1, lds1);
+            stage(2, lds2);
+            stage(3, lds3);
+    #pragma unroll
+            for (int x = 0; x < kScaleLoads; ++x)
+                if (tid + x * kThreads < BM + BN) lds_scale[tid + x * kThreads] = scale_v[x];
+            if constexpr (KS > 1)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 1) * kDma) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((kStages - 1) * kDma) : "memory");
+            read_frags(lds0, 0, fa0, fb0);
+            int t = 0;
+            for (; t + kStages < n_tiles; t += kStages) {
+                tile(lds0, lds1, t);
+                tile(lds1, lds2, t + 1);
+                tile(lds2, lds3, t + 2);
+                tile(lds3, lds0, t + 3);
+            }
+            // 1 to 4 tiles remain, the first of them in lds0
+            if (t + 1 < n_tiles) {
+                tile(lds0, lds1, t++);
+                if (t + 1 < n_tiles) {
+                    tile(lds1, lds2, t++);
+                    if (t + 1 < n_tiles) tile(lds2, lds3, t++);
+                }
+            }
+            const int last = t & 3;
+            last_tile(last == 0 ? lds0 : last == 1 ? lds1 : last == 2 ? lds2 : lds3, t);
+            // no DMA may still be writing this workgroup's LDS when it exits
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        } else if constexpr (E != kRaw) {
+            // K == 0: no main loop, so stage the scales here
+    #pragma unroll
+            for (int x = 0; x < kScaleLoads; ++x)
+                if (tid + x * kThreads < BM + BN) lds_scale[tid + x * kThreads] = scale_v[x];
+            __syncthreads();
+        }
+
     }
 
     // ---- K-split epilogue: sum the partial tiles, then store ----
@@ -702,18 +882,21 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
 // ---------------------------------------------------------------------------
 // host side
 
+// ls: whole-line stages (column-major B; 0 = 64-byte stages throughout).
+// 256 x 256 fits two 64 KB stages; 128 x 128 keeps two so that two
+// workgroups share a CU; the others take three.
 struct Config {
-    int bm, bn, wm, wn, gm, ks;
+    int bm, bn, wm, wn, gm, ks, ls;
 };
 
 constexpr Config kConfigs[] = {
-    {256, 256, 128, 128, 4, 1},  // 0: large shapes
-    {128, 128, 64, 64, 8, 1},    // 1: medium
-    {64, 64, 32, 32, 8, 1},      // 2: small
-    {32, 32, 32, 32, 8, 4},      // 3: few tiles (small M or N): K split over 4 waves
-    {256, 128, 128, 64, 4, 1},   // 4: between 0 and 1 (e.g. M = 1024 of a wide product)
-    {128, 64, 64, 32, 8, 1},     // 5: between 1 and 2 (e.g. M = 256)
-    {64, 32, 64, 32, 8, 4},      // 6: K split over 4 waves, 64 rows (e.g. M = 64 of a wide product)
+    {256, 256, 128, 128, 4, 1, 2},  // 0: large shapes
+    {128, 128, 64, 64, 8, 1, 2},    // 1: medium
+    {64, 64, 32, 32, 8, 1, 3},      // 2: small
+    {32, 32, 32, 32, 8, 4, 0},      // 3: few tiles (small M or N): K split over 4 waves
+    {256, 128, 128, 64, 4, 1, 3},   // 4: between 0 and 1 (e.g. M = 1024 of a wide product)
+    {128, 64, 64, 32, 8, 1, 3},     // 5: between 1 and 2 (e.g. M = 256)
+    {64, 32, 64, 32, 8, 4, 0},      // 6: K split over 4 waves, 64 rows (e.g. M = 64 of a wide product)
 };
 
 // Tiles without K split, largest first: the order in which pick() tries them.
@@ -723,7 +906,7 @@ constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 template <int P, int C, int E, int BR>
 const void *kernel_for() {
     constexpr Config c = kConfigs[C];
-    return reinterpret_cast<const void *>(&gemm_kernel<P, c.bm, c.bn, c.wm, c.wn, c.gm, E, BR, c.ks>);
+    return reinterpret_cast<const void *>(&gemm_kernel<P, c.bm, c.bn, c.wm, c.wn, c.gm, E, BR, c.ks, c.ls>);
 }
 
 template <int P, int E, int BR>

@@ -4,6 +4,8 @@ from __future__ import annotations
 
 import itertools
 
+import pytest
+
 
 def swizzle(r: int) -> int:
     # LDS position of logical 16-byte chunk c of 64-byte row r is c ^ swizzle(r)
@@ -25,6 +27,50 @@ def test_fragment_reads_are_bank_conflict_free():
             # 32 banks: each group of 8 lanes must cover distinct 16-byte bank groups
             for o in (0, 8):
                 assert len({16 * (r % 2) + 4 * (c ^ swizzle(r)) for r in rows[o:o + 8]}) == 8
+
+
+
+def swizzle8(r: int) -> int:
+    # rows of 128 bytes (whole-line staging): logical chunk c of row r sits at c ^ swizzle8(r)
+    return (r & 7) ^ ((r >> 3) & 1)
+
+
+def test_line_swizzle_is_a_permutation_of_each_row():
+    for r in range(1024):
+        assert sorted(c ^ swizzle8(r) for c in range(8)) == list(range(8))
+
+
+def test_line_fragment_reads_are_bank_conflict_free():
+    # a quarter-wave reads 16 consecutive rows (from a multiple of 16) at one logical chunk;
+    # a 128-byte row r at position p covers banks 32*(r%2) + 4p .. +3 of 64
+    for base in range(0, 1024, 16):
+        rows = [base + i for i in range(16)]
+        for c in range(8):
+            assert len({32 * (r % 2) + 4 * (c ^ swizzle8(r)) for r in rows}) == 16
+            # 32 banks: 8 consecutive rows at distinct positions
+            for o in (0, 8):
+                assert len({c ^ swizzle8(r) for r in rows[o:o + 8]}) == 8
+
+
+@pytest.mark.parametrize("bm,bn,waves", [(256, 256, 4), (128, 128, 4), (64, 64, 4), (256, 128, 4), (128, 64, 4)])
+def test_line_dma_fills_every_row_once(bm, bn, waves):
+    # instruction j of wave w writes LDS rows (j*waves + w)*8 .. +7, lane l to row l/8 at
+    # position l%8, fetching logical chunk (l%8) ^ swizzle8(row) of that row: every
+    # (row, position) is written once, with the chunk the fragment reads expect there
+    rows = bm + bn
+    per_wave = rows // 8 // waves
+    seen = {}
+    for w in range(waves):
+        for j in range(per_wave):
+            for lane in range(64):
+                r = (j * waves + w) * 8 + lane // 8
+                pos = lane % 8
+                assert (r, pos) not in seen
+                seen[(r, pos)] = pos ^ swizzle8(r)
+    assert len(seen) == rows * 8
+    for r in range(rows):
+        for c in range(8):
+            assert seen[(r, c ^ swizzle8(r))] == c
 
 
 def remap(bid, nb, tiles_m, tiles_n, band):
@@ -60,7 +106,6 @@ def test_xcd_locality_at_8192():
 # lane i comes from the 8 bytes addressed by source lane j at element p, with
 # (j, p) = (i//4 + 4e, i%4) for b16, (i//8 + 2e, i%8) for b8, (e, i) for b4).
 
-import pytest  # noqa: E402
 
 ROWB = {  # precision: (rows per K tile, rows per read R, elements per 16-byte chunk, bits)
     "f16": (32, 4, 8, 16),
