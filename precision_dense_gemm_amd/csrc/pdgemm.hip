@@ -962,45 +962,46 @@ bool sync_check_enabled() {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Steady throughput of each tile without K split, in TFLOP/s (FP16) or TOP/s
-// (INT8, INT4), measured on a product that gives every one of them whole
-// rounds of one workgroup per CU (M = K = 8192, N = 6144); only the ratios
-// within a row matter.  0 = not a candidate: the K-split tiles, and INT4's
-// 256 x 128 tile, whose in-register unpack costs more VALU per MFMA on the
-// narrower wave tile (at M = 1024, N = K = 8192 one such workgroup per CU ran
-// 13% slower than two 128 x 128 ones).
+// (INT8, INT4): the median of five alternated back-to-back timings on a
+// product that gives every one of them whole rounds of workgroups
+// (M = K = 8192, N = 6144); only the ratios within a row matter.  0 = not a
+// candidate (the K-split tiles).  INT4 runs fastest on 128 x 128: two
+// workgroups per CU hide its in-register unpack.
 constexpr int kTileRate[3][kNumConfigs] = {
-    {1094, 844, 530, 0, 1033, 642, 0},     // FP16
-    {2179, 1549, 1054, 0, 1984, 1279, 0},  // INT8
-    {2313, 2221, 1608, 0, 0, 2019, 0},     // INT4
+    {1261, 1098, 695, 0, 1158, 862, 0},    // FP16
+    {2440, 2172, 1402, 0, 2194, 1728, 0},  // INT8
+    {2415, 2569, 1893, 0, 2376, 2033, 0},  // INT4
 };
 
 // When the 64 x 64 tile fills the chip (at least one workgroup per CU), a
-// time model chooses among the tiles that give at least half the CUs one:
-// the busiest CU sets the time, so a product of T tiles takes T / 256 rounds,
-// each of which costs the tile's area over its throughput.  A partial last
-// round costs 0.6 + 0.4 * (its fill) of a full one, since the fewer CUs run,
-// the higher their clock.  The largest tile within 3% of the cheapest wins
-// (e.g. 144 tiles of 256 x 256 rather than 288 of 256 x 128 at 3072^3, and
-// 128 x 128 for INT4 where 256 x 256 would leave a last round a quarter full).
-// When even the 64 x 64 tile leaves CUs idle (small M or N), a K-split tile
-// puts 4 waves on each of up to 4 times as many tiles.
+// time model chooses among the tiles that give at least three quarters of
+// the CUs one: the busiest CU sets the time, so a product of T tiles takes
+// T / 256 rounds, each of which costs the tile's area over its throughput.
+// A partial last round costs 0.6 + 0.4 * (its fill) of a full one, since the
+// fewer CUs run, the higher their clock.  The cheapest tile wins, the larger
+// one on a tie.  (E.g. 196 tiles of 256 x 256 rather than 392 of 256 x 128
+// at 3584^3, and 128 x 128 for INT4 at 6144^3, where 256 x 256 would leave a
+// last round a quarter full.)  When even the 64 x 64 tile leaves CUs idle
+// (small M or N), a K-split tile puts 4 waves on each of up to 4 times as
+// many tiles.
 int pick(int prec, int64_t M, int64_t N, int64_t K) {
     (void)K;
     auto tiles = [&](int c) { return cdiv(M, kConfigs[c].bm) * cdiv(N, kConfigs[c].bn); };
     if (tiles(2) >= 256) {
-        double cost[kNumConfigs];
-        double cheapest = 0;
+        int best = -1;
+        double best_cost = 0;
         for (int c : kPickOrder) {
             const int64_t t = tiles(c);
-            cost[c] = -1;
-            if (kTileRate[prec][c] == 0 || t < 128) continue;
+            if (kTileRate[prec][c] == 0 || t < 192) continue;
             const double partial = double(t % 256) / 256;
             const double rounds = double(t / 256) + (partial > 0 ? 0.6 + 0.4 * partial : 0.0);
-            cost[c] = rounds * kConfigs[c].bm * kConfigs[c].bn / kTileRate[prec][c];
-            if (cheapest == 0 || cost[c] < cheapest) cheapest = cost[c];
+            const double cost = rounds * kConfigs[c].bm * kConfigs[c].bn / kTileRate[prec][c];
+            if (best < 0 || cost < best_cost) {
+                best = c;
+                best_cost = cost;
+            }
         }
-        for (int c : kPickOrder)
-            if (cost[c] >= 0 && cost[c] <= 1.03 * cheapest) return c;
+        return best;   // the 64 x 64 tile is always a candidate here
     }
     // K split: 64 x 32 when more than 32 rows still fill the chip (each B
     // panel is then staged once rather than once per 32 rows), else 32 x 32
