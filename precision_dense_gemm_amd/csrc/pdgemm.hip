@@ -27,11 +27,11 @@
 //    256*a*b and the int32 sum is exactly 256*C (no overflow while
 //    16384*K < 2^31, K <= 131071).  The epilogue shifts right by 8 (exact).
 //  * Staging: buffer_load_dwordx4 ... lds, a direct global -> LDS copy in
-//    16-byte chunks.  With column-major B and no K split a stage holds 128
-//    bytes of K per row, so that every DMA instruction requests whole
-//    128-byte lines (the L2 returns whole lines: staging 64-byte pieces of
-//    them doubles the L2 -> CU traffic), two or three stages deep; the other
-//    variants stage 64 bytes per row, four stages deep.  The 16-byte chunks
+//    16-byte chunks.  Without a K split a stage holds 128 bytes of K per row
+//    (two K tiles), so that every DMA instruction requests whole 128-byte
+//    lines (the L2 returns whole lines: staging 64-byte pieces of them
+//    doubles the L2 -> CU traffic), two or three stages deep; the K-split
+//    tiles stage 64 bytes per row and wave, four stages deep.  The 16-byte chunks
 //    of each LDS row are
 //    XOR-swizzled by the row index so that fragment reads are free of bank
 //    conflicts (the paper pads shared rows for the same purpose; a swizzle
@@ -218,11 +218,12 @@ __device__ __forceinline__ int bswizzle(int r) {
 // flight), so after the barrier tile t+1 is complete in LDS and stage t is
 // free for tile t+kStages.
 //
-// Whole-line staging (LS > 0, column-major B, no K split): a stage holds two
-// K tiles, 128 bytes per row in eight 16-byte chunks, logical chunk c of row
-// r at position c ^ swizzle8(r); each DMA instruction of a wave writes 1 KB =
-// 8 whole rows, lane l landing in row l/8 at position l%8, so each
-// instruction reads whole 128-byte lines.  LS stages: stage s is fetched LS
+// Whole-line staging (LS > 0, no K split): a stage holds two K tiles, 128
+// bytes per row in eight 16-byte chunks, logical chunk c of row r at position
+// c ^ swizzle8(r); each DMA instruction of a wave writes 1 KB = 8 whole rows,
+// lane l landing in row l/8 at position l%8, so each instruction reads whole
+// 128-byte lines.  (A row-major B part holds the 2 * kKRows rows of B of the
+// two K tiles as in a 64-byte stage, each row of B a whole number of lines.)  LS stages: stage s is fetched LS
 // stages before it is consumed, four k-steps per stage, and the one barrier
 // of a stage comes after its last fragments are in registers, once this
 // wave's DMA of stage s+1 has landed (stages s+2 .. s+LS-1 stay in flight).
@@ -257,10 +258,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     static_assert(kStages == 4, "the main loop is unrolled for four stages");
     static_assert((kStages - 2) * kDma <= 63, "vmcnt holds at most 63 outstanding loads");
     // whole-line staging: 8 rows of 128 bytes per DMA instruction
-    constexpr bool kLine = LS > 0 && BR == kBCol && KS == 1;
+    constexpr bool kLine = LS > 0 && KS == 1;
     constexpr int kDmaL = kRows / 8 / NW;    // DMA instructions per wave per stage
     constexpr int kDmaLA = BM / 8 / NW;      // ... of which fill A rows
     static_assert(!kLine || (BM % (8 * NW) == 0 && BN % (8 * NW) == 0), "stage rows must split evenly over waves");
+    static_assert(!kLine || BR == kBCol || 2 * RB::kKRows * kCpr == 8 * BN, "row-major B part of a whole-line stage");
     static_assert(!kLine || (LS == 2 || LS == 3), "the whole-line loop is unrolled for two or three stages");
     static_assert(!kLine || (LS - 1) * kDmaL <= 63, "vmcnt holds at most 63 outstanding loads");
 
@@ -388,8 +390,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     const int tr_row = tr_i / RB::kQ;                 // row within a read
     const int tr_byte = 8 * (tr_i % RB::kQ);          // byte within the lane's chunks
     const int tr_col_bytes = (16 * ((lane >> 4) & 1)) * (P == kF16 ? 2 : 1) / (P == kI4 ? 2 : 1);
-    auto read_b_rowmajor = [&](const Stage &buf, int s, int j) __attribute__((always_inline)) {
-        const char *bpart = reinterpret_cast<const char *>(&buf[srow + BM][0]);
+    // (bpart: the B part of a stage; s: the k-step within it)
+    auto read_b_rm = [&](const char *bpart, int s, int j) __attribute__((always_inline)) {
         // bytes of K per k-step are 32: 16 f16, 32 int8 or 64 int4 rows, half per lane half
         constexpr int kStepRows = RB::kKRows / 2;
         const int col_bytes = ((wn0 + j * 32) * (P == kF16 ? 2 : 1) / (P == kI4 ? 2 : 1)) + tr_col_bytes + tr_byte;
@@ -415,6 +417,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
             }
         }
         return make_uint4(w[0], w[1], w[2], w[3]);
+    };
+    auto read_b_rowmajor = [&](const Stage &buf, int s, int j) __attribute__((always_inline)) {
+        return read_b_rm(reinterpret_cast<const char *>(&buf[srow + BM][0]), s, j);
     };
 
     auto read_frags = [&](const Stage &buf, int s, uint4 (&fa)[FM], uint4 (&fb)[FN]) __attribute__((always_inline)) {
@@ -574,24 +579,39 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
         const int n_st = (valid + kLineBytes - 1) / kLineBytes;   // stages of two K tiles
         // lane offsets: instruction j of this wave fills rows
         // (j*NW + wave)*8 .. +7; lane l fetches logical chunk
-        // (l%8) ^ swizzle8(row) of row (l/8), rows clamped as above
+        // (l%8) ^ swizzle8(row) of row (l/8), rows clamped as above.
+        // Row-major B: the B part of a stage holds the 2 * kKRows rows of B
+        // of its two K tiles as flat 16-byte chunks (as in a 64-byte stage),
+        // so lane l of a B instruction fills flat chunk f = l of its 1 KB.
         uint32_t voffl[kDmaL];
 #pragma unroll
         for (int j = 0; j < kDmaL; ++j) {
             const int cr = (j * NW + wave) * 8 + (lane >> 3);
             const int lchunk = (lane & 7) ^ swizzle8(cr);
-            if (j < kDmaLA)
+            if (j < kDmaLA) {
                 voffl[j] = (uint32_t)((min(m0 + cr, M - 1) - m0) * args.lda_bytes) + lchunk * 16;
-            else
+            } else if constexpr (BR == kBCol) {
                 voffl[j] = (uint32_t)((min(n0 + cr - BM, N - 1) - n0) * args.ldb_bytes) + lchunk * 16;
+            } else {
+                const int f = (j * NW + wave - BM / 8) * 64 + lane;
+                const int krow = f / kCpr;
+                const int gchunk = (f % kCpr) ^ bswizzle<P, BN>(krow);
+                voffl[j] = (uint32_t)(krow * args.ldb_bytes) + gchunk * 16;
+            }
         }
+        // row-major B: a stage spans 2 * kKRows rows of B
+        const int64_t b_stage_bytes = BR == kBRow ? (int64_t)2 * RB::kKRows * args.ldb_bytes : kLineBytes;
         auto stage_l = [&](int st, LStage &buf) __attribute__((always_inline)) {
             const int kb = st * kLineBytes;
             const bool live = st < n_st;
             const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)(a_base + kb), (short)0, live ? a_end - kb : 0, kRsrcWord3);
+            const int64_t bt = (int64_t)st * b_stage_bytes;
+            const int b_range = !live ? 0
+                                : BR == kBRow ? (int)min(min(b_end - bt, b_stage_bytes), (int64_t)INT32_MAX)
+                                              : (int)(b_end - bt);
             const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(b_base + kb), (short)0, live ? (int)(b_end - kb) : 0, kRsrcWord3);
+                (void *)(b_base + bt), (short)0, b_range, kRsrcWord3);
 #pragma unroll
             for (int j = 0; j < kDmaL; ++j)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kDmaLA ? ra : rb,
@@ -603,7 +623,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
 #pragma unroll
             for (int i = 0; i < FM; ++i) fa[i] = buf[wm0 + i * 32 + frow][ch];
 #pragma unroll
-            for (int j = 0; j < FN; ++j) fb[j] = buf[BM + wn0 + j * 32 + frow][ch];
+            for (int j = 0; j < FN; ++j) {
+                if constexpr (BR == kBCol)
+                    fb[j] = buf[BM + wn0 + j * 32 + frow][ch];
+                else
+                    fb[j] = read_b_rm(reinterpret_cast<const char *>(&buf[BM][0]), q, j);
+            }
         };
         // zero the bytes of k-step q of stage st at or beyond K
         auto mask_l = [&](int st, int q, uint4 (&fa)[FM], uint4 (&fb)[FN]) __attribute__((always_inline)) {
@@ -882,7 +907,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
 // ---------------------------------------------------------------------------
 // host side
 
-// ls: whole-line stages (column-major B; 0 = 64-byte stages throughout).
+// ls: whole-line stages (0 = 64-byte stages: the K-split tiles).
 // 256 x 256 fits two 64 KB stages; 128 x 128 keeps two so that two
 // workgroups share a CU; the others take three.
 struct Config {

@@ -198,3 +198,70 @@ def test_rowmajor_b_layout(prec, cfg):
                             k, n = element_at(lane_bytes[r][grp0 + src], p)
                             want_k = s * steprows + half * (steprows // 2) + r * per_read + e
                             assert (k, n) == (want_k, wn0 + jj * 32 + lane % 32), (prec, cfg, lane, r, e)
+
+
+LINE_CONFIGS = [(256, 256, 128, 128), (128, 128, 64, 64), (64, 64, 32, 32), (256, 128, 128, 64), (128, 64, 64, 32)]
+
+
+@pytest.mark.parametrize("prec", ["f16", "i8", "i4"])
+@pytest.mark.parametrize("cfg", LINE_CONFIGS, ids=["256", "128", "64", "256x128", "128x64"])
+def test_rowmajor_b_line_layout(prec, cfg):
+    # Whole-line stages hold two K tiles: the B part is 2 * krows rows of B.  DMA
+    # instruction j of wave w fills 1 KB block j*NW + w of the stage (lane l: chunk l of
+    # the block); blocks past the A part hold flat chunks f of the B part, row f // cpr,
+    # position f % cpr, fetching chunk position ^ bswizzle(row).  The transposing reads
+    # of k-steps 0..3 must find K-contiguous values of their own column, conflict-free.
+    BM, BN, WM, WN = cfg
+    krows, R, epc, bits = ROWB[prec]
+    Q = 16 // R
+    cpr = BN // epc
+    NW = (BM // WM) * (BN // WN)
+    rows = 2 * krows
+    blocks = (BM + BN) // 8
+    slot_src = {}
+    for wave in range(NW):
+        for j in range(blocks // NW):
+            b = j * NW + wave
+            if b < BM // 8:
+                continue
+            for lane in range(64):
+                f = (b - BM // 8) * 64 + lane
+                krow, pos = f // cpr, f % cpr
+                g = pos ^ bswizzle(prec, BN, krow)
+                assert 0 <= krow < rows and 0 <= g < cpr
+                slot_src[f] = (krow, g)
+    assert sorted(slot_src) == list(range(rows * cpr))
+    assert len(set(slot_src.values())) == rows * cpr
+
+    steprows = krows // 2
+    per_read = 64 // bits
+    for wave in range(NW):
+        wn0 = (wave % (BN // WN)) * WN
+        for s in range(4):
+            for jj in range(WN // 32):
+                lane_bytes = {}
+                for r in range(2):
+                    addrs = []
+                    for lane in range(64):
+                        i, grp, half = lane % 16, (lane >> 4) & 1, lane >> 5
+                        col_bytes = (wn0 + jj * 32) * bits // 8 + (16 * grp) * bits // 8 + 8 * (i % Q)
+                        krow = s * steprows + half * (steprows // 2) + r * R + i // Q
+                        pos = (col_bytes >> 4) ^ bswizzle(prec, BN, krow)
+                        addr = (krow * cpr + pos) * 16 + (col_bytes & 15)
+                        assert 0 <= addr and addr + 8 <= rows * cpr * 16
+                        addrs.append(addr)
+                    lane_bytes[r] = addrs
+                    for hw in (0, 32):
+                        banks = [(a // 4 + w) % 64 for a in addrs[hw:hw + 32] for w in (0, 1)]
+                        assert len(set(banks)) == 64, (prec, cfg, s, jj, r)
+                for lane in range(64):
+                    grp0 = lane - lane % 16
+                    i, half = lane % 16, lane >> 5
+                    for r in range(2):
+                        for e in range(per_read):
+                            src, p = tr_source(prec, i, e)
+                            f, inb = lane_bytes[r][grp0 + src] // 16, lane_bytes[r][grp0 + src] % 16
+                            krow, g = slot_src[f]
+                            k, n = krow, (g * 16 + inb) * 8 // bits + p
+                            want_k = s * steprows + half * (steprows // 2) + r * per_read + e
+                            assert (k, n) == (want_k, wn0 + jj * 32 + lane % 32), (prec, cfg, lane, r, e)
