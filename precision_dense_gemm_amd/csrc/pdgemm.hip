@@ -909,7 +909,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
 
 // ls: whole-line stages (0 = 64-byte stages: the K-split tiles).
 // 256 x 256 fits two 64 KB stages; 128 x 128 keeps two so that two
-// workgroups share a CU; the others take three.
+// workgroups share a CU, except in 7, which takes three for products of at
+// most one tile per CU (where a CU holds one workgroup anyway); the others
+// take three.
 struct Config {
     int bm, bn, wm, wn, gm, ks, ls;
 };
@@ -922,6 +924,7 @@ constexpr Config kConfigs[] = {
     {256, 128, 128, 64, 4, 1, 3},   // 4: between 0 and 1 (e.g. M = 1024 of a wide product)
     {128, 64, 64, 32, 8, 1, 3},     // 5: between 1 and 2 (e.g. M = 256)
     {64, 32, 64, 32, 8, 4, 0},      // 6: K split over 4 waves, 64 rows (e.g. M = 64 of a wide product)
+    {128, 128, 64, 64, 8, 1, 3},    // 7: 1 with three stages, for at most one round of tiles
 };
 
 // Tiles without K split, largest first: the order in which pick() tries them.
@@ -944,6 +947,7 @@ const void *kernel_ptr(int cfg) {
     case 4: return kernel_for<P, 4, E, BR>();
     case 5: return kernel_for<P, 5, E, BR>();
     case 6: return kernel_for<P, 6, E, BR>();
+    case 7: return kernel_for<P, 7, E, BR>();
     default: return nullptr;
     }
 }
@@ -1008,7 +1012,7 @@ constexpr int kTileRate[3][kNumConfigs] = {
 // at 3584^3, and 128 x 128 for INT4 at 6144^3, where 256 x 256 would leave a
 // last round a quarter full.)  When even the 64 x 64 tile leaves CUs idle
 // (small M or N), a K-split tile puts 4 waves on each of up to 4 times as
-// many tiles.
+// many tiles.  128 x 128 with at most one tile per CU takes configuration 7.
 int pick(int prec, int64_t M, int64_t N, int64_t K) {
     (void)K;
     auto tiles = [&](int c) { return cdiv(M, kConfigs[c].bm) * cdiv(N, kConfigs[c].bn); };
@@ -1026,7 +1030,9 @@ int pick(int prec, int64_t M, int64_t N, int64_t K) {
                 best_cost = cost;
             }
         }
-        return best;   // the 64 x 64 tile is always a candidate here
+        // the 64 x 64 tile is always a candidate here.  At most one 128 x 128
+        // tile per CU: the three-stage variant (7), as a CU holds one anyway
+        return best == 1 && tiles(1) <= 256 ? 7 : best;
     }
     // K split: 64 x 32 when more than 32 rows still fill the chip (each B
     // panel is then staged once rather than once per 32 rows), else 32 x 32

@@ -308,6 +308,9 @@ def test_pick_weighs_the_last_partial_round(lib):
         assert tile(prec, 8192, 3072, 8192) == (256, 128)     # 384 tiles of 256 x 256: 1.5 rounds
     for n in (4096, 6144, 8192):
         assert tile(2, n, n, n) == (128, 128)                 # INT4: two workgroups per CU
+    # 128 x 128 at one tile per CU takes its three-stage variant; with more tiles, two stages
+    three_stage = lib.pdgemm_pick_config(0, 2048, 2048, 2048)
+    assert info[three_stage] == (128, 128) and three_stage != lib.pdgemm_pick_config(2, 4096, 4096, 4096)
     # whenever the 64 x 64 tile fills the chip, the pick gives at least three quarters of the CUs a tile
     for prec in range(3):
         for m in range(512, 12289, 448):
