@@ -29,7 +29,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-import torch
+# torch first: in a process that opened a HIP library before importing torch,
+# torch's later device set-up failed (every GPU call returned hipErrorNoDevice)
+import torch  # noqa: E402
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_HERE, "libpdgemm.so")

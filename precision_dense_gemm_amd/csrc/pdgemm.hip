@@ -257,8 +257,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(kStages == 4, "the main loop is unrolled for four stages");
     static_assert((kStages - 2) * kDma <= 63, "vmcnt holds at most 63 outstanding loads");
-    // whole-line staging: 8 rows of 128 bytes per DMA instruction
+    // whole-line staging: 8 rows of 128 bytes per DMA instruction.  Every
+    // tile without K split stages whole lines; 64-byte stages serve the
+    // K-split tiles, whose waves each stage their own 64-byte slices.
     constexpr bool kLine = LS > 0 && KS == 1;
+    static_assert(KS > 1 || LS > 0, "tiles without K split stage whole lines");
     constexpr int kDmaL = kRows / 8 / NW;    // DMA instructions per wave per stage
     constexpr int kDmaLA = BM / 8 / NW;      // ... of which fill A rows
     static_assert(!kLine || (BM % (8 * NW) == 0 && BN % (8 * NW) == 0), "stage rows must split evenly over waves");
