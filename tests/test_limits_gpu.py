@@ -1,0 +1,135 @@
+"""GPU cases at the limits the header states.
+
+* The largest K whose int32 sums cannot overflow: INT8 K = 131071 and INT4
+  K = 131070 (the largest even K; the INT4 planes sum 256 * a * b, so the
+  scaled sum of all -8 products, 16384 * 131070, sits just below 2^31).
+  Checked against the closed forms at the extreme values, on the plain, the
+  K-split and the row-major-B kernels; FP16 with all-ones operands at
+  K = 131072 (every partial sum an integer below 2^24, so C = K exactly).
+* The largest leading dimensions: rows of 4 MiB for A, B and C, so that a
+  256-row tile spans 1 GiB of offsets, checked against the oracle on ragged
+  M, N and K.
+
+Operands' padding past K holds poison, and every case prints its name before
+it touches the GPU.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_util as gu
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+MAX_ROW_BYTES = 1 << 22
+
+
+@pytest.fixture(scope="module")
+def pd():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import precision_dense_gemm_amd as pd
+    return pd
+
+
+@pytest.fixture(scope="module")
+def dev(pd):
+    return torch.device("cuda:0")
+
+
+def filled(rows, ld, cols, value, poison, dtype, dev):
+    """(rows, ld) device buffer: `value` in the first `cols` columns, `poison` after."""
+    t = torch.full((rows, ld), poison, dtype=dtype, device=dev)
+    t[:, :cols] = value
+    return t[:, :cols]
+
+
+# (M, N): the K-split 32 x 32 tile at M = 16, the plain tiles at M = 130
+SHAPES = [(16, 96), (130, 96)]
+
+
+@pytest.mark.parametrize("M,N", SHAPES)
+@pytest.mark.parametrize("b_value,expect", [(-128, 16384), (127, -16256)])
+def test_int8_largest_k(pd, dev, M, N, b_value, expect):
+    K, ld = 131071, 131072
+    gu.note(f"[case] i8 largest K={K} M={M} N={N} b={b_value}")
+    A = filled(M, ld, K, -128, 127, torch.int8, dev)
+    Bt = filled(N, ld, K, b_value, 127, torch.int8, dev)
+    C = pd.gemm_i8(A, Bt)
+    B = filled(K, N + 16, N, b_value, 127, torch.int8, dev)   # the same B, row-major
+    Cr = pd.gemm_i8_rowb(A, B)
+    torch.cuda.synchronize()
+    assert expect * K < 2 ** 31
+    assert torch.all(C == expect * K) and torch.all(Cr == expect * K)
+
+
+@pytest.mark.parametrize("M,N", SHAPES)
+@pytest.mark.parametrize("b_byte,expect", [(0x88, 64), (0x77, -56)])
+def test_int4_largest_k(pd, dev, M, N, b_byte, expect):
+    K, ld_bytes = 131070, 65536          # K / 2 = 65535 bytes of data per row
+    gu.note(f"[case] i4 largest K={K} M={M} N={N} b=0x{b_byte:02x}")
+    A = filled(M, ld_bytes, K // 2, 0x88, 0x77, torch.uint8, dev)     # all -8
+    Bt = filled(N, ld_bytes, K // 2, b_byte, 0x77, torch.uint8, dev)
+    C = pd.gemm_i4(A, Bt, K)
+    B = filled(K, N // 2 + 16, N // 2, b_byte, 0x77, torch.uint8, dev)   # row-major, packed along N
+    Cr = pd.gemm_i4_rowb(A, B, K, N)
+    torch.cuda.synchronize()
+    assert 16384 * K < 2 ** 31   # the scaled sum of the all -8 case
+    assert torch.all(C == expect * K) and torch.all(Cr == expect * K)
+
+
+@pytest.mark.parametrize("M,N", SHAPES)
+def test_f16_long_k_ones(pd, dev, M, N):
+    K = 131072
+    gu.note(f"[case] f16 ones K={K} M={M} N={N}")
+    A = filled(M, K + 64, K, 1.0, float("nan"), torch.float16, dev)
+    Bt = filled(N, K + 64, K, 1.0, float("nan"), torch.float16, dev)
+    C = pd.gemm_f16(A, Bt)
+    torch.cuda.synchronize()
+    assert torch.all(C == K)
+
+
+LD = {"f16": MAX_ROW_BYTES // 2, "i8": MAX_ROW_BYTES, "i4": MAX_ROW_BYTES * 2}   # in elements
+
+
+@pytest.mark.parametrize("prec", ["f16", "i8", "i4"])
+@pytest.mark.parametrize("cfg", [0, 3])
+def test_largest_leading_dimensions(pd, dev, prec, cfg):
+    # 256 x 256 tiles (configuration 0) and the K-split 32 x 32 tiles (3), with rows of
+    # A, B and C of 4 MiB; M, N and K ragged
+    M, N, K = 250, 70, 200
+    ld = LD[prec]
+    ldc = MAX_ROW_BYTES // 4
+    gu.note(f"[case] largest ld {prec} cfg={cfg} lda=ldb={ld} ldc={ldc}")
+    A, Bt = synth.operands(prec, M, N, K, 77, 78)
+    cols = K // 2 if prec == "i4" else K
+    ld_cols = ld // 2 if prec == "i4" else ld
+    dt = {"f16": torch.float16, "i8": torch.int8, "i4": torch.uint8}[prec]
+    poison = {"f16": float("nan"), "i8": 127, "i4": 0x77}[prec]
+    Ad = torch.full((M, ld_cols), poison, dtype=dt, device=dev)
+    Ad[:, :cols] = torch.from_numpy(A).to(dev)
+    Bd = torch.full((N, ld_cols), poison, dtype=dt, device=dev)
+    Bd[:, :cols] = torch.from_numpy(Bt).to(dev)
+    out_dtype = torch.float32 if prec == "f16" else torch.int32
+    Cbuf = torch.zeros((M, ldc), dtype=out_dtype, device=dev)
+    out = Cbuf[:, :N]
+    if prec == "f16":
+        pd.gemm_f16(Ad[:, :cols], Bd[:, :cols], out=out, cfg=cfg)
+    elif prec == "i8":
+        pd.gemm_i8(Ad[:, :cols], Bd[:, :cols], out=out, cfg=cfg)
+    else:
+        pd.gemm_i4(Ad[:, :cols], Bd[:, :cols], K, out=out, cfg=cfg)
+    torch.cuda.synchronize()
+    C = out.cpu().numpy()
+    assert torch.count_nonzero(Cbuf[:, N:]) == 0, "stores past column N"
+    del Ad, Bd, Cbuf
+    if prec == "f16":
+        R, S = oracle.gemm_f16(A, Bt)
+        gu.assert_f16_close(C, R, S, f"largest ld {prec} cfg{cfg}")
+    else:
+        ref = oracle.gemm_i8(A, Bt) if prec == "i8" else oracle.gemm_i4(A, Bt, K)
+        gu.assert_int_equal(C, ref, f"largest ld {prec} cfg{cfg}")
