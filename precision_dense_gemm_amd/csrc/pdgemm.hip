@@ -914,17 +914,19 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
 // 256 x 256 fits two 64 KB stages; 128 x 128 keeps two so that two
 // workgroups share a CU, except in 7, which takes three for products of at
 // most one tile per CU (where a CU holds one workgroup anyway); the others
-// take three.
+// take three.  The 256-row tiles run 8 waves, two per SIMD, so that one
+// wave's fragment reads, INT4 unpacking and barrier wait overlap the other's
+// MFMAs (their accumulators then live in VGPRs); 128 x 128 ran slower so.
 struct Config {
     int bm, bn, wm, wn, gm, ks, ls;
 };
 
 constexpr Config kConfigs[] = {
-    {256, 256, 128, 128, 4, 1, 2},  // 0: large shapes
+    {256, 256, 128, 64, 4, 1, 2},   // 0: large shapes (8 waves)
     {128, 128, 64, 64, 8, 1, 2},    // 1: medium
     {64, 64, 32, 32, 8, 1, 3},      // 2: small
     {32, 32, 32, 32, 8, 4, 0},      // 3: few tiles (small M or N): K split over 4 waves
-    {256, 128, 128, 64, 4, 1, 3},   // 4: between 0 and 1 (e.g. M = 1024 of a wide product)
+    {256, 128, 64, 64, 4, 1, 3},    // 4: between 0 and 1 (e.g. M = 1024 of a wide product; 8 waves)
     {128, 64, 64, 32, 8, 1, 3},     // 5: between 1 and 2 (e.g. M = 256)
     {64, 32, 64, 32, 8, 4, 0},      // 6: K split over 4 waves, 64 rows (e.g. M = 64 of a wide product)
     {128, 128, 64, 64, 8, 1, 3},    // 7: 1 with three stages, for at most one round of tiles
@@ -997,12 +999,11 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // (INT8, INT4): the median of five alternated back-to-back timings on a
 // product that gives every one of them whole rounds of workgroups
 // (M = K = 8192, N = 6144); only the ratios within a row matter.  0 = not a
-// candidate (the K-split tiles).  INT4 runs fastest on 128 x 128: two
-// workgroups per CU hide its in-register unpack.
+// candidate (the K-split tiles, and 7, which stands in for 1).
 constexpr int kTileRate[3][kNumConfigs] = {
-    {1261, 1098, 695, 0, 1158, 862, 0},    // FP16
-    {2440, 2172, 1402, 0, 2194, 1728, 0},  // INT8
-    {2415, 2569, 1893, 0, 2376, 2033, 0},  // INT4
+    {1299, 1113, 686, 0, 1189, 855, 0, 0},    // FP16
+    {2541, 2178, 1374, 0, 2293, 1669, 0, 0},  // INT8
+    {2789, 2563, 1868, 0, 2610, 2033, 0, 0},  // INT4
 };
 
 // When the 64 x 64 tile fills the chip (at least one workgroup per CU), a

@@ -283,8 +283,8 @@ def test_pick_prefers_large_tiles_that_fill_the_chip(lib):
     for m, n in ((1024, 8192), (256, 8192), (16, 8192), (8192, 8192), (512, 512)):
         bm, bn = tile(m, n)[0]
         assert -(-m // bm) * -(-n // bn) >= 256
-    # INT4 takes 128 x 128 rather than 256 x 128
-    assert info[lib.pdgemm_pick_config(2, 1024, 8192, 8192)][:2] == (128, 128)
+    # INT4 too takes 256 x 128 here (with 8 waves it overlaps its unpack with the MFMAs)
+    assert info[lib.pdgemm_pick_config(2, 1024, 8192, 8192)][:2] == (256, 128)
 
 
 def test_pick_weighs_the_last_partial_round(lib):
@@ -299,18 +299,19 @@ def test_pick_weighs_the_last_partial_round(lib):
         info[cfg] = tuple(v.value for v in vals)[:2]
     def tile(prec, m, n, k):
         return info[lib.pdgemm_pick_config(prec, m, n, k)]
-    for prec in (0, 1):
+    for prec in range(3):
         assert tile(prec, 3584, 3584, 3584) == (256, 256)     # 196 tiles, not 392 of 256 x 128
         assert tile(prec, 1792, 8192, 8192) == (256, 256)     # 224 tiles
         assert tile(prec, 8192, 8192, 8192) == (256, 256)
         assert tile(prec, 12288, 4096, 4096) == (256, 256)
-        assert tile(prec, 6144, 6144, 6144) == (128, 128)     # 576 tiles of 256 x 256: 2.25 rounds
         assert tile(prec, 8192, 3072, 8192) == (256, 128)     # 384 tiles of 256 x 256: 1.5 rounds
-    for n in (4096, 6144, 8192):
+        assert tile(prec, 1024, 8192, 8192) == (256, 128)
+    assert tile(0, 6144, 6144, 6144) == (256, 128)            # 576 tiles of 256 x 256: 2.25 rounds
+    for n in (5120, 6144, 7168):
         assert tile(2, n, n, n) == (128, 128)                 # INT4: two workgroups per CU
     # 128 x 128 at one tile per CU takes its three-stage variant; with more tiles, two stages
     three_stage = lib.pdgemm_pick_config(0, 2048, 2048, 2048)
-    assert info[three_stage] == (128, 128) and three_stage != lib.pdgemm_pick_config(2, 4096, 4096, 4096)
+    assert info[three_stage] == (128, 128) and three_stage != lib.pdgemm_pick_config(2, 6144, 6144, 6144)
     # whenever the 64 x 64 tile fills the chip, the pick gives at least three quarters of the CUs a tile
     for prec in range(3):
         for m in range(512, 12289, 448):
