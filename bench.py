@@ -156,15 +156,27 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_n8192_hbm_counters.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "precision_dense_gemm_amd", "csrc", "pdgemm.hip")
 
 
+def code_text(text):
+    """C++ text without its // comments, indentation and blank lines (the kernel source
+    holds no // inside string literals), so that a comment edit keeps the hash."""
+    out = []
+    for line in text.split("\n"):
+        code = line.split("//", 1)[0].strip()
+        if code:
+            out.append(" ".join(code.split()))
+    return "\n".join(out)
+
+
 def kernel_source_sha(source=KERNEL_SOURCE):
-    """sha256 of what decides the code a launch runs: the device part of the kernel source
-    (everything before its host-side section) and the host's tile table, instantiation and
-    tile choice (from the Config struct to the argument checks)."""
+    """sha256 of what decides the code a launch runs: the code (comments aside) of the
+    device part of the kernel source (everything before its host-side section) and of the
+    host's tile table, instantiation and tile choice (from the Config struct to the
+    argument checks)."""
     import hashlib
     text = open(source, encoding="utf-8").read()
     device = text[:text.index("// host side")]
     tiles = text[text.index("struct Config {"):text.index("int validate(")]
-    return hashlib.sha256((device + tiles).encode()).hexdigest()
+    return hashlib.sha256(code_text(device + "\n" + tiles).encode()).hexdigest()
 
 
 def measured_traffic(path=TRAFFIC_FILE, source=KERNEL_SOURCE):

@@ -42,8 +42,8 @@
 //    staged as K rows of the tile and read with gfx950's transposing LDS reads
 //    (ds_read_b64_tr_b16 / _b8 / _b4), which hand each lane K-contiguous
 //    values of its own column: the same fragments, no transposition pass.
-//  * Tiles: a workgroup of 4 waves computes a BM x BN block of C, each wave a
-//    WM x WN sub-block made of (WM/32) x (WN/32) MFMA tiles held in
+//  * Tiles: a workgroup of 4 or 8 waves computes a BM x BN block of C, each
+//    wave a WM x WN sub-block made of (WM/32) x (WN/32) MFMA tiles held in
 //    accumulator registers for the whole K loop.
 //  * Scheduling over 8 XCDs: workgroups are dispatched round-robin over the
 //    XCDs, so the block id is remapped to give each XCD a contiguous range of

@@ -17,6 +17,17 @@ def test_traffic_summary_matches_current_kernel_or_is_ignored(tmp_path):
     assert bench.measured_traffic(str(fake)) == {}
 
 
+def test_source_hash_ignores_comments_not_code(tmp_path):
+    src = ("__device__ int f(int x) { return x + 1; }  // one\n"
+           "// host side\nstruct Config {\n  int a;  // field\n};\nint validate(")
+    a, b, c = (tmp_path / n for n in ("a.hip", "b.hip", "c.hip"))
+    a.write_text(src)
+    b.write_text(src.replace("// one", "// another comment").replace("  int a;", "\n    int a;\n"))
+    c.write_text(src.replace("x + 1", "x + 2"))
+    ha, hb, hc = (bench.kernel_source_sha(str(p)) for p in (a, b, c))
+    assert ha == hb and ha != hc
+
+
 def test_multi_gpu_request_is_refused():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
