@@ -27,11 +27,11 @@
 //    256*a*b and the int32 sum is exactly 256*C (no overflow while
 //    16384*K < 2^31, K <= 131071).  The epilogue shifts right by 8 (exact).
 //  * Staging: buffer_load_dwordx4 ... lds, a direct global -> LDS copy in
-//    16-byte chunks.  Without a K split a stage holds 128 bytes of K per row
-//    (two K tiles), so that every DMA instruction requests whole 128-byte
-//    lines (the L2 returns whole lines: staging 64-byte pieces of them
-//    doubles the L2 -> CU traffic), two or three stages deep; the K-split
-//    tiles stage 64 bytes per row and wave, four stages deep.  The 16-byte chunks
+//    16-byte chunks.  A stage holds 128 bytes of K per row (per wave, with a
+//    K split), so that every DMA instruction requests whole 128-byte lines
+//    (the L2 returns whole lines: staging 64-byte pieces of them doubles the
+//    L2 -> CU traffic), two or three stages deep; the 32 x 32 K-split tile
+//    stages 64 bytes per row and wave, four stages deep.  The 16-byte chunks
 //    of each LDS row are
 //    XOR-swizzled by the row index so that fragment reads are free of bank
 //    conflicts (the paper pads shared rows for the same purpose; a swizzle
@@ -218,11 +218,11 @@ __device__ __forceinline__ int bswizzle(int r) {
 // flight), so after the barrier tile t+1 is complete in LDS and stage t is
 // free for tile t+kStages.
 //
-// Whole-line staging (LS > 0, no K split): a stage holds two K tiles, 128
-// bytes per row in eight 16-byte chunks, logical chunk c of row r at position
-// c ^ swizzle8(r); each DMA instruction of a wave writes 1 KB = 8 whole rows,
-// lane l landing in row l/8 at position l%8, so each instruction reads whole
-// 128-byte lines.  (A row-major B part holds the 2 * kKRows rows of B of the
+// Whole-line staging (LS > 0): a stage holds two K tiles, 128 bytes per row
+// (with a K split: per row of each wave's slice) in eight 16-byte chunks,
+// logical chunk c of row r at position c ^ swizzle8(r); each DMA instruction
+// of a wave writes 1 KB = 8 whole rows, lane l landing in row l/8 at
+// position l%8, so each instruction reads whole 128-byte lines.  (A row-major B part holds the 2 * kKRows rows of B of the
 // two K tiles as in a 64-byte stage, each row of B a whole number of lines.)  LS stages: stage s is fetched LS
 // stages before it is consumed, four k-steps per stage, and the one barrier
 // of a stage comes after its last fragments are in registers, once this
@@ -257,14 +257,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(kStages == 4, "the main loop is unrolled for four stages");
     static_assert((kStages - 2) * kDma <= 63, "vmcnt holds at most 63 outstanding loads");
-    // whole-line staging: 8 rows of 128 bytes per DMA instruction.  Every
-    // tile without K split stages whole lines; 64-byte stages serve the
-    // K-split tiles, whose waves each stage their own 64-byte slices.
-    constexpr bool kLine = LS > 0 && KS == 1;
-    static_assert(KS > 1 || LS > 0, "tiles without K split stage whole lines");
-    constexpr int kDmaL = kRows / 8 / NW;    // DMA instructions per wave per stage
-    constexpr int kDmaLA = BM / 8 / NW;      // ... of which fill A rows
-    static_assert(!kLine || (BM % (8 * NW) == 0 && BN % (8 * NW) == 0), "stage rows must split evenly over waves");
+    // whole-line staging: 8 rows of 128 bytes per DMA instruction (with a K
+    // split, each wave stages its own 128-byte slice of every row)
+    constexpr bool kLine = LS > 0;
+    constexpr int kDmaL = KS > 1 ? kSub / 8 : kRows / 8 / NW;   // DMA instructions per wave per stage
+    constexpr int kDmaLA = KS > 1 ? BM / 8 : BM / 8 / NW;       // ... of which fill A rows
+    static_assert(!kLine || (KS > 1 ? BM % 8 == 0 && BN % 8 == 0 : BM % (8 * NW) == 0 && BN % (8 * NW) == 0),
+                  "stage rows must split evenly over waves");
     static_assert(!kLine || BR == kBCol || 2 * RB::kKRows * kCpr == 8 * BN, "row-major B part of a whole-line stage");
     static_assert(!kLine || (LS == 2 || LS == 3), "the whole-line loop is unrolled for two or three stages");
     static_assert(!kLine || (LS - 1) * kDmaL <= 63, "vmcnt holds at most 63 outstanding loads");
@@ -578,34 +577,38 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
 
     if constexpr (kLine) {
         // ---- whole-line staging ----
-        constexpr int kLineBytes = 2 * kRowBytes;
-        const int n_st = (valid + kLineBytes - 1) / kLineBytes;   // stages of two K tiles
-        // lane offsets: instruction j of this wave fills rows
-        // (j*NW + wave)*8 .. +7; lane l fetches logical chunk
-        // (l%8) ^ swizzle8(row) of row (l/8), rows clamped as above.
-        // Row-major B: the B part of a stage holds the 2 * kKRows rows of B
-        // of its two K tiles as flat 16-byte chunks (as in a 64-byte stage),
-        // so lane l of a B instruction fills flat chunk f = l of its 1 KB.
+        constexpr int kLineBytes = 2 * kRowBytes;         // bytes of K per row and wave slice
+        constexpr int kStageK = KS * kLineBytes;           // bytes of K per row per stage
+        const int n_st = (valid + kStageK - 1) / kStageK;  // stages of two K tiles
+        // lane offsets: instruction j of this wave fills stage rows
+        // (j*NW + wave)*8 .. +7 (K split: rows j*8 .. +7 of its own slice);
+        // lane l fetches logical chunk (l%8) ^ swizzle8(row) of row (l/8),
+        // rows clamped as above.  Row-major B: the B part of a stage (of a
+        // slice) holds the 2 * kKRows rows of B of its two K tiles as flat
+        // 16-byte chunks (as in a 64-byte stage), so lane l of a B
+        // instruction fills flat chunk f = l of its 1 KB.
+        const int kofs = slice * kLineBytes;               // this wave's bytes of a stage's K
         uint32_t voffl[kDmaL];
 #pragma unroll
         for (int j = 0; j < kDmaL; ++j) {
-            const int cr = (j * NW + wave) * 8 + (lane >> 3);
+            const int blk = KS > 1 ? j : j * NW + wave;    // 1 KB block of the stage (slice)
+            const int cr = blk * 8 + (lane >> 3);
             const int lchunk = (lane & 7) ^ swizzle8(cr);
             if (j < kDmaLA) {
-                voffl[j] = (uint32_t)((min(m0 + cr, M - 1) - m0) * args.lda_bytes) + lchunk * 16;
+                voffl[j] = (uint32_t)((min(m0 + cr, M - 1) - m0) * args.lda_bytes) + lchunk * 16 + kofs;
             } else if constexpr (BR == kBCol) {
-                voffl[j] = (uint32_t)((min(n0 + cr - BM, N - 1) - n0) * args.ldb_bytes) + lchunk * 16;
+                voffl[j] = (uint32_t)((min(n0 + cr - BM, N - 1) - n0) * args.ldb_bytes) + lchunk * 16 + kofs;
             } else {
-                const int f = (j * NW + wave - BM / 8) * 64 + lane;
+                const int f = (blk - BM / 8) * 64 + lane;
                 const int krow = f / kCpr;
                 const int gchunk = (f % kCpr) ^ bswizzle<P, BN>(krow);
-                voffl[j] = (uint32_t)(krow * args.ldb_bytes) + gchunk * 16;
+                voffl[j] = (uint32_t)((slice * 2 * RB::kKRows + krow) * args.ldb_bytes) + gchunk * 16;
             }
         }
-        // row-major B: a stage spans 2 * kKRows rows of B
-        const int64_t b_stage_bytes = BR == kBRow ? (int64_t)2 * RB::kKRows * args.ldb_bytes : kLineBytes;
+        // row-major B: a stage spans KS * 2 * kKRows rows of B
+        const int64_t b_stage_bytes = BR == kBRow ? (int64_t)KS * 2 * RB::kKRows * args.ldb_bytes : kStageK;
         auto stage_l = [&](int st, LStage &buf) __attribute__((always_inline)) {
-            const int kb = st * kLineBytes;
+            const int kb = st * kStageK;
             const bool live = st < n_st;
             const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)(a_base + kb), (short)0, live ? a_end - kb : 0, kRsrcWord3);
@@ -618,24 +621,25 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
 #pragma unroll
             for (int j = 0; j < kDmaL; ++j)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kDmaLA ? ra : rb,
-                                                         LDS_PTR(&buf[(j * NW + wave) * 8][0]), 16, voffl[j], 0, 0, 0);
+                                                         LDS_PTR(&buf[KS > 1 ? srow + j * 8 : (j * NW + wave) * 8][0]),
+                                                         16, voffl[j], 0, 0, 0);
         };
         // fragments of k-step q (0..3) of a stage: logical chunk 2q + half
         auto read_l = [&](const LStage &buf, int q, uint4 (&fa)[FM], uint4 (&fb)[FN]) __attribute__((always_inline)) {
             const int ch = (2 * q + fhalf) ^ swizzle8(frow);   // fragment rows start at multiples of 32
 #pragma unroll
-            for (int i = 0; i < FM; ++i) fa[i] = buf[wm0 + i * 32 + frow][ch];
+            for (int i = 0; i < FM; ++i) fa[i] = buf[srow + wm0 + i * 32 + frow][ch];
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 if constexpr (BR == kBCol)
-                    fb[j] = buf[BM + wn0 + j * 32 + frow][ch];
+                    fb[j] = buf[srow + BM + wn0 + j * 32 + frow][ch];
                 else
-                    fb[j] = read_b_rm(reinterpret_cast<const char *>(&buf[BM][0]), q, j);
+                    fb[j] = read_b_rm(reinterpret_cast<const char *>(&buf[srow + BM][0]), q, j);
             }
         };
         // zero the bytes of k-step q of stage st at or beyond K
         auto mask_l = [&](int st, int q, uint4 (&fa)[FM], uint4 (&fb)[FN]) __attribute__((always_inline)) {
-            const int nb = valid - (st * kLineBytes + (2 * q + fhalf) * 16);
+            const int nb = valid - (st * kStageK + kofs + (2 * q + fhalf) * 16);
             uint32_t m[4];
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
@@ -672,7 +676,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
             interleave(NoDma{});
             // this wave's DMA of stage st+1 has landed and its reads of `cur`
             // are done; after the barrier the same holds for every wave
-            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((LS - 2) * kDmaL) : "memory");
+            // (K split: every wave reads only its own slice)
+            if constexpr (KS > 1)
+                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((LS - 2) * kDmaL) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((LS - 2) * kDmaL) : "memory");
             stage_l(st + LS, cur);
             read_l(nxt, 0, fa0, fb0);
             mma(fa1, fb1);
@@ -700,7 +708,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
 #pragma unroll
             for (int x = 0; x < kScaleLoads; ++x)
                 if (tid + x * kThreads < BM + BN) lds_scale[tid + x * kThreads] = scale_v[x];
-            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((LS - 1) * kDmaL) : "memory");
+            if constexpr (KS > 1)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"((LS - 1) * kDmaL) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((LS - 1) * kDmaL) : "memory");
             read_l(ln0, 0, fa0, fb0);
             int st = 0;
             if constexpr (LS == 2) {
@@ -786,8 +797,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     if constexpr (KS > 1) {
         using Sc = typename Prec<P>::Out;    // the sums (int32 or fp32)
         constexpr int kPer = 16 / KS;
-        static_assert(sizeof(lds0) >= KS * 16 * kWave * sizeof(Sc), "partials of a block fit in one stage");
-        Sc *const part = reinterpret_cast<Sc *>(&lds0[0][0]);
+        constexpr size_t kStage0Bytes = kLine ? sizeof(ln0) : sizeof(lds0);
+        static_assert(kStage0Bytes >= KS * 16 * kWave * sizeof(Sc), "partials of a block fit in one stage");
+        Sc *const part = kLine ? reinterpret_cast<Sc *>(&ln0[0][0]) : reinterpret_cast<Sc *>(&lds0[0][0]);
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -910,7 +922,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
 // ---------------------------------------------------------------------------
 // host side
 
-// ls: whole-line stages (0 = 64-byte stages: the K-split tiles).
+// ls: whole-line stages, or 0 for four 64-byte stages.  Only the 32 x 32
+// K-split tile keeps 64-byte stages: at M = 16 and 512^3, where it runs, whole
+// lines were no faster (their 4-wave 512-byte K tiles make few, deep stages),
+// while the 64 x 32 K-split tile gained 10-18% from them (FP16 and INT8).
 // 256 x 256 fits two 64 KB stages; 128 x 128 keeps two so that two
 // workgroups share a CU, except in 7, which takes three for products of at
 // most one tile per CU (where a CU holds one workgroup anyway); the others
@@ -928,7 +943,7 @@ constexpr Config kConfigs[] = {
     {32, 32, 32, 32, 8, 4, 0},      // 3: few tiles (small M or N): K split over 4 waves
     {256, 128, 64, 64, 4, 1, 3},    // 4: between 0 and 1 (e.g. M = 1024 of a wide product; 8 waves)
     {128, 64, 64, 32, 8, 1, 3},     // 5: between 1 and 2 (e.g. M = 256)
-    {64, 32, 64, 32, 8, 4, 0},      // 6: K split over 4 waves, 64 rows (e.g. M = 64 of a wide product)
+    {64, 32, 64, 32, 8, 4, 3},      // 6: K split over 4 waves, 64 rows (e.g. M = 64 of a wide product)
     {128, 128, 64, 64, 8, 1, 3},    // 7: 1 with three stages, for at most one round of tiles
 };
 

@@ -52,7 +52,8 @@ def test_line_fragment_reads_are_bank_conflict_free():
                 assert len({c ^ swizzle8(r) for r in rows[o:o + 8]}) == 8
 
 
-@pytest.mark.parametrize("bm,bn,waves", [(256, 256, 4), (128, 128, 4), (64, 64, 4), (256, 128, 4), (128, 64, 4)])
+@pytest.mark.parametrize("bm,bn,waves", [(256, 256, 8), (128, 128, 4), (64, 64, 4), (256, 128, 8), (128, 64, 4),
+                                         (32, 32, 1), (64, 32, 1)])
 def test_line_dma_fills_every_row_once(bm, bn, waves):
     # instruction j of wave w writes LDS rows (j*waves + w)*8 .. +7, lane l to row l/8 at
     # position l%8, fetching logical chunk (l%8) ^ swizzle8(row) of that row: every
@@ -200,11 +201,14 @@ def test_rowmajor_b_layout(prec, cfg):
                             assert (k, n) == (want_k, wn0 + jj * 32 + lane % 32), (prec, cfg, lane, r, e)
 
 
-LINE_CONFIGS = [(256, 256, 128, 128), (128, 128, 64, 64), (64, 64, 32, 32), (256, 128, 128, 64), (128, 64, 64, 32)]
+# the tiles without K split (4 or 8 waves), and one K slice of the K-split tiles (a slice is
+# staged and read by one wave, as a one-wave tile)
+LINE_CONFIGS = [(256, 256, 128, 64), (128, 128, 64, 64), (64, 64, 32, 32), (256, 128, 64, 64), (128, 64, 64, 32),
+                (32, 32, 32, 32), (64, 32, 64, 32)]
 
 
 @pytest.mark.parametrize("prec", ["f16", "i8", "i4"])
-@pytest.mark.parametrize("cfg", LINE_CONFIGS, ids=["256", "128", "64", "256x128", "128x64"])
+@pytest.mark.parametrize("cfg", LINE_CONFIGS, ids=["256", "128", "64", "256x128", "128x64", "ks32x32", "ks64x32"])
 def test_rowmajor_b_line_layout(prec, cfg):
     # Whole-line stages hold two K tiles: the B part is 2 * krows rows of B.  DMA
     # instruction j of wave w fills 1 KB block j*NW + w of the stage (lane l: chunk l of
