@@ -327,14 +327,20 @@ def test_ksplit_small_m(pd, dev, prec, shape, cfg):
     check_full(prec, A, Bt, K, C, f"ksplit {prec} {shape}")
 
 
-def test_ksplit_f16_is_deterministic(pd, dev):
-    M, N, K = 16, 2048, 4096
-    gu.note("[case] ksplit f16 determinism")
+@pytest.mark.parametrize("cfg", [3, 6])
+def test_ksplit_f16_is_deterministic(pd, dev, cfg):
+    # the partial tiles of the K split are summed in a fixed wave order
+    M, N, K = 48, 2048, 4100
+    gu.note(f"[case] ksplit f16 determinism cfg={cfg}")
     A, Bt = synth.operands("f16", M, N, K, 41, 42)
-    Ad, Bd = torch.from_numpy(A).to(dev), torch.from_numpy(Bt).to(dev)
-    ref = pd.gemm_f16(Ad, Bd, cfg=3)
+    ld = gu.round_up(K, 8)
+    Ad = torch.from_numpy(synth.with_leading_dim(A, ld)).to(dev)[:, :K]
+    Bd = torch.from_numpy(synth.with_leading_dim(Bt, ld)).to(dev)[:, :K]
+    ref = pd.gemm_f16(Ad, Bd, cfg=cfg)
     for _ in range(3):
-        assert torch.equal(pd.gemm_f16(Ad, Bd, cfg=3).view(torch.int32), ref.view(torch.int32))
+        assert torch.equal(pd.gemm_f16(Ad, Bd, cfg=cfg).view(torch.int32), ref.view(torch.int32))
+    R, S = gu.oracle_full("f16", A, Bt, K)
+    gu.assert_f16_close(ref.cpu().numpy(), R, S, f"ksplit determinism cfg{cfg}")
 
 
 @pytest.mark.parametrize("prec", PRECS)
