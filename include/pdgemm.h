@@ -38,6 +38,10 @@
  * carry fp32 rounding only: every element satisfies
  * |C - sum_k a_ik b_kj| <= 1e-3 * sum_k |a_ik b_kj| for K up to 16384 (the
  * worst-case bound of K fp32 additions, K * 2^-24, stays below 1e-3).
+ * Each FP16 sum runs in a fixed order (no atomics), so a call gives the same
+ * bits every time for a given shape and tile configuration.  The
+ * configurations without a K split share one order and give the same bits
+ * as each other; the K-split configurations group K differently.
  *
  * Alignment (checked): A and B 16-byte aligned, with lda and ldb spanning a
  * multiple of 16 bytes (f16: lda, ldb % 8 == 0; i8: % 16; i4: % 32); C
@@ -51,10 +55,11 @@
  *
  * Ownership and execution: every pointer is device memory owned by the
  * caller, on the device the stream belongs to.  C must not overlap A, B or
- * the scales (the result is then undefined).  The library never allocates, frees, copies or synchronizes.  The
- * call enqueues work on `stream` (a hipStream_t passed as void*; NULL is the
- * default stream) and returns once it is enqueued.  Entry points are
- * thread-safe and keep no state between calls.
+ * the scales (the result is then undefined).  The library never allocates,
+ * frees, copies or synchronizes.  The call enqueues work on `stream` (a
+ * hipStream_t passed as void*; NULL is the default stream) and returns once
+ * it is enqueued.  Entry points are thread-safe and keep no state between
+ * calls.
  *
  * Errors: 0 on success.  Negative values are argument errors, found on the
  * host before any HIP call is made, with nothing enqueued.  Positive values
