@@ -327,6 +327,22 @@ def test_ksplit_small_m(pd, dev, prec, shape, cfg):
     check_full(prec, A, Bt, K, C, f"ksplit {prec} {shape}")
 
 
+def test_configs_without_k_split_give_the_same_fp16_bits(pd, dev):
+    # every tile without a K split sums each element over K in the same order
+    M, N, K = 300, 260, 1030
+    gu.note("[case] f16 bits across configurations")
+    A, Bt = synth.operands("f16", M, N, K, 61, 62)
+    ld = gu.round_up(K, 8)
+    Ad = torch.from_numpy(synth.with_leading_dim(A, ld)).to(dev)[:, :K]
+    Bd = torch.from_numpy(synth.with_leading_dim(Bt, ld)).to(dev)[:, :K]
+    info = {c: pd.config_info(c) for c in range(pd.num_configs())}
+    plain = [c for c, v in info.items() if v["threads"] == (v["block_m"] // v["wave_m"]) * (v["block_n"] // v["wave_n"]) * 64]
+    assert len(plain) >= 5
+    outs = [pd.gemm_f16(Ad, Bd, cfg=c).view(torch.int32) for c in plain]
+    for c, o in zip(plain[1:], outs[1:]):
+        assert torch.equal(o, outs[0]), f"configuration {c} differs from {plain[0]}"
+
+
 @pytest.mark.parametrize("cfg", [3, 6])
 def test_ksplit_f16_is_deterministic(pd, dev, cfg):
     # the partial tiles of the K split are summed in a fixed wave order
