@@ -196,37 +196,37 @@ __device__ __forceinline__ int bswizzle(int r) {
     return RowB<P>::kQ * ((r / v) % span);
 }
 
-// One workgroup computes a BM x BN block of C with (BM/WM) x (BN/WN) waves.
+// One workgroup computes a BM x BN block of C with (BM/WM) x (BN/WN) waves
+// (times KS with a K split, whose waves share the block).
 //
-// K is consumed in tiles of 64 bytes per row (32 f16, 64 int8 or 128 packed
-// int4 values).  LDS holds kStages stages; a stage is BM rows of A then BN
-// rows of B, 64 bytes each, in four 16-byte chunks, logical chunk c of row r
-// at position c ^ swizzle(r).  A stage is filled by buffer_load_dwordx4 ...
-// lds: each instruction of a wave writes 1 KB = 16 whole rows, lane l landing
-// in row l/4 at position l%4, so lane l fetches logical chunk
-// (l%4) ^ swizzle(row) of its row.  (A row-major B fills the B part of a
-// stage with K rows instead, see RowB; with a K split (KS > 1) a K tile is
-// KS x 64 bytes and a stage holds one such A-then-B slice per wave.)
+// K is consumed in K tiles of 64 bytes per row (32 f16, 64 int8 or 128
+// packed int4 values); a k-step is 32 of those bytes.  A k-step reads one
+// 16-byte fragment per lane for each of a wave's WM/32 row blocks of A and
+// WN/32 column blocks of B (row = lane%32, 16-byte half = lane/32) and
+// issues the MFMAs on them; fragments are read one k-step ahead.
 //
-// Tile t lives in stage t % kStages and is fetched kStages tiles before it
-// is consumed.  Per tile a wave runs two k-steps; a k-step reads one 16-byte
-// fragment per lane for each of its WM/32 row blocks of A and WN/32 column
-// blocks of B (row = lane%32, 16-byte half = lane/32) and issues the MFMAs
-// on them; fragments are read one k-step ahead.  The one barrier of a tile
-// comes after its second fragments are in registers: each wave first waits
-// only for its own DMA of tile t+1 (tiles t+2 .. t+kStages-1 stay in
-// flight), so after the barrier tile t+1 is complete in LDS and stage t is
-// free for tile t+kStages.
+// Whole-line staging (LS > 0, every tile but the 32 x 32 K-split one): a
+// stage holds two K tiles, 128 bytes per row (with a K split: per row of
+// each wave's own slice) in eight 16-byte chunks, logical chunk c of row r at
+// position c ^ swizzle8(r); BM rows of A, then BN rows of B (a row-major B
+// part holds the 2 * kKRows rows of B of the two K tiles as flat chunks,
+// each row of B a whole number of lines).  Each DMA instruction of a wave
+// writes 1 KB = 8 whole rows, lane l landing in row l/8 at position l%8, so
+// each instruction reads whole 128-byte lines.  Stage s is fetched LS
+// stages before it is consumed, four k-steps per stage; the one barrier of
+// a stage comes after its last fragments are in registers, once this wave's
+// DMA of stage s+1 has landed (stages s+2 .. s+LS-1 stay in flight), and a
+// K-split wave, which reads only its own slice, needs no barrier.
 //
-// Whole-line staging (LS > 0): a stage holds two K tiles, 128 bytes per row
-// (with a K split: per row of each wave's slice) in eight 16-byte chunks,
-// logical chunk c of row r at position c ^ swizzle8(r); each DMA instruction
-// of a wave writes 1 KB = 8 whole rows, lane l landing in row l/8 at
-// position l%8, so each instruction reads whole 128-byte lines.  (A row-major B part holds the 2 * kKRows rows of B of the
-// two K tiles as in a 64-byte stage, each row of B a whole number of lines.)  LS stages: stage s is fetched LS
-// stages before it is consumed, four k-steps per stage, and the one barrier
-// of a stage comes after its last fragments are in registers, once this
-// wave's DMA of stage s+1 has landed (stages s+2 .. s+LS-1 stay in flight).
+// 64-byte staging (LS = 0, the 32 x 32 K-split tile): kStages stages, each
+// with one 64-byte slice of KS x 64 bytes of K per row and wave; each DMA
+// instruction of a wave writes 1 KB = 16 rows of its slice, lane l landing
+// in row l/4 at position l%4 (logical chunk c of row r at position
+// c ^ swizzle(r)).  Tile t lives in stage t % kStages and is fetched
+// kStages tiles before it is consumed, two k-steps per tile; each wave
+// waits only for its own DMA of tile t+1 (tiles t+2 .. t+kStages-1 stay in
+// flight).  (The same path serves tiles without K split, with the stage
+// rows spread over the waves and a barrier per tile.)
 template <int P, int BM, int BN, int WM, int WN, int GM, int E, int BR, int KS, int LS>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kernel(Args args) {
     // The body uses gfx950-only types (buffer resources), which the host
