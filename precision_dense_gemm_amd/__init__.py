@@ -344,9 +344,13 @@ def prepare(prec: str, A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor, K: 
     if rc != 0:
         raise PdgemmError(rc)
 
+    # the callable holds the tensors, so their memory outlives it
+    keep = (A, Bt, out) + (tuple(scales) if scales is not None else ())
+
     def launch():
         rc = fn(*args)
         if rc != 0:
             raise PdgemmError(rc)
 
+    launch.tensors = keep
     return launch
