@@ -11,6 +11,8 @@ HBM before the timed region starts.  The JSON line reports:
                 HIP events on the launch stream over the timed steps, TOPS, fraction
                 of peak; and
                 the same GEMM timed over back-to-back launches after the steps
+                (R launches captured in one HIP graph, median of 3 replays, so
+                that host launch cost is not timed)
   roofline      the GEMM that takes the largest share of a step, against the
                 MFMA peak of its own precision
   cpu_baseline  the CPU oracle (plain triple loop) timed on a row sample of
@@ -294,35 +296,40 @@ def main():
     step_ops = sum(gemm_ops(n) for _, n, *_ in work)
     value = step_ops / (ms_per_step * 1e-3) / 1e12
 
-    # Back-to-back timing of each GEMM on its own (after the timed steps):
-    # one event pair around R launches, so the per-launch event cost does not
-    # swamp the few-microsecond kernels; inputs stay warm in L2/MALL.
+    # Back-to-back timing of one GEMM on its own (after the timed steps): R
+    # launches captured in one HIP graph and replayed, so that neither host
+    # launch cost nor per-launch events enter the few-microsecond kernels;
+    # inputs stay warm in L2/MALL.  make_go prepares the launch on the stream
+    # current at its call (the capture stream); prepare() enqueues the first of
+    # the R launches itself.  Median of `replays` replays, per launch.
+    def time_b2b(make_go, est_ms, replays=3):
+        reps = int(min(200, max(5, 2.0 / max(est_ms, 1e-3))))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            go = make_go()
+            for _ in range(reps - 1):
+                go()
+        g.replay()
+        times = []
+        for _ in range(replays):
+            s0 = torch.cuda.Event(enable_timing=True)
+            e0 = torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            g.replay()
+            e0.record(stream)
+            e0.synchronize()
+            times.append(s0.elapsed_time(e0) / reps)
+        del g, go
+        return float(np.median(times))
+
+    def plain(prec, n, Ad, Bd, C):
+        return lambda: pd.prepare(prec, Ad, Bd, C, K=n)
+
     b2b = {}
     for w in work:
         prec, n = w[0], w[1]
         est = float(np.mean([s.elapsed_time(e) for s, e in ev[(prec, n)]])) if ev[(prec, n)] else 1.0
-        reps = int(min(200, max(5, 2.0 / max(est, 1e-3))))
-        launch(*w)
-        s0 = torch.cuda.Event(enable_timing=True)
-        e0 = torch.cuda.Event(enable_timing=True)
-        s0.record(stream)
-        for _ in range(reps):
-            launch(*w)
-        e0.record(stream)
-        e0.synchronize()
-        b2b[(prec, n)] = s0.elapsed_time(e0) / reps
-
-    def time_b2b(go, est_ms):
-        reps = int(min(200, max(5, 2.0 / max(est_ms, 1e-3))))
-        go()
-        s0 = torch.cuda.Event(enable_timing=True)
-        e0 = torch.cuda.Event(enable_timing=True)
-        s0.record(stream)
-        for _ in range(reps):
-            go()
-        e0.record(stream)
-        e0.synchronize()
-        return s0.elapsed_time(e0) / reps
+        b2b[(prec, n)] = time_b2b(plain(*w), est)
 
     # ---- the dequantizing epilogue at N = 8192 (not part of the step) ----
     dequant = {}
@@ -334,7 +341,9 @@ def main():
             sb_h = synth.f32_scales(n, synth.config_seed(SWEEP_CFG_ID, n, synth.OPERAND_B) + 3)
             sad, sbd = torch.from_numpy(sa_h).to(dev), torch.from_numpy(sb_h).to(dev)
             Ch = torch.empty((n, n), dtype=torch.float16, device=dev)
-            go = pd.prepare(prec, Ad, Bd, Ch, K=n, scales=(sad, sbd))
+            def dequant_go():
+                return pd.prepare(prec, Ad, Bd, Ch, K=n, scales=(sad, sbd))
+            dequant_go()
             torch.cuda.synchronize()
             entry = {"out": "f16"}
             if not args.no_parity:
@@ -352,8 +361,8 @@ def main():
             # alternate the two so that clock and power drift hit both alike
             ds, rs = [], []
             for _ in range(3):
-                ds.append(time_b2b(go, b2b[(prec, n)]))
-                rs.append(time_b2b(launchers[(prec, n)], b2b[(prec, n)]))
+                ds.append(time_b2b(dequant_go, b2b[(prec, n)]))
+                rs.append(time_b2b(plain(prec, n, Ad, Bd, C), b2b[(prec, n)]))
             ms_d, ms_r = float(np.median(ds)), float(np.median(rs))
             entry.update({
                 "ms_back_to_back": round(ms_d, 5),
@@ -380,7 +389,9 @@ def main():
                 Brow = np.ascontiguousarray(Bt.T)
             Brd = torch.from_numpy(Brow).to(dev)
             Cr = torch.empty_like(C)
-            go = pd.prepare(prec, Ad, Brd, Cr, K=n, rowb=True)
+            def rowb_go():
+                return pd.prepare(prec, Ad, Brd, Cr, K=n, rowb=True)
+            rowb_go()
             launchers[(prec, n)]()
             torch.cuda.synchronize()
             entry = {"same_as_column_major": bool(torch.equal(Cr.view(torch.int32), C.view(torch.int32)))}
@@ -400,8 +411,8 @@ def main():
                 parity[f"{prec}:{n}:rowb"] = entry["parity"]
             rs, cs = [], []
             for _ in range(3):
-                rs.append(time_b2b(go, b2b[(prec, n)]))
-                cs.append(time_b2b(launchers[(prec, n)], b2b[(prec, n)]))
+                rs.append(time_b2b(rowb_go, b2b[(prec, n)]))
+                cs.append(time_b2b(plain(prec, n, Ad, Bd, C), b2b[(prec, n)]))
             ms_r, ms_c = float(np.median(rs)), float(np.median(cs))
             entry.update({
                 "ms_back_to_back": round(ms_r, 5),
@@ -423,7 +434,9 @@ def main():
                 continue
             for M in SHAPE_MS:
                 Cm = torch.empty((M, n), dtype=C.dtype, device=dev)
-                go = pd.prepare(prec, Ad[:M], Bd, Cm, K=n)
+                def shape_go():
+                    return pd.prepare(prec, Ad[:M], Bd, Cm, K=n)
+                shape_go()
                 torch.cuda.synchronize()
                 entry = {"M": M, "N": n, "K": n,
                          "cfg": pd.pick_config({"f16": 0, "i8": 1, "i4": 2}[prec], M, n, n)}
@@ -441,7 +454,7 @@ def main():
                         ok = bool(np.array_equal(got.astype(np.int64), ref))
                     entry["parity"] = ok
                     parity[f"{prec}:{M}x{n}x{n}"] = ok
-                ms = time_b2b(go, 0.05)
+                ms = time_b2b(shape_go, 0.05)
                 entry["ms_back_to_back"] = round(ms, 5)
                 entry["roofline"] = shape_roofline(prec, M, n, n, ms)
                 if prec != "f16":
@@ -451,13 +464,13 @@ def main():
                     sbh = synth.f32_scales(n, synth.config_seed(SWEEP_CFG_ID, n, synth.OPERAND_B) + 3)
                     Ch = torch.empty((M, n), dtype=torch.float16, device=dev)
                     scl = (torch.from_numpy(sah).to(dev), torch.from_numpy(sbh).to(dev))
-                    god = pd.prepare(prec, Ad[:M], Bd, Ch, K=n, scales=scl)
-                    entry["dequant_f16_ms_back_to_back"] = round(time_b2b(god, 0.05), 5)
+                    entry["dequant_f16_ms_back_to_back"] = round(time_b2b(
+                        lambda: pd.prepare(prec, Ad[:M], Bd, Ch, K=n, scales=scl), 0.05), 5)
                     del Ch, scl
                 if prec in brow_dev:
                     # the same product with B row-major
-                    gor = pd.prepare(prec, Ad[:M], brow_dev[prec], Cm, K=n, rowb=True)
-                    entry["rowb_ms_back_to_back"] = round(time_b2b(gor, 0.05), 5)
+                    entry["rowb_ms_back_to_back"] = round(time_b2b(
+                        lambda: pd.prepare(prec, Ad[:M], brow_dev[prec], Cm, K=n, rowb=True), 0.05), 5)
                 shapes[f"{prec}:{M}x{n}x{n}"] = entry
                 log(f"[bench] shape {prec} {M}x{n}x{n}: {ms * 1e3:.1f} us "
                     f"({entry['roofline']['bound']} {entry['roofline']['frac']:.3f})")
