@@ -12,7 +12,9 @@ HBM before the timed region starts.  The JSON line reports:
                 of peak; and
                 the same GEMM timed over back-to-back launches after the steps
                 (R launches captured in one HIP graph, median of 3 replays, so
-                that host launch cost is not timed)
+                that host launch cost is not timed); for N <= 2048 also cold:
+                each launch after a 512 MiB fill that evicts L2 and MALL, so
+                its operands come from HBM (median of 10)
   roofline      the GEMM that takes the largest share of a step, against the
                 MFMA peak of its own precision
   cpu_baseline  the CPU oracle (plain triple loop) timed on a row sample of
@@ -78,6 +80,8 @@ def parse():
     ap.add_argument("--case", action="append", default=[],
                     help="time only prec:N (repeatable), e.g. f16:8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache timing of the N <= 2048 GEMMs")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--no-dequant", action="store_true",
                     help="skip the dequantizing-epilogue measurement")
@@ -135,6 +139,7 @@ def gemm_ops(n):
 
 
 SHAPE_MS = (16, 64, 256, 1024)   # rows of A for the non-square shapes M x 8192 x 8192
+COLD_MAX_N, COLD_REPS = 2048, 10   # cold-cache timing: sweep sizes up to this N, launches each
 
 
 def shape_roofline(prec, M, N, K, ms):
@@ -325,6 +330,29 @@ def main():
     def plain(prec, n, Ad, Bd, C):
         return lambda: pd.prepare(prec, Ad, Bd, C, K=n)
 
+    # Cold-cache timing of the small GEMMs (outside the step): before each
+    # launch a 512 MiB fill evicts the L2s and the 256 MB MALL, so the operands
+    # come from HBM; events bracket the launch alone.  Median of COLD_REPS.
+    cold = {}
+    if not args.no_cold:
+        scrub = torch.empty(1 << 27, dtype=torch.float32, device=dev)   # 512 MiB
+        for w in work:
+            prec, n = w[0], w[1]
+            if n > COLD_MAX_N:
+                continue
+            times = []
+            for r in range(COLD_REPS):
+                scrub.fill_(float(r))
+                s0 = torch.cuda.Event(enable_timing=True)
+                e0 = torch.cuda.Event(enable_timing=True)
+                s0.record(stream)
+                launch(*w)
+                e0.record(stream)
+                e0.synchronize()
+                times.append(s0.elapsed_time(e0))
+            cold[(prec, n)] = float(np.median(times))
+        del scrub
+
     b2b = {}
     for w in work:
         prec, n = w[0], w[1]
@@ -492,6 +520,9 @@ def main():
             "ms_back_to_back": round(ms_b, 5),
             "tops_back_to_back": round(gemm_ops(n) / (ms_b * 1e-3) / 1e12, 2),
             "min_hbm_gbs": round(hbm_bytes / (ms * 1e-3) / 1e9, 1),
+            **({"ms_cold": round(cold[(prec, n)], 5),
+                "cold_min_hbm_gbs": round(hbm_bytes / (cold[(prec, n)] * 1e-3) / 1e9, 1)}
+               if (prec, n) in cold else {}),
             "l4_tops_context": round(gemm_ops(n) / (L4_MS[prec][n] * 1e-3) / 1e12, 3),
         }
         if f"{prec}:{n}" in parity:
