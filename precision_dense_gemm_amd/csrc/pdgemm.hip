@@ -49,6 +49,8 @@
 //    XCDs, so the block id is remapped to give each XCD a contiguous range of
 //    tiles, and tiles are ordered in bands of GM block rows so that the
 //    workgroups resident on one XCD share A and B panels in its L2.
+//  * C is stored non-temporally: at N = 8192 its 268 MB would otherwise push
+//    the A and B panels out of the 256 MB MALL between rounds of tiles.
 //  * Ragged edges: rows of A (and columns of a column-major B) past M / N are
 //    clamped to the last valid one, and the columns of a row-major B past N
 //    are read from its padding; their results are discarded.  The buffer
@@ -915,8 +917,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
                         } else {
                             v = acc[i][j][e];
                         }
+                        // non-temporal: C is not read again here, and
+                        // streaming it past the MALL keeps A and B there
+                        // for the later rounds of tiles
                         if (keep(r, j))
-                            *reinterpret_cast<Out *>(row_c + lane_off + j * 32 * (int)sizeof(Out)) = v;
+                            __builtin_nontemporal_store(
+                                v, reinterpret_cast<Out *>(row_c + lane_off + j * 32 * (int)sizeof(Out)));
                     }
                     // dequantized values are converted one row at a time
                     if constexpr (E != kRaw) __builtin_amdgcn_sched_barrier(0);
