@@ -27,6 +27,9 @@ HBM before the timed region starts.  The JSON line reports:
                 paper's "transposed B", read with transposing LDS loads), timed
                 back to back alternately with the column-major B kernel (medians
                 of 3), checked bit-equal to it and against the oracle
+  telemetry     (outside the step) socket power, graphics clock (mean over
+                the XCDs) and hotspot temperature from amdsmi while the sweep
+                runs back to back for 3 s, with the board's power limit
   shapes        (outside the step) non-square inference shapes M x 8192 x 8192,
                 M in {16, 64, 256, 1024}: the first M rows of the sweep's
                 N = 8192 operands, timed back to back and placed on their own
@@ -80,6 +83,8 @@ def parse():
     ap.add_argument("--case", action="append", default=[],
                     help="time only prec:N (repeatable), e.g. f16:8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-telemetry", action="store_true",
+                    help="skip the power / clock sampling under sustained sweep load")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache timing of the N <= 2048 GEMMs")
     ap.add_argument("--no-parity", action="store_true")
@@ -134,12 +139,72 @@ def trace_summary(path):
                 print(f"    {c:28s} dispatches {len(v):5d}  mean {np.mean(v):18.1f}")
 
 
+def sample_power(step, ms_per_step):
+    """Run `step` back to back for about TELEMETRY_S seconds while a thread
+    samples amdsmi's GPU metrics; return socket power, graphics clock and
+    hotspot temperature during the load (medians / max), or None when amdsmi
+    is not available."""
+    import threading
+
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                samples.append((time.time(), m.get("current_socket_power"), m.get("current_gfxclks"),
+                                m.get("temperature_hotspot")))
+            except Exception:
+                pass
+            stop.wait(0.01)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    steps = max(1, int(TELEMETRY_S * 1e3 / max(ms_per_step, 1e-3)))
+    torch.cuda.synchronize()
+    t0 = time.time()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.time()
+    stop.set()
+    th.join()
+    try:
+        limit_uw = amdsmi.amdsmi_get_power_info(handle).get("power_limit")
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        limit_uw = None
+    inside = [s for s in samples if t0 + 0.5 < s[0] < t1 - 0.1]
+    power = [s[1] for s in inside if isinstance(s[1], (int, float))]
+    clocks = [float(np.mean(s[2])) for s in inside if isinstance(s[2], (list, tuple)) and s[2]
+              and all(isinstance(c, (int, float)) for c in s[2])]
+    temps = [s[3] for s in inside if isinstance(s[3], (int, float))]
+    return {
+        "load_s": round(t1 - t0, 2),
+        "samples": len(inside),
+        "socket_power_w_median": float(np.median(power)) if power else None,
+        "socket_power_w_max": float(max(power)) if power else None,
+        "power_limit_w": round(limit_uw / 1e6, 1) if isinstance(limit_uw, (int, float)) else None,
+        "gfxclk_mhz_median": round(float(np.median(clocks)), 1) if clocks else None,
+        "temp_hotspot_c_max": float(max(temps)) if temps else None,
+        "note": "amdsmi metrics refresh about once a second; samples from inside the load only",
+    }
+
+
 def gemm_ops(n):
     return 2.0 * n * n * n
 
 
 SHAPE_MS = (16, 64, 256, 1024)   # rows of A for the non-square shapes M x 8192 x 8192
 COLD_MAX_N, COLD_REPS = 2048, 10   # cold-cache timing: sweep sizes up to this N, launches each
+TELEMETRY_S = 3.0                  # seconds of sustained sweep load sampled for power and clock
 
 
 def shape_roofline(prec, M, N, K, ms):
@@ -358,6 +423,14 @@ def main():
         prec, n = w[0], w[1]
         est = float(np.mean([s.elapsed_time(e) for s, e in ev[(prec, n)]])) if ev[(prec, n)] else 1.0
         b2b[(prec, n)] = time_b2b(plain(*w), est)
+
+    # ---- power and clock under sustained load (outside the timed steps) ----
+    # amdsmi's metrics table refreshes about once a second, far slower than a
+    # step, so the sweep runs for TELEMETRY_S while a thread samples it; only
+    # samples taken well inside the load are kept.
+    telemetry = None
+    if not args.no_telemetry:
+        telemetry = sample_power(lambda: [launch(*w) for w in work], ms_per_step)
 
     # ---- the dequantizing epilogue at N = 8192 (not part of the step) ----
     dequant = {}
@@ -611,6 +684,7 @@ def main():
         "dequant": dequant or None,
         "layout": layout or None,
         "shapes": shapes or None,
+        "telemetry": telemetry,
     }
     print(json.dumps(out), flush=True)
     if parity and not all(parity.values()):
