@@ -40,3 +40,10 @@ def test_trace_summary_of_a_small_trace(tmp_path):
                    '"void (anonymous namespace)::gemm_kernel<0, 256, 256, 128, 128, 4>((anonymous namespace)::Args)",262144,256,5000,9000\n')
     r = subprocess.run([sys.executable, bench.__file__, "--trace-summary", str(csv)], capture_output=True, text=True)
     assert r.returncode == 0 and "3.00" in r.stdout and "gemm_kernel<0, 256, 256, 128, 128, 4>" in r.stdout
+
+
+def test_telemetry_is_absent_without_a_gpu():
+    # amdsmi finds no device here: the section is reported as null, the step is never run
+    ran = []
+    assert bench.sample_power(lambda: ran.append(1), 1.0) is None
+    assert not ran
