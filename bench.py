@@ -8,15 +8,17 @@ HBM before the timed region starts.  The JSON line reports:
   value         whole-step throughput in TOPS (2*M*N*K per GEMM, summed over
                 the sweep, divided by the wall time of a step)
   per_gemm      per (precision, N): mean (also median and minimum) kernel time from
-                HIP events on the launch stream over the timed steps, TOPS, fraction
-                of peak; and
+                HIP events on the launch stream around every GEMM of K steps run
+                right after the timed ones (the timed steps carry events around
+                the dominant GEMM only), TOPS, fraction of peak; and
                 the same GEMM timed over back-to-back launches after the steps
                 (R launches captured in one HIP graph, median of 3 replays, so
                 that host launch cost is not timed); for N <= 2048 also cold:
                 each launch after a 512 MiB fill that evicts L2 and MALL, so
                 its operands come from HBM (median of 10)
-  roofline      the GEMM that takes the largest share of a step, against the
-                MFMA peak of its own precision
+  roofline      the GEMM that takes the largest share of a step, timed by its
+                HIP events inside the timed steps, against the MFMA peak of its
+                own precision
   cpu_baseline  the CPU oracle (plain triple loop) timed on a row sample of
                 every GEMM of the sweep and scaled to whole GEMMs
   dequant       (outside the step) the INT8 / INT4 GEMMs at N = 8192 with the
@@ -345,23 +347,43 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
 
-    ev = {(p, n): [] for p, n, *_ in work}
-    pool = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in work] for _ in range(args.steps)]
+    def instrumented_steps(count, only=None):
+        """Run `count` steps with a HIP event pair on the launch stream around
+        every GEMM (or only around `only`); return the event pairs per GEMM."""
+        out = {(p, n): [] for p, n, *_ in work}
+        pairs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  if only is None or (w[0], w[1]) == only else None for w in work] for _ in range(count)]
+        for step in range(count):
+            for w, se in zip(work, pairs[step]):
+                if se is None:
+                    launch(*w)
+                    continue
+                se[0].record(stream)
+                launch(*w)
+                se[1].record(stream)
+                out[(w[0], w[1])].append(se)
+        return out
+
+    # The dominant GEMM (the largest share of a step) gets an event pair in
+    # the timed steps, for the roofline; an event pair around every GEMM would
+    # add its own cost to the step, so the per-GEMM in-step times come from
+    # instrumented steps after the timed ones.
+    probe = instrumented_steps(1)
+    torch.cuda.synchronize()
+    dom_key = max(probe, key=lambda k: probe[k][0][0].elapsed_time(probe[k][0][1]))
+
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for step in range(args.steps):
-        for w, (s, e) in zip(work, pool[step]):
-            s.record(stream)
-            launch(*w)
-            e.record(stream)
+    timed = instrumented_steps(args.steps, only=dom_key)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for step in range(args.steps):
-        for w, se in zip(work, pool[step]):
-            ev[(w[0], w[1])].append(se)
     ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+    dom_ms = [s.elapsed_time(e) for s, e in timed[dom_key]]
+
+    ev = instrumented_steps(args.steps)
+    torch.cuda.synchronize()
+    log(f"[bench] {args.steps} instrumented steps for the per-GEMM times")
 
     step_ops = sum(gemm_ops(n) for _, n, *_ in work)
     value = step_ops / (ms_per_step * 1e-3) / 1e12
@@ -606,16 +628,19 @@ def main():
         if key in per:
             per[key]["hbm_bytes_profiled"] = nbytes
 
-    # dominant kernel: the largest share of a step
-    dom = max(per, key=lambda k: per[k]["ms"])
-    dprec, dn = dom.split(":")[0], int(dom.split(":")[1])
+    # dominant kernel: the largest share of a step, timed by its own event
+    # pairs inside the timed steps
+    dprec, dn = dom_key
+    dom = f"{dprec}:{dn}"
+    dom_tops = gemm_ops(dn) / (float(np.mean(dom_ms)) * 1e-3) / 1e12
+    per[dom]["ms_timed_steps"] = round(float(np.mean(dom_ms)), 5)
     roofline = {
         "bound": "mfma",
         "kernel": f"gemm_kernel {dprec} N={dn}",
-        "achieved": per[dom]["tops"],
+        "achieved": round(dom_tops, 2),
         "peak": PEAK[dprec],
         "unit": "TFLOP/s" if dprec == "f16" else "TOPS",
-        "frac": round(per[dom]["tops"] / PEAK[dprec], 4),
+        "frac": round(dom_tops / PEAK[dprec], 4),
         # HBM bytes per launch, rocprofv3 counters scaled by a 1 GiB copy
         "traffic": traffic.get(dom),
     }
