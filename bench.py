@@ -276,7 +276,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the GEMM shards by output panels with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(across GPUs the GEMM would shard by output panels, with no exchange)", file=sys.stderr)
         sys.exit(2)
 
     import torch
