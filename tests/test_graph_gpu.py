@@ -73,3 +73,32 @@ def test_captured_gemm_replays(pd, dev, prec, shape):
         R, S = oracle.gemm_f16(A, Bt)
         gu.assert_f16_close(eager.cpu().numpy(), R, S, "graph f16")
     del g
+
+
+@pytest.mark.parametrize("prec", ["f16", "i8", "i4"])
+def test_prepared_launches_captured_in_a_graph(pd, dev, prec):
+    # prepare() inside a capture: its first launch and the callable's later ones
+    # are all recorded on the capture stream, as the back-to-back timing uses them
+    M, N, K = 300, 200, 512
+    gu.note(f"[case] graph prepare {prec} {M}x{N}x{K}")
+    A, Bt = synth.operands(prec, M, N, K, 93, 94)
+    Ad, Bd = torch.from_numpy(A).to(dev), torch.from_numpy(Bt).to(dev)
+    out = torch.empty((M, N), dtype=torch.float32 if prec == "f16" else torch.int32, device=dev)
+    pd.prepare(prec, Ad, Bd, out, K=K)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        go = pd.prepare(prec, Ad, Bd, out, K=K)
+        go()
+        go()
+    for replay in range(3):
+        out.view(torch.int32).fill_(gu.C_SENTINEL_BITS)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), eager.view(torch.int32)), f"replay {replay}"
+    if prec != "f16":
+        ref = oracle.gemm_i8(A, Bt) if prec == "i8" else oracle.gemm_i4(A, Bt, K)
+        gu.assert_int_equal(eager.cpu().numpy(), ref, f"graph prepare {prec}")
+    del g
