@@ -17,6 +17,11 @@ Sources of truth used here:
     nibble positions) against numpy integer outer products;
   * algebraic invariants (transpose symmetry, linearity, thread-count
     independence, entry-wise vs full agreement).
+
+The whole-product form in oracle/matmul.py (the same definition with the sum
+over k done by one fp64 matrix product, used for full-size comparisons) is
+pinned by the MATMUL_PINS: the worked example, closed forms, exact brute
+force, product tables, and agreement with the pinned triple loop.
 """
 from __future__ import annotations
 
@@ -405,6 +410,150 @@ def pin_rowb():
     assert np.array_equal(Re, Rf[rows, cols]) and np.array_equal(Se, Sf[rows, cols])
 
 
+
+# --------------------------------------------------------------------------
+# pins of the whole-product form (oracle/matmul.py: the same definition with
+# the sum over k done by one fp64 matrix product), each taking that module so
+# that planted mistakes in a copy of it can be run through them
+
+def _lab_int_operands():
+    g, A, _ = _lab_operands()
+    M, N, K = g["M"], g["N"], g["K"]
+    B8 = np.array([[8 * r + c - 64 for c in range(N)] for r in range(K)], dtype=np.int8)
+    B4 = np.array([[((8 * r + c) % 16) - 8 for c in range(N)] for r in range(K)], dtype=np.int8)
+    return g, A, B8, B4
+
+
+def pin_matmul_lab(mm):
+    """The PTX tutorial's printed example, with B in both layouts."""
+    g, A, Bmat = _lab_operands()
+    for R, _ in (mm.gemm_f16(A.astype(np.float16), Bmat.T.astype(np.float16)),
+                 mm.gemm_f16(A.astype(np.float16), Bmat.astype(np.float16), rowb=True)):
+        for r, c, v in g["printed_entries"]:
+            assert R[r, c] == v, (r, c, R[r, c], v)
+        assert np.array_equal(R, Bmat[: g["M"]])
+    _, Ar, _ = _lab_operands(reverse_rows=True)
+    R2, _ = mm.gemm_f16(Ar.astype(np.float16), Bmat.T.astype(np.float16))
+    assert list(R2[0]) == g["row_reversed_A_first_row"]
+    R3, _ = mm.gemm_f16(Ar.astype(np.float16), Bmat.astype(np.float16), rowb=True)
+    assert list(R3[0]) == g["row_reversed_A_first_row"]
+    g, A, B8, B4 = _lab_int_operands()
+    assert np.array_equal(mm.gemm_i8(A.astype(np.int8), np.ascontiguousarray(B8.T)), B8.astype(np.int64))
+    assert np.array_equal(mm.gemm_i8(A.astype(np.int8), B8, rowb=True), B8.astype(np.int64))
+    pa = synth.pack_int4(A.astype(np.int8))
+    assert np.array_equal(mm.gemm_i4(pa, synth.pack_int4(np.ascontiguousarray(B4.T))), B4.astype(np.int64))
+    assert np.array_equal(mm.gemm_i4(pa, synth.pack_int4(B4), rowb=True), B4.astype(np.int64))
+    _, Ar, _ = _lab_operands(reverse_rows=True)
+    C4r = mm.gemm_i4(synth.pack_int4(Ar.astype(np.int8)), synth.pack_int4(np.ascontiguousarray(B4.T)))
+    assert np.array_equal(C4r, B4[::-1].astype(np.int64))
+
+
+def pin_matmul_closed_forms(mm):
+    M, N, K = 5, 7, 34
+    R, S = mm.gemm_f16(np.ones((M, K), np.float16), np.ones((N, K), np.float16))
+    assert np.all(R == K) and np.all(S == K)
+    R, S = mm.gemm_f16(np.full((M, K), -1.0, np.float16), np.ones((N, K), np.float16))
+    assert np.all(R == -K) and np.all(S == K)
+    R, S = mm.gemm_f16(np.full((M, K), -0.5, np.float16), np.full((K, N), 2.0, np.float16), rowb=True)
+    assert np.all(R == -K) and np.all(S == K)
+    assert np.all(mm.gemm_i8(np.full((M, K), -128, np.int8), np.full((N, K), -128, np.int8)) == 16384 * K)
+    assert np.all(mm.gemm_i8(np.full((M, K), -128, np.int8), np.full((N, K), 127, np.int8)) == -16256 * K)
+    p = synth.pack_int4
+    assert np.all(mm.gemm_i4(p(np.full((M, K), -8, np.int8)), p(np.full((N, K), -8, np.int8))) == 64 * K)
+    assert np.all(mm.gemm_i4(p(np.full((M, K), -8, np.int8)), p(np.full((N, K), 7, np.int8))) == -56 * K)
+    assert np.all(mm.gemm_i4(p(np.full((M, K), 7, np.int8)), p(np.full((K, 2 * N), -8, np.int8)),
+                             N=2 * N, rowb=True) == -56 * K)
+    # K = 0: the empty sum
+    assert np.all(mm.gemm_i8(np.ones((M, 16), np.int8), np.ones((N, 16), np.int8), K=0) == 0)
+    R, S = mm.gemm_f16(np.ones((M, 16), np.float16), np.ones((N, 16), np.float16), K=0)
+    assert R.shape == (M, N) and np.all(R == 0) and np.all(S == 0)
+
+
+def pin_matmul_brute_force(mm):
+    """Exact Python evaluation on tiny shapes, padding filled with poison, both B layouts."""
+    rng = np.random.default_rng(23)
+    for (m, n, k) in [(m, n, k) for m in (1, 2, 5, 8) for n in (1, 3, 7) for k in (1, 2, 5, 8)]:
+        a8 = rng.integers(-128, 128, (m, k), dtype=np.int8)
+        b8 = rng.integers(-128, 128, (n, k), dtype=np.int8)
+        E, _ = _exact_eval("i8", a8, b8, k)
+        assert mm.gemm_i8(_padded(a8, k + 3, 127), _padded(b8, k + 5, -128), K=k).tolist() == E
+        b8r = np.vstack([_padded(np.ascontiguousarray(b8.T), n + 2, 127), np.full((2, n + 2), -128, np.int8)])
+        assert mm.gemm_i8(_padded(a8, k + 1, 127), b8r, K=k, N=n, rowb=True).tolist() == E
+        k4 = 2 * k
+        a4 = rng.integers(-8, 8, (m, k4), dtype=np.int8)
+        b4 = rng.integers(-8, 8, (n, k4), dtype=np.int8)
+        pa = _padded(synth.pack_int4(a4), k + 2, 0x77)
+        pb = _padded(synth.pack_int4(b4), k + 1, 0x88)
+        E4, _ = _exact_eval("i4", synth.pack_int4(a4), synth.pack_int4(b4), k4)
+        assert mm.gemm_i4(pa, pb, K=k4).tolist() == E4
+        if k4 > 2:   # odd K: the last byte's high nibble stays out
+            E4o, _ = _exact_eval("i4", synth.pack_int4(a4), synth.pack_int4(b4), k4 - 1)
+            assert mm.gemm_i4(pa, pb, K=k4 - 1).tolist() == E4o
+        n4 = 2 * n
+        b4r = rng.integers(-8, 8, (k, n4), dtype=np.int8)
+        a4k = rng.integers(-8, 8, (m, 2 * k), dtype=np.int8)
+        b4rp = np.vstack([_padded(synth.pack_int4(b4r), n + 2, 0x77), np.full((2, n + 2), 0x88, np.uint8)])
+        E4r = _exact_eval_rowb("i4", synth.pack_int4(a4k), synth.pack_int4(b4r), n4, k)[0]
+        got = mm.gemm_i4(_padded(synth.pack_int4(a4k), k + 1, 0x77), b4rp, K=k, N=n4, rowb=True)
+        assert got.tolist() == E4r
+        if n4 > 1:   # odd N: the last byte's high nibble stays out
+            got = mm.gemm_i4(_padded(synth.pack_int4(a4k), k + 1, 0x77), b4rp, K=k, N=n4 - 1, rowb=True)
+            assert got.tolist() == [row[:n4 - 1] for row in E4r]
+        ah = rng.uniform(-2, 2, (m, k)).astype(np.float16)
+        bh = rng.uniform(-2, 2, (n, k)).astype(np.float16)
+        Eh, Sh = _exact_eval("f16", ah, bh, k)
+        R, S = mm.gemm_f16(_padded(ah, k + 4, np.float16(np.nan)), _padded(bh, k + 2, np.float16(np.inf)), K=k)
+        bhr = np.vstack([_padded(np.ascontiguousarray(bh.T), n + 2, np.float16(np.inf)),
+                         np.full((1, n + 2), np.nan, np.float16)])
+        Rr, Sr = mm.gemm_f16(_padded(ah, k + 2, np.float16(np.nan)), bhr, K=k, N=n, rowb=True)
+        for i in range(m):
+            for j in range(n):
+                for RR, SS in ((R, S), (Rr, Sr)):
+                    assert abs(Fraction(RR[i, j]) - Eh[i][j]) <= Fraction(k, 2 ** 52) * Sh[i][j], ("f16", m, n, k)
+                    assert abs(Fraction(SS[i, j]) - Sh[i][j]) <= Fraction(k, 2 ** 52) * Sh[i][j]
+
+
+def pin_matmul_product_tables(mm):
+    v = np.arange(-128, 128, dtype=np.int8).reshape(256, 1)
+    assert np.array_equal(mm.gemm_i8(v, v), np.outer(v.astype(np.int64), v.astype(np.int64)))
+    w = np.arange(-8, 8, dtype=np.int8)
+    z = np.zeros(16, np.int8)
+    even = synth.pack_int4(np.stack([w, z], axis=1))
+    odd = synth.pack_int4(np.stack([z, w], axis=1))
+    outer = np.outer(w.astype(np.int64), w.astype(np.int64))
+    assert np.array_equal(mm.gemm_i4(even, even), outer)
+    assert np.array_equal(mm.gemm_i4(odd, odd), outer)
+    assert np.all(mm.gemm_i4(even, odd) == 0)
+    a = np.array([[0x8F]], np.uint8)   # (k0 = -1, k1 = -8)
+    b = np.array([[0x12]], np.uint8)   # (k0 = 2, k1 = 1)
+    assert mm.gemm_i4(a, b)[0, 0] == (-1) * 2 + (-8) * 1
+
+
+def pin_matmul_matches_triple_loop(mm):
+    """Against the pinned triple loop of oracle_gemm.c on multi-row random shapes."""
+    for prec, (M, N, K) in (("f16", (37, 45, 300)), ("i8", (40, 33, 517)), ("i4", (29, 50, 402))):
+        A, Bt = synth.operands(prec, M, N, K, 101, 102)
+        if prec == "f16":
+            R, S = oracle.gemm_f16(A, Bt, K=K)
+            for B, rowb in ((Bt, False), (np.ascontiguousarray(Bt.T), True)):
+                Rm, Sm = mm.gemm_f16(A, B, K=K, N=N, rowb=rowb)
+                assert np.all(np.abs(Rm - R) <= 2 * K * 2.0 ** -53 * S)
+                assert np.all(np.abs(Sm - S) <= 2 * K * 2.0 ** -53 * S)
+        elif prec == "i8":
+            C = oracle.gemm_i8(A, Bt, K=K)
+            assert np.array_equal(mm.gemm_i8(A, Bt, K=K), C)
+            assert np.array_equal(mm.gemm_i8(A, np.ascontiguousarray(Bt.T), K=K, N=N, rowb=True), C)
+        else:
+            C = oracle.gemm_i4(A, Bt, K=K)
+            assert np.array_equal(mm.gemm_i4(A, Bt, K=K), C)
+            Br = synth.pack_int4(np.ascontiguousarray(synth.unpack_int4(Bt)[:, :K].T))
+            assert np.array_equal(mm.gemm_i4(A, Br, K=K, N=N, rowb=True), C)
+
+
+MATMUL_PINS = [pin_matmul_lab, pin_matmul_closed_forms, pin_matmul_brute_force,
+               pin_matmul_product_tables, pin_matmul_matches_triple_loop]
+
+
 PINS = [pin_half_decoder, pin_mma_lab_f16, pin_mma_lab_integer, pin_closed_forms,
         pin_identities, pin_brute_force_tiny, pin_product_tables, pin_invariants,
         pin_half_rounding, pin_dequant, pin_rowb]
@@ -416,6 +565,12 @@ PINS = [pin_half_decoder, pin_mma_lab_f16, pin_mma_lab_integer, pin_closed_forms
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
 def test_pin(oracle_lib, pin):
     pin()
+
+
+@pytest.mark.parametrize("pin", MATMUL_PINS, ids=[p.__name__ for p in MATMUL_PINS])
+def test_matmul_pin(oracle_lib, pin):
+    import oracle.matmul
+    pin(oracle.matmul)
 
 
 def test_rejects_bad_arguments(oracle_lib):

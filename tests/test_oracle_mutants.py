@@ -79,3 +79,39 @@ def test_mutant_is_caught(tmp_path, source, name):
     finally:
         oracle._lib, oracle.LIBRARY = saved_lib, saved_path
     assert caught, f"no pin caught the planted mistake {name}"
+
+
+# Planted mistakes in a copy of oracle/matmul.py, the whole-product form; each
+# must make at least one of the MATMUL_PINS fail.
+MATMUL_MUTANTS = {
+    "nibble_order": ("nib[:, 0::2] = b & 0x0F\n    nib[:, 1::2] = b >> 4",
+                     "nib[:, 0::2] = b >> 4\n    nib[:, 1::2] = b & 0x0F"),
+    "no_sign_extend": ("nib = np.where(nib < 8, nib, nib - 16)", "nib = nib"),
+    "magnitude_signed": ("return a @ b, np.abs(a) @ np.abs(b)", "return a @ b, np.abs(a @ b)"),
+    "drop_last_k": ("        return x[:, :count]", "        return x[:, :max(count - 1, 0)]"),
+    "rowb_read_as_colmajor": ("        b = decode(B, N)[:K]\n", "        b = decode(B, K)[:N].T\n"),
+    "colmajor_read_as_rowb": ("        b = decode(B, K)[:N].T", "        b = decode(B, N)[:K]"),
+    "negated_sum": ("    return np.rint(a @ b).astype(np.int64)", "    return np.rint(-(a @ b)).astype(np.int64)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MATMUL_MUTANTS))
+def test_matmul_mutant_is_caught(tmp_path, name):
+    import importlib.util
+    import oracle.matmul
+    old, new = MATMUL_MUTANTS[name]
+    text = open(oracle.matmul.__file__).read()
+    assert old in text, f"mutation site for {name} no longer exists in oracle/matmul.py"
+    path = tmp_path / f"matmul_{name}.py"
+    path.write_text(text.replace(old, new))
+    spec = importlib.util.spec_from_file_location(f"matmul_mutant_{name}", path)
+    mutant = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mutant)
+    caught = []
+    for pin in pins.MATMUL_PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, ValueError):
+            # a mutant that makes a pin's shapes inconsistent is caught too
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"
