@@ -1,5 +1,5 @@
 """Helpers for the GPU parity tests: padded device operands, guarded outputs,
-sampled-entry and Freivalds checks against the oracle."""
+whole-output and sampled-entry checks against the oracle."""
 from __future__ import annotations
 
 import sys
@@ -7,6 +7,7 @@ import sys
 import numpy as np
 
 import oracle
+import oracle.matmul
 import synth
 
 F16_REL = 1e-3          # per-element bound |C - R| <= F16_REL * S
@@ -83,6 +84,24 @@ def oracle_full(prec, A, Bt, K):
     return oracle.gemm_i4(A, Bt, K=K)
 
 
+def oracle_whole(prec, A, B, K, N=None, rowb=False):
+    """The whole product from the oracle's matrix-product form (oracle/matmul.py):
+    (R, S) for FP16, exact int64 for INT8 / INT4."""
+    f = {"f16": oracle.matmul.gemm_f16, "i8": oracle.matmul.gemm_i8, "i4": oracle.matmul.gemm_i4}[prec]
+    return f(A, B, K=K, N=N, rowb=rowb)
+
+
+def check_whole(prec, A, B, K, C, what="", rowb=False):
+    """Every element of C against the oracle: within 1e-3 * S for FP16, bit-exact
+    for the integer paths."""
+    ref = oracle_whole(prec, A, B, K, N=C.shape[1], rowb=rowb)
+    if prec == "f16":
+        assert_f16_close(C, ref[0], ref[1], what)
+    else:
+        assert_int_equal(C, ref, what)
+    return ref
+
+
 def sample_positions(M: int, N: int, count: int, seed: int, tiles=(256, 128, 64, 32)):
     """Random positions plus every tile-edge row/column pair and the corners."""
     rng = np.random.default_rng(seed)
@@ -114,39 +133,3 @@ def check_sampled(prec, A, Bt, K, C, rows, cols, what=""):
         assert_int_equal(got, oracle.entries_i8(A, Bt, rows, cols, K=K), what)
     else:
         assert_int_equal(got, oracle.entries_i4(A, Bt, rows, cols, K=K), what)
-
-
-def freivalds_int(prec, A, Bt, K, C, seed, rounds=2):
-    """Exact integer check C x == A (B x) over the whole matrix (int64, no overflow for
-    |x| <= 2^20 at the sizes used here)."""
-    if prec == "i4":
-        Av = synth.unpack_int4(A)[:, :K].astype(np.int64)
-        Bv = synth.unpack_int4(Bt)[:, :K].astype(np.int64)
-    else:
-        Av = A[:, :K].astype(np.int64)
-        Bv = Bt[:, :K].astype(np.int64)
-    C64 = C.astype(np.int64)
-    rng = np.random.default_rng(seed)
-    for _ in range(rounds):
-        x = rng.integers(-(2 ** 20), 2 ** 20, C.shape[1], dtype=np.int64)
-        lhs = C64 @ x
-        rhs = Av @ (Bv.T @ x)
-        assert np.array_equal(lhs, rhs), f"Freivalds check failed ({prec})"
-
-
-def freivalds_f16(A, Bt, K, C, seed, rounds=2):
-    """Necessary condition of the per-element bound over the whole matrix:
-    for x in {-1, +1}^N, |C x - A (B x)| <= 1e-3 * |A| (|B| 1) + fp64 slack."""
-    Ad = A[:, :K].astype(np.float64)
-    Bd = Bt[:, :K].astype(np.float64)
-    Cd = C.astype(np.float64)
-    N = C.shape[1]
-    sum_s = np.abs(Ad) @ (np.abs(Bd).T @ np.ones(N))
-    bound = F16_REL * sum_s
-    # fp64 rounding of the three products: below (2N + K) unit roundoffs of sum_s
-    slack = (2 * N + K + 4) * 2.0 ** -52 * sum_s
-    rng = np.random.default_rng(seed)
-    for _ in range(rounds):
-        x = rng.choice([-1.0, 1.0], size=N)
-        diff = np.abs(Cd @ x - Ad @ (Bd.T @ x))
-        assert np.all(diff <= bound + slack), f"f16 row-sum bound violated, worst excess {np.max(diff - bound)}"

@@ -275,14 +275,14 @@ def test_unit_scales_match_plain_gemm(pd, dev, prec):
 
 # ---------------------------------------------------------------------------
 # full size, in the launch the benchmark times (prepared, library tile choice):
-# sampled entries against the oracle, bit for bit
+# every element against the oracle, bit for bit
 
 @pytest.mark.parametrize("prec", INT_PRECS)
 @pytest.mark.parametrize("out", OUTS)
 @pytest.mark.parametrize("M", [16, 64, 8192])
-def test_full_size_sampled(pd, dev, prec, out, M):
+def test_full_size(pd, dev, prec, out, M):
     """M x 8192 x 8192 (the first M rows of the 8192^3 operands) in the launch the
-    benchmark times; sampled entries bit for bit."""
+    benchmark times; every element bit for bit."""
     n = 8192
     sa_seed = synth.config_seed(5, n, synth.OPERAND_A)
     sb_seed = synth.config_seed(5, n, synth.OPERAND_B)
@@ -297,7 +297,14 @@ def test_full_size_sampled(pd, dev, prec, out, M):
     torch.cuda.synchronize()
     C = outv.cpu().numpy()
     del Ad, Bd, outv
-    rows, cols = gu.sample_positions(M, n, 1024, seed=n + M)
+    # every element: exact sums from the oracle's matrix-product form, then the
+    # oracle's epilogue
+    S = gu.oracle_whole(prec, A, Bt, n)
+    want = oracle.dequant(S, sa, sb, half_out=(out == "f16"))
+    assert_bits_equal(C, want, f"{prec}->{out} {M}x{n}x{n}")
+    del S, want
+    # and sampled entries with the sums from the triple loop
+    rows, cols = gu.sample_positions(M, n, 512, seed=n + M)
     S = oracle.entries_i8(A, Bt, rows, cols) if prec == "i8" else oracle.entries_i4(A, Bt, rows, cols)
     want = oracle.dequant_entries(S, sa[rows], sb[cols], half_out=(out == "f16"))
     assert_bits_equal(C[rows, cols], want, f"{prec}->{out} {M}x{n}x{n} sampled")

@@ -188,8 +188,8 @@ def test_k_zero(pd, dev, prec):
 @pytest.mark.parametrize("prec", PRECS)
 @pytest.mark.parametrize("n", [2048, 8192])
 def test_full_size_matches_column_major(pd, dev, prec, n):
-    """The workload shapes with B row-major: sampled entries against the oracle, a
-    whole-matrix Freivalds check, and bit equality with the column-major kernel."""
+    """The workload shapes with B row-major: every element against the oracle, sampled
+    entries against its triple loop, and bit equality with the column-major kernel."""
     seed_a = synth.config_seed(6, n, synth.OPERAND_A)
     gu.note(f"[case] rowb {prec} {n}^3 seed {seed_a:#x}")
     A, B, Bvals = rowb_operands(prec, n, n, n, seed_a)
@@ -204,13 +204,12 @@ def test_full_size_matches_column_major(pd, dev, prec, n):
     assert torch.equal(Cr.view(torch.int32), Cc.view(torch.int32)), "row-major B differs from column-major B"
     C = Cr.cpu().numpy()
     del Ad, Bd, Btd, Cr, Cc
-    rows, cols = gu.sample_positions(n, n, 1024, seed=n + 7)
+    gu.check_whole(prec, A, B, n, C, f"rowb {prec} {n}", rowb=True)
+    rows, cols = gu.sample_positions(n, n, 512, seed=n + 7)
     got = C[rows, cols]
     if prec == "f16":
         R, S = oracle.entries_f16_rowb(A, B, rows, cols)
         gu.assert_f16_close(got, R, S, f"rowb {prec} {n}")
-        gu.freivalds_f16(A, Bt, n, C, seed=n)
     else:
         ref = (oracle.entries_i8_rowb if prec == "i8" else oracle.entries_i4_rowb)(A, B, rows, cols)
         gu.assert_int_equal(got, ref, f"rowb {prec} {n}")
-        gu.freivalds_int(prec, A, Bt, n, C, seed=n)
