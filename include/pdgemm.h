@@ -61,12 +61,25 @@
  * it is enqueued.  Entry points are thread-safe and keep no state between
  * calls.
  *
- * Errors: 0 on success.  Negative values are argument errors, found on the
- * host before any HIP call is made, with nothing enqueued.  Positive values
- * are hipError_t codes from the launch.  When the environment variable
- * PDGEMM_SYNC_CHECK is set to 1 at the first call, every call also
- * synchronizes its stream and returns any execution error.  The library
- * never aborts or exits the process.
+ * Errors.  The convention follows "Chapter 5 · The Toolchain", Section 5.3
+ * "Error handling that actually works" (the GPU programming book's toolchain
+ * chapter): every call that can fail reports it, and because a launch is
+ * asynchronous, a fault inside a kernel only shows at a later synchronizing
+ * call, so catching it at its source takes a check after the launch plus a
+ * synchronize, which serializes and is kept out of release and timing paths.
+ * Here:
+ *   - 0 on success;
+ *   - negative values (PDGEMM_E* below) are argument errors, found on the
+ *     host before any HIP call is made, with nothing enqueued;
+ *   - positive values are hipError_t codes of the launch itself (the
+ *     launch-time check of that section);
+ *   - with the environment variable PDGEMM_SYNC_CHECK set to 1 at the first
+ *     call, every call also synchronizes its stream and returns any execution
+ *     error (the section's debug-build synchronize; off by default, since it
+ *     serializes the caller's stream);
+ *   - pdgemm_strerror() turns any of these codes into a message.
+ * That section's checking macro prints and exits the process; a library must
+ * not, so this one only returns codes and never aborts or exits.
  * ---------------------------------------------------------------------------
  */
 #ifndef PDGEMM_H
@@ -78,15 +91,17 @@
 extern "C" {
 #endif
 
+/* Return codes (error convention: "Chapter 5 · The Toolchain", Section 5.3;
+ * see the file header). */
 #define PDGEMM_OK 0
 #define PDGEMM_EINVAL_DIM (-1)  /* M, N or K negative or too large (K > 2^30, over 2^32 work-items), or gemm_i4 K > 131071 */
 #define PDGEMM_EINVAL_LD (-2)   /* lda < K, ldb < K (row-major B: ldb < N), ldc < N, or a row above 4 MiB */
 #define PDGEMM_ENULL (-3)       /* NULL pointer for an operand with nonzero extent */
 #define PDGEMM_EINVAL_I4 (-4)   /* gemm_i4: K, lda or ldb odd */
 #define PDGEMM_EALIGN (-5)      /* a pointer or leading dimension breaks the alignment rules */
-#define PDGEMM_EINVAL_CFG (-6)  /* unknown precision or tile configuration, dequantizing FP16, or a
-                                   configuration without the variant (row-major B on a K-split tile);
-                                   reported before any other check */
+#define PDGEMM_EINVAL_CFG (-6)  /* unknown precision or tile configuration, or a dequantizing
+                                   epilogue for FP16; reported before any other check.  Every
+                                   configuration, the K-split ones included, serves both B layouts */
 
 #define PDGEMM_I4_MAX_K 131071
 
@@ -181,10 +196,15 @@ int pdgemm_pick_config(int prec, int64_t M, int64_t N, int64_t K);
 int pdgemm_config_info(int cfg, int *block_m, int *block_n, int *wave_m, int *wave_n,
                        int *threads);
 
-/* Static message for a return code (never NULL). */
+/* Static message for a return code (never NULL): the PDGEMM_E* codes above,
+ * or hipGetErrorString() for a positive hipError_t.  Part of the error
+ * convention of "Chapter 5 · The Toolchain", Section 5.3 (every error made
+ * readable where it is reported). */
 const char *pdgemm_strerror(int code);
 
-/* Library version as major*10000 + minor*100 + patch. */
+/* Library version as major*10000 + minor*100 + patch.  No passage of the
+ * pages defines a version query; it exists so that a caller can check which
+ * build it loaded. */
 int pdgemm_version(void);
 
 #ifdef __cplusplus
