@@ -351,8 +351,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     const int64_t b_row_valid = ((int64_t)min(BN, N - n0) * (P == kF16 ? 16 : (P == kI8 ? 8 : 4)) + 7) / 8;
     const int64_t b_end = BR == kBRow ? (int64_t)(K - 1) * args.ldb_bytes + ((b_row_valid + 15) & ~int64_t(15))
                                       : (int64_t)(min(BN, N - n0) - 1) * args.ldb_bytes + valid16;
-    // row-major B: a K tile is KS slices of kKRows rows of B
+    // row-major B: a K tile is KS slices of kKRows rows of B.  A wave's
+    // slice is addressed from a base of its own (its first row of B), so
+    // that a lane's 32-bit offset spans at most kKRows rows (at most 512 MiB
+    // with rows of 4 MiB) whatever the slice.
     const int64_t b_tile_bytes = BR == kBRow ? (int64_t)KS * RB::kKRows * args.ldb_bytes : kTileBytes;
+    const int64_t b_slice_rows = BR == kBRow ? (int64_t)slice * RB::kKRows * args.ldb_bytes : 0;
     const int lrow = lane >> 2;              // row within the 16-row group
     const int lpos = lane & 3;               // LDS position written by this lane
     uint32_t voff[kDma];
@@ -373,7 +377,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
             const int f = (cr - BM) * kChunks + lpos;
             const int krow = f / kCpr;
             const int gchunk = (f % kCpr) ^ bswizzle<P, BN>(krow);
-            voff[j] = (uint32_t)((slice * RB::kKRows + krow) * args.ldb_bytes) + gchunk * 16;
+            voff[j] = (uint32_t)(krow * args.ldb_bytes) + gchunk * 16;
         }
     }
 
@@ -382,11 +386,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
         const bool live = t < n_tiles;
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(a_base + kb), (short)0, live ? a_end - kb : 0, kRsrcWord3);
-        const int64_t bt = (int64_t)t * b_tile_bytes;
-        // a row-major tile spans KS * kKRows rows of B; the range never
-        // exceeds it (nor 2^31 - 1: every offset a lane forms is below that)
+        const int64_t bt = (int64_t)t * b_tile_bytes + b_slice_rows;
+        // a row-major slice spans kKRows rows of B; the range never exceeds
+        // it (nor 2^31 - 1: every offset a lane forms is below that), and is
+        // zero for a slice that starts past row K - 1
         const int b_range = !live ? 0
-                            : BR == kBRow ? (int)min(min(b_end - bt, b_tile_bytes), (int64_t)INT32_MAX)
+                            : BR == kBRow ? (int)max(min(min(b_end - bt, (int64_t)RB::kKRows * args.ldb_bytes),
+                                                         (int64_t)INT32_MAX), (int64_t)0)
                                           : (int)(b_end - bt);
         const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(b_base + bt), (short)0, b_range, kRsrcWord3);
@@ -623,19 +629,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
                 const int f = (blk - BM / 8) * 64 + lane;
                 const int krow = f / kCpr;
                 const int gchunk = (f % kCpr) ^ bswizzle<P, BN>(krow);
-                voffl[j] = (uint32_t)((slice * 2 * RB::kKRows + krow) * args.ldb_bytes) + gchunk * 16;
+                voffl[j] = (uint32_t)(krow * args.ldb_bytes) + gchunk * 16;
             }
         }
-        // row-major B: a stage spans KS * 2 * kKRows rows of B
+        // row-major B: a stage spans KS * 2 * kKRows rows of B, a wave's
+        // slice 2 * kKRows of them, from a base of its own (as above)
         const int64_t b_stage_bytes = BR == kBRow ? (int64_t)KS * 2 * RB::kKRows * args.ldb_bytes : kStageK;
+        const int64_t b_slice_bytes = (int64_t)2 * RB::kKRows * args.ldb_bytes;
         auto stage_l = [&](int st, LStage &buf) __attribute__((always_inline)) {
             const int kb = st * kStageK;
             const bool live = st < n_st;
             const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)(a_base + kb), (short)0, live ? a_end - kb : 0, kRsrcWord3);
-            const int64_t bt = (int64_t)st * b_stage_bytes;
+            const int64_t bt = (int64_t)st * b_stage_bytes + (BR == kBRow ? slice * b_slice_bytes : 0);
             const int b_range = !live ? 0
-                                : BR == kBRow ? (int)min(min(b_end - bt, b_stage_bytes), (int64_t)INT32_MAX)
+                                : BR == kBRow ? (int)max(min(min(b_end - bt, b_slice_bytes), (int64_t)INT32_MAX),
+                                                         (int64_t)0)
                                               : (int)(b_end - bt);
             const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)(b_base + bt), (short)0, b_range, kRsrcWord3);
@@ -1114,7 +1123,7 @@ int launch(int prec, int cfg, int epi, int br, int64_t M, int64_t N, int64_t K, 
            void *C, int64_t ldc, void *stream) {
     if (prec < 0 || prec > 2 || cfg < 0 || cfg >= kNumConfigs) return PDGEMM_EINVAL_CFG;
     if (epi != kRaw && prec == kF16) return PDGEMM_EINVAL_CFG;
-    const void *fn = kernel_ptr(prec, cfg, epi, br);   // null: no such kernel (e.g. K split, row-major B)
+    const void *fn = kernel_ptr(prec, cfg, epi, br);   // null: no such kernel (dequantizing row-major B)
     if (!fn) return PDGEMM_EINVAL_CFG;
     int rc = validate(prec, epi, br, M, N, K, A, lda, B, ldb, C, ldc, scale_a, scale_b);
     if (rc != PDGEMM_OK) return rc;

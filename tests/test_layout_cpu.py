@@ -269,3 +269,45 @@ def test_rowmajor_b_line_layout(prec, cfg):
                             k, n = krow, (g * 16 + inb) * 8 // bits + p
                             want_k = s * steprows + half * (steprows // 2) + r * per_read + e
                             assert (k, n) == (want_k, wn0 + jj * 32 + lane % 32), (prec, cfg, lane, r, e)
+
+
+# Tiles (block rows, block columns, K split, whole-line stages) as the kernel's
+# configuration table defines them; the 32 x 32 K-split tile stages 64-byte K
+# tiles, every other tile whole 128-byte lines.
+TILES = [(256, 256, 1, True), (128, 128, 1, True), (64, 64, 1, True), (32, 32, 4, False),
+         (256, 128, 1, True), (128, 64, 1, True), (64, 32, 4, True), (128, 128, 1, True)]
+MAX_ROW_BYTES = 1 << 22
+
+
+def test_tile_table_matches_library():
+    import precision_dense_gemm_amd as pd
+    assert pd.num_configs() == len(TILES)
+    for cfg, (bm, bn, ks, _) in enumerate(TILES):
+        info = pd.config_info(cfg)
+        assert (info["block_m"], info["block_n"]) == (bm, bn)
+        assert info["threads"] == (bm // info["wave_m"]) * (bn // info["wave_n"]) * ks * 64
+
+
+@pytest.mark.parametrize("prec", ["f16", "i8", "i4"])
+@pytest.mark.parametrize("cfg", range(len(TILES)))
+def test_operand_offsets_fit_32_bits(prec, cfg):
+    # Every DMA lane forms a 32-bit offset from the base of a buffer resource
+    # whose range is capped at 2^31 - 1 bytes: an offset beyond it would read
+    # zeros, one beyond 2^32 would wrap.  At the largest rows the library
+    # accepts (4 MiB), each resource must span fewer rows than 2^31 bytes hold.
+    # A and a column-major B: one resource per tile of rows (BM or BN rows),
+    # offsets up to (rows - 1) * ld + the last 16-byte chunk of a stage.
+    # Row-major B: one resource per wave slice of a stage (K-split waves get a
+    # base of their own), spanning the K rows of that slice: krows (64-byte
+    # stages) or 2 * krows (whole lines).
+    bm, bn, ks, line = TILES[cfg]
+    krows = ROWB[prec][0]
+    ld = MAX_ROW_BYTES
+    stage_k = (128 if line else 64) * ks     # bytes of K per row per stage
+    limit = 2 ** 31 - 1
+    for rows in (bm, bn):
+        assert (rows - 1) * ld + stage_k <= limit
+    slice_rows = krows * (2 if line else 1)
+    cpr_bytes = ld                            # a row of B: every chunk of it may be addressed
+    assert (slice_rows - 1) * ld + cpr_bytes <= limit + 1
+    assert slice_rows * ld <= 2 ** 30, "a slice of a row-major B stage spans at most 1 GiB"

@@ -8,7 +8,8 @@
   K = 131072 (every partial sum an integer below 2^24, so C = K exactly).
 * The largest leading dimensions: rows of 4 MiB for A, B and C, so that a
   256-row tile spans 1 GiB of offsets, checked against the oracle on ragged
-  M, N and K.
+  M, N and K; and rows of 4 MiB for a row-major B on the K-split tiles, whose
+  stages span up to 1024 rows of B.
 
 Operands' padding past K holds poison, and every case prints its name before
 it touches the GPU.
@@ -133,3 +134,51 @@ def test_largest_leading_dimensions(pd, dev, prec, cfg):
     else:
         ref = oracle.gemm_i8(A, Bt) if prec == "i8" else oracle.gemm_i4(A, Bt, K)
         gu.assert_int_equal(C, ref, f"largest ld {prec} cfg{cfg}")
+
+
+@pytest.mark.parametrize("prec", ["f16", "i8", "i4"])
+@pytest.mark.parametrize("cfg", [0, 3, 6])
+def test_largest_leading_dimension_row_major_b(pd, dev, prec, cfg):
+    # B row-major with rows of 4 MiB, on the 256 x 256 tile (0) and on the K-split
+    # tiles (3: 32 x 32, 6: 64 x 32), whose waves each stage their own slice of
+    # rows of B; K reaches the last slice of a stage (a 64 x 32 INT4 stage spans
+    # 1024 rows of B, 4 GiB at this row size)
+    M, N, K = 50, 70, 1000
+    ld = LD[prec]
+    ldc = MAX_ROW_BYTES // 4
+    gu.note(f"[case] largest ldb row-major B {prec} cfg={cfg} ldb={ld} ldc={ldc} K={K}")
+    if prec == "i4":
+        A = synth.pack_int4(synth.int4_values(M, K, 91))
+        B = synth.pack_int4(np.ascontiguousarray(synth.int4_values(N, K, 92).T))   # (K, N/2)
+        cols_a, cols_b, ld_cols = K // 2, N // 2, ld // 2
+    else:
+        A, Bt = synth.operands(prec, M, N, K, 91, 92)
+        B = np.ascontiguousarray(Bt.T)                                           # (K, N)
+        cols_a, cols_b, ld_cols = K, N, ld
+    dt = {"f16": torch.float16, "i8": torch.int8, "i4": torch.uint8}[prec]
+    poison = {"f16": float("nan"), "i8": 127, "i4": 0x77}[prec]
+    Ad = torch.full((M, gu.round_up(cols_a, 16) + 16), poison, dtype=dt, device=dev)
+    Ad[:, :cols_a] = torch.from_numpy(A).to(dev)
+    # two extra rows past K, all poison
+    Bd = torch.full((K + 2, ld_cols), poison, dtype=dt, device=dev)
+    Bd[:K, :cols_b] = torch.from_numpy(B).to(dev)
+    out_dtype = torch.float32 if prec == "f16" else torch.int32
+    Cbuf = torch.zeros((M, ldc), dtype=out_dtype, device=dev)
+    out = Cbuf[:, :N]
+    Bv = Bd[:K, :cols_b]
+    if prec == "f16":
+        pd.gemm_f16_rowb(Ad[:, :cols_a], Bv, out=out, cfg=cfg)
+    elif prec == "i8":
+        pd.gemm_i8_rowb(Ad[:, :cols_a], Bv, out=out, cfg=cfg)
+    else:
+        pd.gemm_i4_rowb(Ad[:, :cols_a], Bv, K, N, out=out, cfg=cfg)
+    torch.cuda.synchronize()
+    C = out.cpu().numpy()
+    assert torch.count_nonzero(Cbuf[:, N:]) == 0, "stores past column N"
+    del Ad, Bd, Bv, Cbuf
+    if prec == "f16":
+        R, S = oracle.gemm_f16_rowb(A, B, N=N, K=K)
+        gu.assert_f16_close(C, R, S, f"largest ldb rowb {prec} cfg{cfg}")
+    else:
+        ref = (oracle.gemm_i8_rowb if prec == "i8" else oracle.gemm_i4_rowb)(A, B, N=N, K=K)
+        gu.assert_int_equal(C, ref, f"largest ldb rowb {prec} cfg{cfg}")
