@@ -3,24 +3,32 @@
 One step is one pass of the precision sweep: C = A*B at N = 512, 1024, 2048,
 4096 and 8192 (square) for FP16 (fp32 accumulate), INT8 and packed INT4
 (int32 accumulate), 15 GEMMs on seeded synthetic inputs that are resident in
-HBM before the timed region starts.  The JSON line reports:
+HBM before the timed region starts.  Two JSON lines go to stdout, the
+headline last:
 
+headline line
   value         whole-step throughput in TOPS (2*M*N*K per GEMM, summed over
                 the sweep, divided by the wall time of a step)
-  per_gemm      per (precision, N): mean (also median and minimum) kernel time from
-                HIP events on the launch stream around every GEMM of K steps run
-                right after the timed ones (the timed steps carry events around
-                the dominant GEMM only), TOPS, fraction of peak; and
-                the same GEMM timed over back-to-back launches after the steps
-                (R launches captured in one HIP graph, median of 3 replays, so
-                that host launch cost is not timed); for N <= 2048 also cold:
-                each launch after a 512 MiB fill that evicts L2 and MALL, so
-                its operands come from HBM (median of 10)
+  per_gemm      per (precision, N): mean kernel time from HIP events on the
+                launch stream around every GEMM of K steps run right after the
+                timed ones (the timed steps carry events around the dominant
+                GEMM only), TOPS and fraction of peak; the same GEMM back to
+                back (R launches captured in one HIP graph, median of 3
+                replays, so that host launch cost is not timed); for N <= 2048
+                also cold (each launch after a 512 MiB fill that evicts L2 and
+                MALL, median of 10); and its sampled parity flag
+  c3            (outside the step) the FP16 8192^3 GEMM on N(0,1)/sqrt(K)
+                operands, timed between the sweep's other GEMMs and back to back
   roofline      the GEMM that takes the largest share of a step, timed by its
                 HIP events inside the timed steps, against the MFMA peak of its
                 own precision
   cpu_baseline  the CPU oracle (plain triple loop) timed on a row sample of
-                every GEMM of the sweep and scaled to whole GEMMs
+                every GEMM of the sweep and scaled to whole GEMMs, with the
+                host CPU model
+
+detail line ("kind": "bench_detail"; also written to --detail PATH)
+  per_gemm      medians and minima of the in-step times, HBM rates, the
+                pages' L4 figures as context
   dequant       (outside the step) the INT8 / INT4 GEMMs at N = 8192 with the
                 dequantizing epilogue, ((float)S * scale_a[i]) * scale_b[j]
                 rounded to binary16, timed back to back alternately with the
@@ -64,6 +72,7 @@ PEAK = {"f16": 2500.0, "i8": 5000.0, "i4": 5000.0}
 HBM_PEAK_GBS = 8000.0
 IN_BYTES = {"f16": 2.0, "i8": 1.0, "i4": 0.5}
 SWEEP_CFG_ID = 4  # seeds of the sweep workload: (cfg_id << 32) ^ (N << 8) ^ operand
+C3_CFG_ID, C3_N = 3, 8192   # FP16 8192^3 on N(0,1)/sqrt(K) operands, seeded as workload 3
 # the pages' own durations for these GEMMs on an NVIDIA L4 (ms; best kernel per
 # precision and size, Table I-c), reported as context only
 L4_MS = {
@@ -96,6 +105,10 @@ def parse():
                     help="skip the non-square (small M) measurement")
     ap.add_argument("--no-layout", action="store_true",
                     help="skip the row-major-B measurement")
+    ap.add_argument("--no-c3", action="store_true",
+                    help="skip the FP16 8192^3 N(0,1)/sqrt(K) workload")
+    ap.add_argument("--detail", metavar="PATH",
+                    help="also write the bench_detail JSON line to PATH")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of C per GEMM for the CPU baseline (default 192)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -198,6 +211,18 @@ def sample_power(step, ms_per_step):
         "temp_hotspot_c_max": float(max(temps)) if temps else None,
         "note": "amdsmi metrics refresh about once a second; samples from inside the load only",
     }
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo, or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def gemm_ops(n):
@@ -308,6 +333,19 @@ def main():
         host[(prec, n)] = (A, Bt)
         work.append((prec, n, Ad, Bd, C))
         log(f"[bench] inputs {prec} N={n} ready in {time.time() - t0:.1f}s")
+
+    # config c3: the FP16 8192^3 GEMM on N(0,1)/sqrt(K) operands (its own
+    # seeds), timed beside the sweep's uniform FP16 8192 entry (outside the step)
+    c3 = None
+    if not args.case and not args.no_c3:
+        t0 = time.time()
+        n3 = C3_N
+        sa = synth.config_seed(C3_CFG_ID, n3, synth.OPERAND_A)
+        sb = synth.config_seed(C3_CFG_ID, n3, synth.OPERAND_B)
+        A3, B3 = synth.operands("f16", n3, n3, n3, sa, sb, dist="normal")
+        c3 = (torch.from_numpy(A3).to(dev), torch.from_numpy(B3).to(dev),
+              torch.empty((n3, n3), dtype=torch.float32, device=dev), A3, B3)
+        log(f"[bench] inputs c3 f16 N={n3} N(0,1)/sqrt(K) ready in {time.time() - t0:.1f}s")
 
     # one prepared launcher per GEMM: arguments are checked and marshalled
     # once, so host time per launch stays far below the smallest kernel
@@ -439,6 +477,45 @@ def main():
                 times.append(s0.elapsed_time(e0))
             cold[(prec, n)] = float(np.median(times))
         del scrub
+
+    # config c3 (outside the step): events around each of `steps` launches
+    # separated by the sweep's other GEMMs (as inside a step), and back to back
+    c3_entry = None
+    if c3 is not None:
+        A3d, B3d, C3d, A3, B3 = c3
+        go3 = pd.prepare("f16", A3d, B3d, C3d, K=C3_N)
+        torch.cuda.synchronize()
+        if not args.no_parity:
+            import oracle
+            rng = np.random.default_rng(C3_N + 3)
+            rows, cols = rng.integers(0, C3_N, 256), rng.integers(0, C3_N, 256)
+            R, S = oracle.entries_f16(A3, B3, rows, cols)
+            got = C3d.cpu().numpy()[rows, cols]
+            parity["c3"] = bool(np.all(np.abs(got.astype(np.float64) - R) <= 1e-3 * S))
+            log(f"[bench] parity c3: {'ok' if parity['c3'] else 'FAIL'}")
+        times = []
+        for _ in range(args.steps):
+            for w in work:
+                if (w[0], w[1]) != ("f16", 8192):
+                    launch(*w)
+            s0 = torch.cuda.Event(enable_timing=True)
+            e0 = torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            go3()
+            e0.record(stream)
+            times.append((s0, e0))
+        torch.cuda.synchronize()
+        ms3 = float(np.mean([a.elapsed_time(b) for a, b in times]))
+        ms3_b = time_b2b(lambda: pd.prepare("f16", A3d, B3d, C3d, K=C3_N), ms3)
+        tops3 = gemm_ops(C3_N) / (ms3 * 1e-3) / 1e12
+        tops3_b = gemm_ops(C3_N) / (ms3_b * 1e-3) / 1e12
+        c3_entry = {"workload": f"f16 {C3_N}^3, N(0,1)/sqrt(K)", "ms": round(ms3, 5), "tops": round(tops3, 1),
+                    "frac": round(tops3 / PEAK["f16"], 4), "ms_b2b": round(ms3_b, 5),
+                    "tops_b2b": round(tops3_b, 1), "frac_b2b": round(tops3_b / PEAK["f16"], 4)}
+        if "c3" in parity:
+            c3_entry["parity"] = parity["c3"]
+        log(f"[bench] c3: {ms3:.4f} ms in sweep order, {ms3_b:.4f} ms back to back")
+        del times
 
     b2b = {}
     for w in work:
@@ -599,7 +676,7 @@ def main():
                     f"({entry['roofline']['bound']} {entry['roofline']['frac']:.3f})")
                 del Cm
 
-    per = {}
+    per = {}      # full per-GEMM detail (printed on the detail line)
     for (prec, n), pairs in ev.items():
         times = [s.elapsed_time(e) for s, e in pairs]
         ms = float(np.mean(times)) if times else float("nan")
@@ -671,6 +748,8 @@ def main():
             "value": round(step_ops / total_s / 1e12, 6),
             "unit": "TOPS",
             "cores": threads,
+            "cpu_model": cpu_model(),
+            "host_cpus": os.cpu_count(),
             "kind": "oracle",
             "sample": f"first {rows} rows of C for each of the {len(work)} GEMMs "
                       f"({sampled_ops / 1e9:.1f} GOP), time scaled by N/{rows} per GEMM",
@@ -683,6 +762,33 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log("[bench] calibration copy: 3 x 1 GiB device-to-device")
+
+    # the headline line carries the metric for every GEMM of the sweep in a
+    # compact form: in-step and back-to-back ms, TOPS, fraction of peak
+    compact = {}
+    for key, e in per.items():
+        c = {"ms": e["ms"], "tops": round(e["tops"], 1), "frac": e["frac_of_peak"],
+             "ms_b2b": e["ms_back_to_back"], "tops_b2b": round(e["tops_back_to_back"], 1),
+             "frac_b2b": round(e["tops_back_to_back"] / PEAK[key.split(":")[0]], 4)}
+        if "ms_cold" in e:
+            c["ms_cold"] = e["ms_cold"]
+        if "parity" in e:
+            c["parity"] = e["parity"]
+        compact[key] = c
+
+    detail = {
+        "kind": "bench_detail",
+        "per_gemm": per,
+        "dequant": dequant or None,
+        "layout": layout or None,
+        "shapes": shapes or None,
+        "telemetry": telemetry,
+    }
+    detail_text = json.dumps(detail)
+    if args.detail:
+        with open(args.detail, "w") as f:
+            f.write(detail_text + "\n")
+    print(detail_text, flush=True)
 
     out = {
         "metric": METRIC,
@@ -703,13 +809,12 @@ def main():
             "gemms_per_step": len(work),
             "layout": "A row-major, B column-major, C row-major",
         },
-        "per_gemm": per,
+        "per_gemm": compact,
+        "c3": c3_entry,
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "dequant": dequant or None,
-        "layout": layout or None,
-        "shapes": shapes or None,
-        "telemetry": telemetry,
+        "detail": "per-GEMM medians and minima, HBM rates, the dequantizing epilogue, row-major B, "
+                  "non-square shapes and power telemetry are on the preceding bench_detail line",
     }
     print(json.dumps(out), flush=True)
     if parity and not all(parity.values()):
