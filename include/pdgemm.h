@@ -103,6 +103,9 @@ extern "C" {
                                    epilogue for FP16; reported before any other check.  Every
                                    configuration, the K-split ones included, serves both B layouts */
 
+#define PDGEMM_EWORKSPACE (-7)  /* *_ws entry points: workspace smaller than pdgemm_i4_workspace_size(),
+                                   a negative size, or a workspace not 16-byte aligned */
+
 #define PDGEMM_I4_MAX_K 131071
 
 /* FP16 inputs (IEEE binary16 bit patterns), fp32 accumulation, fp32 output. */
@@ -160,6 +163,58 @@ int gemm_i8_rowb(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
                  const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream);
 int gemm_i4_rowb(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
                  const uint8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream);
+
+/* INT4 GEMM on the FP6 matrix cores, with a caller-provided workspace.
+ *
+ * The same operation, layouts, results (bit for bit) and errors as gemm_i4,
+ * gemm_i4_rowb and gemm_i4_dequant.  gfx950 has no signed 4-bit MFMA; the
+ * entry points above run INT4 on the INT8 MFMA as two nibble planes, two
+ * MFMAs per 64 values of K.  These run it on the FP6 MFMA
+ * (v_mfma_scale_f32_32x32x64_f8f6f4, about twice the INT8 MFMA rate), one
+ * MFMA per 64 values: every INT4 value v is exact as the e2m3 value v / 8,
+ * block scales of 2^3 on both operands make each product the integer a * b,
+ * and the fp32 accumulators hold exact integers (|C| <= 64 K < 2^24).  A
+ * pre-pass converts A and B into that format once, into the workspace
+ * (3/4 of a byte per value, in 32-row x 128-value units; B row-major is
+ * transposed there), and the GEMM reads the workspace.  This replaces the
+ * paper's native m16n8k64 .s4 MMA ("Hand-Written PTX Tensor-Core GEMM
+ * Kernels ...", Listing 2, Section IV-C), which has no gfx950 counterpart.
+ *
+ * pdgemm_i4_workspace_size() gives the bytes a shape needs, or 0 where the
+ * entry points run the INT8-MFMA kernels instead (shapes of few tiles, where
+ * the pre-pass would not pay; the workspace may then be NULL).  The
+ * workspace is device memory owned by the caller, 16-byte aligned, not
+ * overlapping A, B, C or the scales; its contents on return are undefined.
+ * Calls that share a workspace must not run concurrently.  Both kernels are
+ * enqueued on `stream`; nothing is allocated or synchronized.  A workspace
+ * that is NULL (with a nonzero size needed) returns PDGEMM_ENULL, one that
+ * is too small or misaligned PDGEMM_EWORKSPACE. */
+int64_t pdgemm_i4_workspace_size(int64_t M, int64_t N, int64_t K);
+int gemm_i4_ws(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+               const uint8_t *B, int64_t ldb, int32_t *C, int64_t ldc,
+               void *workspace, int64_t workspace_bytes, void *stream);
+int gemm_i4_rowb_ws(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+                    const uint8_t *B, int64_t ldb, int32_t *C, int64_t ldc,
+                    void *workspace, int64_t workspace_bytes, void *stream);
+int gemm_i4_dequant_ws(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+                       const uint8_t *B, int64_t ldb, const float *scale_a,
+                       const float *scale_b, void *C, int64_t ldc, int out_f16,
+                       void *workspace, int64_t workspace_bytes, void *stream);
+
+/* The FP6 path with an explicit tile configuration (0 <= cfg <
+ * pdgemm_i4_f6_num_configs()), whatever the shape: B column-major or (with
+ * b_rowmajor) row-major; with scale_a and scale_b non-NULL the dequantizing
+ * epilogue (C fp32, or binary16 with out_f16), else int32 C.  The workspace
+ * must hold what pdgemm_i4_f6_workspace_bytes() gives.  pdgemm_i4_f6_pick()
+ * is the configuration the *_ws entry points take for a shape (-1: the
+ * INT8-MFMA kernels). */
+int pdgemm_i4_f6_cfg(int cfg, int b_rowmajor, int64_t M, int64_t N, int64_t K,
+                     const void *A, int64_t lda, const void *B, int64_t ldb,
+                     const float *scale_a, const float *scale_b, void *C, int64_t ldc,
+                     int out_f16, void *workspace, int64_t workspace_bytes, void *stream);
+int pdgemm_i4_f6_num_configs(void);
+int pdgemm_i4_f6_pick(int64_t M, int64_t N, int64_t K);
+int64_t pdgemm_i4_f6_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Precision ids and tile configurations, for the calls below. */
 #define PDGEMM_PREC_F16 0

@@ -68,6 +68,23 @@ lib.pdgemm_pick_config.argtypes = [_i, _i64, _i64, _i64]
 lib.pdgemm_pick_config.restype = _i
 lib.pdgemm_config_info.argtypes = [_i] + [ctypes.POINTER(_i)] * 5
 lib.pdgemm_config_info.restype = _i
+lib.pdgemm_i4_workspace_size.argtypes = [_i64, _i64, _i64]
+lib.pdgemm_i4_workspace_size.restype = _i64
+lib.pdgemm_i4_f6_workspace_bytes.argtypes = [_i64, _i64, _i64]
+lib.pdgemm_i4_f6_workspace_bytes.restype = _i64
+lib.pdgemm_i4_f6_pick.argtypes = [_i64, _i64, _i64]
+lib.pdgemm_i4_f6_pick.restype = _i
+lib.pdgemm_i4_f6_num_configs.argtypes = []
+lib.pdgemm_i4_f6_num_configs.restype = _i
+for _name in ("gemm_i4_ws", "gemm_i4_rowb_ws"):
+    getattr(lib, _name).argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+    getattr(lib, _name).restype = _i
+lib.gemm_i4_dequant_ws.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i64, _i, _p, _i64,
+                                   _p]
+lib.gemm_i4_dequant_ws.restype = _i
+lib.pdgemm_i4_f6_cfg.argtypes = [_i, _i, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i64, _i, _p,
+                                 _i64, _p]
+lib.pdgemm_i4_f6_cfg.restype = _i
 lib.pdgemm_strerror.argtypes = [_i]
 lib.pdgemm_strerror.restype = ctypes.c_char_p
 lib.pdgemm_version.argtypes = []
@@ -105,6 +122,34 @@ def config_info(cfg: int) -> dict:
     return {k: v.value for k, v in zip(keys, vals)}
 
 
+def i4_workspace_size(M: int, N: int, K: int) -> int:
+    """Bytes of workspace the INT4 workspace entry points need for this shape
+    (0 where they run the INT8-MFMA kernels)."""
+    return lib.pdgemm_i4_workspace_size(M, N, K)
+
+
+def i4_f6_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Bytes of workspace of the FP6 path for this shape, whichever tile it takes."""
+    return lib.pdgemm_i4_f6_workspace_bytes(M, N, K)
+
+
+def i4_f6_pick(M: int, N: int, K: int) -> int:
+    """The FP6 tile the workspace entry points take for this shape (-1: INT8-MFMA kernels)."""
+    return lib.pdgemm_i4_f6_pick(M, N, K)
+
+
+def i4_f6_num_configs() -> int:
+    return lib.pdgemm_i4_f6_num_configs()
+
+
+def i4_workspace(M: int, N: int, K: int, device=None, f6: bool = False) -> torch.Tensor:
+    """A workspace tensor for an INT4 GEMM of this shape (at least 256 bytes; with f6,
+    sized for the FP6 path whatever the library would pick)."""
+    n = i4_f6_workspace_bytes(M, N, K) if f6 else i4_workspace_size(M, N, K)
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
 def _row_major_2d(t: torch.Tensor, name: str):
     if t.dim() != 2:
         raise ValueError(f"{name} must be 2-D")
@@ -133,9 +178,23 @@ def _scale(t: torch.Tensor, n: int, name: str) -> int:
     return t.data_ptr()
 
 
-def _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None, N=None, rowb=False):
+def _workspace(ws, device):
+    """(pointer, bytes) of a workspace tensor (or (None, 0))."""
+    if ws is None:
+        return None, 0
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+        raise TypeError("workspace must be a contiguous GPU tensor")
+    if ws.device != device:
+        raise ValueError("workspace must be on the operands' GPU")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None, N=None, rowb=False,
+             workspace=None, f6cfg=None):
     """The C function and its argument tuple for one GEMM (dequantizing when
-    scales = (scale_a, scale_b) is given; B row-major when rowb, with N given)."""
+    scales = (scale_a, scale_b) is given; B row-major when rowb, with N given;
+    INT4 on the FP6 cores with a workspace, by the library's choice or with
+    the FP6 tile f6cfg)."""
     M = A.shape[0]
     N = Bt.shape[0] if N is None else N
     ldc = _row_major_2d(out, "out")
@@ -144,6 +203,30 @@ def _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None, N=None, ro
         raise ValueError("operands, scales and out must be on the same GPU")
     if tuple(out.shape) != (M, N):
         raise ValueError(f"out must have shape {(M, N)}")
+    if workspace is not None or f6cfg is not None:
+        if prec != PREC_I4:
+            raise ValueError("a workspace serves the INT4 GEMM on the FP6 cores only")
+        if cfg is not None:
+            raise ValueError("cfg selects an INT8-MFMA tile; the FP6 tile is f6cfg")
+        ws, ws_bytes = _workspace(workspace, out.device)
+        sa = sb = None
+        if scales is not None:
+            if out.dtype not in (torch.float32, torch.float16):
+                raise TypeError("a dequantizing GEMM writes float32 or float16")
+            sa, sb = _scale(scales[0], M, "scale_a"), _scale(scales[1], N, "scale_b")
+        half = 1 if out.dtype == torch.float16 else 0
+        if f6cfg is not None:
+            return lib.pdgemm_i4_f6_cfg, (f6cfg, 1 if rowb else 0, M, N, K, A.data_ptr(), lda,
+                                          Bt.data_ptr(), ldb, sa, sb, out.data_ptr(), ldc, half, ws,
+                                          ws_bytes, _stream(stream))
+        if scales is not None:
+            if rowb:
+                raise ValueError("the dequantizing epilogue takes a column-major B")
+            return lib.gemm_i4_dequant_ws, (M, N, K, A.data_ptr(), lda, Bt.data_ptr(), ldb, sa, sb,
+                                            out.data_ptr(), ldc, half, ws, ws_bytes, _stream(stream))
+        fn = lib.gemm_i4_rowb_ws if rowb else lib.gemm_i4_ws
+        return fn, (M, N, K, A.data_ptr(), lda, Bt.data_ptr(), ldb, out.data_ptr(), ldc, ws, ws_bytes,
+                    _stream(stream))
     if rowb:
         if scales is not None:
             raise ValueError("the dequantizing epilogue takes a column-major B")
@@ -170,8 +253,9 @@ def _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None, N=None, ro
     return lib.pdgemm_dequant_cfg, (prec, cfg) + args
 
 
-def _call(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None, N=None, rowb=False):
-    fn, args = _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales, N, rowb)
+def _call(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None, N=None, rowb=False, workspace=None,
+          f6cfg=None):
+    fn, args = _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales, N, rowb, workspace, f6cfg)
     rc = fn(*args)
     if rc != 0:
         raise PdgemmError(rc)
@@ -211,8 +295,10 @@ def gemm_i8(A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor | None = None,
 
 
 def gemm_i4(A: torch.Tensor, Bt: torch.Tensor, K: int | None = None,
-            out: torch.Tensor | None = None, stream=None, cfg: int | None = None) -> torch.Tensor:
-    """C = A * B for packed INT4 A (M, K/2) and Bt (N, K/2) bytes; int32 C (M, N)."""
+            out: torch.Tensor | None = None, stream=None, cfg: int | None = None,
+            workspace: torch.Tensor | None = None, f6cfg: int | None = None) -> torch.Tensor:
+    """C = A * B for packed INT4 A (M, K/2) and Bt (N, K/2) bytes; int32 C (M, N).
+    With a workspace (see i4_workspace) the library may run it on the FP6 cores."""
     if A.dtype != torch.uint8 or Bt.dtype != torch.uint8:
         raise TypeError("gemm_i4 takes uint8 tensors of packed 4-bit values")
     if K is None:
@@ -224,14 +310,14 @@ def gemm_i4(A: torch.Tensor, Bt: torch.Tensor, K: int | None = None,
         out = torch.empty((A.shape[0], Bt.shape[0]), dtype=torch.int32, device=A.device)
     elif out.dtype != torch.int32:
         raise TypeError("gemm_i4 writes an int32 output")
-    return _call(PREC_I4, A, Bt, out, K, lda, ldb, stream, cfg)
+    return _call(PREC_I4, A, Bt, out, K, lda, ldb, stream, cfg, workspace=workspace, f6cfg=f6cfg)
 
 
 _DTYPES = {"f16": (torch.float16, torch.float32, PREC_F16), "i8": (torch.int8, torch.int32, PREC_I8),
            "i4": (torch.uint8, torch.int32, PREC_I4)}
 
 
-def _gemm_rowb(prec, A, B, K, N, out, stream, cfg):
+def _gemm_rowb(prec, A, B, K, N, out, stream, cfg, workspace=None, f6cfg=None):
     in_t, out_t, p = _DTYPES[prec]
     if A.dtype != in_t or B.dtype != in_t:
         raise TypeError(f"{prec} with row-major B takes {in_t} operands")
@@ -245,7 +331,8 @@ def _gemm_rowb(prec, A, B, K, N, out, stream, cfg):
         out = torch.empty((A.shape[0], N), dtype=out_t, device=A.device)
     elif out.dtype != out_t:
         raise TypeError(f"{prec} writes a {out_t} output")
-    return _call(p, A, B, out, K, lda, ldb, stream, cfg, N=N, rowb=True)
+    return _call(p, A, B, out, K, lda, ldb, stream, cfg, N=N, rowb=True, workspace=workspace,
+                 f6cfg=f6cfg)
 
 
 def gemm_f16_rowb(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None,
@@ -261,10 +348,10 @@ def gemm_i8_rowb(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = No
 
 
 def gemm_i4_rowb(A: torch.Tensor, B: torch.Tensor, K: int | None = None, N: int | None = None,
-                 out: torch.Tensor | None = None, stream=None,
-                 cfg: int | None = None) -> torch.Tensor:
+                 out: torch.Tensor | None = None, stream=None, cfg: int | None = None,
+                 workspace: torch.Tensor | None = None, f6cfg: int | None = None) -> torch.Tensor:
     """C = A * B for packed INT4 A (M, K/2) and row-major B (K, N/2 bytes, packed along N)."""
-    return _gemm_rowb("i4", A, B, K, N, out, stream, cfg)
+    return _gemm_rowb("i4", A, B, K, N, out, stream, cfg, workspace, f6cfg)
 
 
 def gemm_i8_dequant(A: torch.Tensor, Bt: torch.Tensor, scale_a: torch.Tensor,
@@ -287,7 +374,8 @@ def gemm_i8_dequant(A: torch.Tensor, Bt: torch.Tensor, scale_a: torch.Tensor,
 def gemm_i4_dequant(A: torch.Tensor, Bt: torch.Tensor, scale_a: torch.Tensor,
                     scale_b: torch.Tensor, K: int | None = None,
                     out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
-                    stream=None, cfg: int | None = None) -> torch.Tensor:
+                    stream=None, cfg: int | None = None, workspace: torch.Tensor | None = None,
+                    f6cfg: int | None = None) -> torch.Tensor:
     """Packed INT4 GEMM with the dequantizing epilogue of gemm_i8_dequant."""
     if A.dtype != torch.uint8 or Bt.dtype != torch.uint8:
         raise TypeError("gemm_i4_dequant takes uint8 tensors of packed 4-bit values")
@@ -298,11 +386,13 @@ def gemm_i4_dequant(A: torch.Tensor, Bt: torch.Tensor, scale_a: torch.Tensor,
     lda, ldb = 2 * _row_major_2d(A, "A"), 2 * _row_major_2d(Bt, "Bt")
     if out is None:
         out = torch.empty((A.shape[0], Bt.shape[0]), dtype=out_dtype, device=A.device)
-    return _call(PREC_I4, A, Bt, out, K, lda, ldb, stream, cfg, (scale_a, scale_b))
+    return _call(PREC_I4, A, Bt, out, K, lda, ldb, stream, cfg, (scale_a, scale_b), workspace=workspace,
+                 f6cfg=f6cfg)
 
 
 def prepare(prec: str, A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor, K: int | None = None,
-            stream=None, cfg: int | None = None, scales=None, rowb: bool = False):
+            stream=None, cfg: int | None = None, scales=None, rowb: bool = False,
+            workspace: torch.Tensor | None = None, f6cfg: int | None = None):
     """Check and marshal one GEMM once; return a no-argument callable that
     enqueues it again (on the stream current now) through the C ABI.
 
@@ -311,7 +401,8 @@ def prepare(prec: str, A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor, K: 
     the kernel time even for small shapes.  The tensors must stay alive.
     With scales = (scale_a, scale_b) an INT8 / INT4 GEMM is the dequantizing
     one, and out is float32 or float16.  With rowb, Bt is a row-major B
-    (K, N) instead (INT4: packed along N) and N is out's column count.
+    (K, N) instead (INT4: packed along N) and N is out's column count.  An
+    INT4 GEMM with a workspace runs through the workspace entry points.
     """
     integer_out = (torch.int32,) if scales is None else (torch.float32, torch.float16)
     if prec == "f16":
@@ -339,13 +430,14 @@ def prepare(prec: str, A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor, K: 
     elif A.shape[1] * per < K or Bt.shape[1] * per < K:
         raise ValueError("operands hold fewer than K values per row")
     fn, args = _marshal(p, A, Bt, out, K, lda, ldb, stream, cfg, scales, N=N if rowb else None,
-                        rowb=rowb)
+                        rowb=rowb, workspace=workspace, f6cfg=f6cfg)
     rc = fn(*args)  # validates the arguments once, and is a first launch
     if rc != 0:
         raise PdgemmError(rc)
 
     # the callable holds the tensors, so their memory outlives it
-    keep = (A, Bt, out) + (tuple(scales) if scales is not None else ())
+    keep = (A, Bt, out) + (tuple(scales) if scales is not None else ()) + (
+        (workspace,) if workspace is not None else ())
 
     def launch():
         rc = fn(*args)

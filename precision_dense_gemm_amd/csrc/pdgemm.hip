@@ -97,6 +97,13 @@ template <> struct Prec<kI4> {
     using Out = int32_t;
     using Acc = intx16_t;
 };
+// INT4 run as e2m3 values on the FP6 matrix cores (an internal id: the
+// entry points take INT4 and return int32): exact integer sums in fp32
+constexpr int kF6 = 3;
+template <> struct Prec<kF6> {
+    using Out = int32_t;
+    using Acc = floatx16_t;
+};
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
@@ -216,6 +223,121 @@ __device__ __forceinline__ int bswizzle(int r) {
     return RowB<P>::kQ * ((r / v) % span);
 }
 
+// Block id -> tile (tile_m, tile_n).  Workgroups are dispatched round-robin
+// over the 8 XCDs, so the block id is remapped to give each XCD a contiguous
+// range of tiles, and tiles are ordered in bands of GM block rows (column by
+// column within a band), so that the workgroups resident on one XCD share A
+// and B panels in its L2.
+template <int GM>
+__device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int &tile_m, int &tile_n) {
+    const int nb = gridDim.x;
+    const int bid = blockIdx.x;
+    const int q = nb >> 3, r = nb & 7;
+    const int xcd = bid & 7, loc = bid >> 3;
+    const int id = (xcd < r) ? xcd * (q + 1) + loc : r * (q + 1) + (xcd - r) * q + loc;
+    const int band = id / (GM * tiles_n);
+    const int first_m = band * GM;
+    const int rows = min(tiles_m - first_m, GM);
+    const int in_band = id - band * GM * tiles_n;
+    tile_m = first_m + in_band % rows;
+    tile_n = in_band / rows;
+}
+
+// Epilogue of a tile without K split: the accumulators of a wave's WM x WN
+// sub-block (FM x FN MFMA blocks of 32 x 32) stored to row-major C, converted
+// per precision (INT4 planes: the exact >> 8; INT4 on the FP6 cores: the
+// integer-valued fp32 sum to int32) and, with a dequantizing epilogue, scaled.
+// Register e of lane l in MFMA block (i, j) holds row
+// i*32 + 8*(e/4) + 4*(l/32) + e%4 and column j*32 + l%32 of the wave's
+// tile.  Row offsets are wave-uniform (scalar registers); each lane adds
+// one 32-bit offset, so a store costs no vector address arithmetic.
+template <int P, int E, int BM, int BN, int FM, int FN, typename AccT>
+__device__ __forceinline__ void store_tile(void *C, int64_t ldc, int M, int N, AccT (&acc)[FM][FN], int m0, int n0,
+                                           int wm0, int wn0, int lane, const float *lds_scale) {
+    using Out = typename OutOf<P, E>::type;
+    const int frow = lane & 31;
+    const int fhalf = lane >> 5;
+    char *const wave_c = reinterpret_cast<char *>(C) +
+                         ((int64_t)(m0 + wm0) * ldc + n0 + wn0) * (int64_t)sizeof(Out);
+    const int64_t row_bytes = ldc * (int64_t)sizeof(Out);
+    const uint32_t lane_off = (uint32_t)(4 * fhalf * row_bytes) + frow * (uint32_t)sizeof(Out);
+    const bool interior = m0 + BM <= M && n0 + BN <= N;
+    const int rows_left = M - (m0 + wm0) - 4 * fhalf;  // rows this lane may write: r < rows_left
+    const int cols_left = N - (n0 + wn0) - frow;        // columns: j*32 < cols_left
+
+    // this lane's scales: 4 consecutive rows per quarter of a 32-row
+    // block (one 16-byte LDS read each), one column per column block
+    float sb[E == kRaw ? 1 : FN];
+    if constexpr (E != kRaw) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) sb[j] = lds_scale[BM + wn0 + j * 32 + frow];
+    }
+    auto store_all = [&](auto &&keep) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            float4 sa[E == kRaw ? 1 : 4];
+            if constexpr (E != kRaw) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    sa[q] = *reinterpret_cast<const float4 *>(&lds_scale[wm0 + i * 32 + 8 * q + 4 * fhalf]);
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = i * 32 + 8 * (e >> 2) + (e & 3);   // wave-uniform part of the row
+                char *const row_c = wave_c + r * row_bytes;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    Out v;
+                    if constexpr (E != kRaw) {
+                        // ((float)sum * scale_a) * scale_b, rounded once per step
+                        // (on the FP6 cores the sum already is that binary32 value)
+                        float c;
+                        if constexpr (P == kF6)
+                            c = acc[i][j][e];
+                        else
+                            c = (float)(P == kI4 ? acc[i][j][e] >> 8 : acc[i][j][e]);
+                        const float4 a4 = sa[e >> 2];
+                        c = c * ((e & 3) == 0 ? a4.x : (e & 3) == 1 ? a4.y : (e & 3) == 2 ? a4.z : a4.w);
+                        c = c * sb[j];
+                        // The binary16 result is the binary32 product rounded
+                        // again.  The backend would otherwise fold product and
+                        // narrowing into one mixed-precision FMA, which rounds
+                        // once (and turns -0 into +0): the empty asm makes the
+                        // binary32 value opaque to it.
+                        if constexpr (E == kDequantF16) asm("" : "+v"(c));
+                        v = (Out)c;
+                    } else if constexpr (P == kI4) {
+                        v = acc[i][j][e] >> 8;
+                    } else if constexpr (P == kF6) {
+                        v = (int32_t)acc[i][j][e];   // an integer below 2^24 in magnitude: exact
+                    } else {
+                        v = acc[i][j][e];
+                    }
+                    // non-temporal: C is not read again here, and
+                    // streaming it past the MALL keeps A and B there
+                    // for the later rounds of tiles
+                    if (keep(r, j))
+                        __builtin_nontemporal_store(
+                            v, reinterpret_cast<Out *>(row_c + lane_off + j * 32 * (int)sizeof(Out)));
+                }
+                // dequantized values are converted one row at a time
+                if constexpr (E != kRaw) __builtin_amdgcn_sched_barrier(0);
+            }
+            // one row block at a time keeps accumulator reads from piling up
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    if constexpr (E != kRaw) {
+        // one path: with two, more of the accumulators are copied out of
+        // the accumulation registers ahead of the branch
+        store_all([&](int r, int j) { return interior || (r < rows_left && j * 32 < cols_left); });
+    } else if (interior) {
+        store_all([](int, int) { return true; });
+    } else {
+        store_all([&](int r, int j) { return r < rows_left && j * 32 < cols_left; });
+    }
+}
+
 // One workgroup computes a BM x BN block of C with (BM/WM) x (BN/WN) waves
 // (times KS with a K split, whose waves share the block).
 //
@@ -310,19 +432,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
 
     // ---- block id -> tile, XCD-aware and banded by GM block rows ----
     int tile_m, tile_n;
-    {
-        const int nb = gridDim.x;
-        const int bid = blockIdx.x;
-        const int q = nb >> 3, r = nb & 7;
-        const int xcd = bid & 7, loc = bid >> 3;
-        const int id = (xcd < r) ? xcd * (q + 1) + loc : r * (q + 1) + (xcd - r) * q + loc;
-        const int band = id / (GM * args.tiles_n);
-        const int first_m = band * GM;
-        const int rows = min(args.tiles_m - first_m, GM);
-        const int in_band = id - band * GM * args.tiles_n;
-        tile_m = first_m + in_band % rows;
-        tile_n = in_band / rows;
-    }
+    tile_of<GM>(args.tiles_m, args.tiles_n, tile_m, tile_n);
     const int m0 = tile_m * BM;
     const int n0 = tile_n * BN;
 
@@ -871,85 +981,476 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     }
 
     // ---- epilogue: 32x32 MFMA result layout -> row-major C ----
-    // Register e of lane l in MFMA block (i, j) holds row
-    // i*32 + 8*(e/4) + 4*(l/32) + e%4 and column j*32 + l%32 of the wave's
-    // tile.  Row offsets are wave-uniform (scalar registers); each lane adds
-    // one 32-bit offset, so a store costs no vector address arithmetic.
-    if constexpr (KS == 1) {
-        char *const wave_c = reinterpret_cast<char *>(args.C) +
-                             ((int64_t)(m0 + wm0) * args.ldc + n0 + wn0) * (int64_t)sizeof(Out);
-        const int64_t row_bytes = args.ldc * (int64_t)sizeof(Out);
-        const uint32_t lane_off = (uint32_t)(4 * fhalf * row_bytes) + frow * (uint32_t)sizeof(Out);
-        const bool interior = m0 + BM <= M && n0 + BN <= N;
-        const int rows_left = M - (m0 + wm0) - 4 * fhalf;  // rows this lane may write: r < rows_left
-        const int cols_left = N - (n0 + wn0) - frow;        // columns: j*32 < cols_left
+    if constexpr (KS == 1)
+        store_tile<P, E, BM, BN, FM, FN>(args.C, args.ldc, M, N, acc, m0, n0, wm0, wn0, lane, lds_scale);
+#endif  // __HIP_DEVICE_COMPILE__
+}
 
-        // this lane's scales: 4 consecutive rows per quarter of a 32-row
-        // block (one 16-byte LDS read each), one column per column block
-        float sb[E == kRaw ? 1 : FN];
-        if constexpr (E != kRaw) {
+// ---------------------------------------------------------------------------
+// INT4 on the FP6 matrix cores
+//
+// gfx950's v_mfma_scale_f32_32x32x64_f8f6f4 multiplies 6-bit e2m3 values
+// (1 sign, 2 exponent bits of bias 1, 3 mantissa bits) at about twice the
+// rate of the INT8 MFMA.  Every INT4 value v in [-8, 7] is exact in e2m3 as
+// v / 8: |v| = 0..7 are the subnormals m / 8 (exponent 0, mantissa m) and
+// |v| = 8 is 1.0 (exponent 1, mantissa 0), so the 6-bit code of v / 8 is
+// sign << 5 | |v|.  Each operand carries the block scale 2^3 (E8M0 code
+// 130), so an MFMA adds the exact integer products a * b, and the fp32
+// accumulators hold exact integers: |C| <= 64 K < 2^24 for K <= 131071.
+// One MFMA covers 64 values of K per output, where the INT8 path needs two
+// (one per nibble plane), and the main loop holds no unpacking.
+//
+// The cost is the format: 32 values take 24 bytes (six registers) per lane,
+// and turning nibbles into 6-bit codes takes about three VALU operations per
+// value.  Done per fragment in the main loop, that would cost more than the
+// MFMAs, because every operand row is read by many workgroups.  So a
+// pre-pass (f6_pack_kernel) converts each operand once into a workspace
+// "image", and the GEMM (gemm_f6_kernel) stages the image with straight
+// 1 KB DMA copies.
+//
+// Image layout.  Rows (of A, or columns of B) come in groups of 32 and K in
+// blocks of 128 values; unit (g, b) of an operand is 3072 bytes at offset
+// (g * nkb + b) * 3072, nkb = ceil(K / 128).  A unit holds, for each row r
+// of the group and each k-step s (64 values) and lane half h (32 values,
+// as the MFMA takes them: lane (row, h) holds k = 64 s + 32 h + e), the six
+// code words of those 32 values: words 0-3 ("main", 16 bytes) and words 4-5
+// ("tail", 8 bytes).
+//   main part, bytes 0 .. 2047:    row r at 64 r, logical chunk c = 2 s + h
+//                                  at 16-byte position c ^ swizzle(r)
+//   tail part, bytes 2048 .. 3071: row r at 2048 + 32 r, logical slot
+//                                  c = 2 s + h at 8-byte position
+//                                  c ^ tswizzle(r)
+// A GEMM stage is one K block: the units of the tile's row groups, copied
+// as they are into LDS (main parts as 64-byte rows, tail parts as 32-byte
+// rows).  Rows past M (N) and values past K are zero codes in the image, so
+// the GEMM needs no masking; groups past the image read as zeros through the
+// buffer range.  Within the 32 values of a fragment the pre-pass orders the
+// codes as its SWAR arithmetic leaves them (the even k of each dword, then
+// the odd ones); A and B use the same order, so the MFMA still pairs equal k.
+
+// 8-byte tail slot positions: the 32 lanes of a half-wave read 32 rows at
+// one logical slot; with 64 banks, row r at position p covers banks
+// 8 (r % 8) + 2 p .. + 1, so rows r and r + 8 j must differ in p.
+__device__ __forceinline__ int tswizzle(int r) { return (r >> 3) & 3; }
+
+// four 6-bit codes, one per byte (bits 0-5), packed into bits 0 .. 23
+__device__ __forceinline__ uint32_t pack4_codes(uint32_t x) {
+    const uint32_t z = (x & 0x00FF00FFu) | ((x & 0xFF00FF00u) >> 2);   // codes at bits 0, 6, 16, 22
+    return (z & 0xFFFu) | ((z >> 4) & 0xFFF000u);                        // ... at 0, 6, 12, 18
+}
+
+// 8 two's complement nibbles -> the e2m3 codes of their values / 8: those of
+// the even nibbles in lo (bits 0 .. 23), of the odd ones in hi.
+__device__ __forceinline__ void s4_to_e2m3(uint32_t w, uint32_t &lo, uint32_t &hi) {
+    const uint32_t t = w & 0x88888888u;      // sign bits
+    const uint32_t s1 = t >> 3;              // 1 in each negative nibble
+    const uint32_t neg = (t << 1) - s1;      // 0xF in each negative nibble (no carries across)
+    const uint32_t mag = (w ^ neg) + s1;     // |v| per nibble, 0 .. 8 (16 - n for a negative n)
+    const uint32_t e = (mag & 0x0F0F0F0Fu) | ((t << 2) & 0x20202020u);          // sign to bit 5
+    const uint32_t o = ((mag >> 4) & 0x0F0F0F0Fu) | ((t >> 2) & 0x20202020u);
+    lo = pack4_codes(e);
+    hi = pack4_codes(o);
+}
+
+// 32 packed INT4 values (16 bytes) -> their six code words (192 bits: eight
+// 24-bit groups of four codes, dense)
+__device__ __forceinline__ void fragment_to_e2m3(const uint4 &w, uint4 &main, uint2 &tail) {
+    uint32_t p[8];
+    s4_to_e2m3(w.x, p[0], p[1]);
+    s4_to_e2m3(w.y, p[2], p[3]);
+    s4_to_e2m3(w.z, p[4], p[5]);
+    s4_to_e2m3(w.w, p[6], p[7]);
+    main.x = p[0] | (p[1] << 24);
+    main.y = (p[1] >> 8) | (p[2] << 16);
+    main.z = (p[2] >> 16) | (p[3] << 8);
+    main.w = p[4] | (p[5] << 24);
+    tail.x = (p[5] >> 8) | (p[6] << 16);
+    tail.y = (p[6] >> 16) | (p[7] << 8);
+}
+
+constexpr int kF6Block = 128;    // K values per image unit and per GEMM stage
+constexpr int kF6Unit = 3072;    // bytes per unit: 32 rows x (64 main + 32 tail)
+constexpr int kF6Main = 2048;    // bytes of the main part of a unit
+constexpr int kF6Scale = 130;    // E8M0 block scale 2^3 (bias 127)
+
+// One operand of the pre-pass.
+struct F6Operand {
+    const uint8_t *src;   // packed INT4
+    uint8_t *img;         // the image
+    int64_t ld_bytes;     // row stride of src
+    int rows;             // rows of the image (M for A, N for B)
+    int groups;           // ceil(rows / 32)
+    int rowmajor;         // B only: src is K x N packed along N (row-major B)
+};
+
+struct F6PackArgs {
+    F6Operand op[2];      // A, B
+    int K, nkb;
+    int blocks_a;         // workgroups of A; the rest convert B
+};
+
+// The pre-pass: one wave per unit (four per workgroup), lane (r, h) = (lane
+// % 32, lane / 32) converting the 2 x 32 values of row r, half h of the
+// unit's two k-steps.  K-contiguous rows (A, column-major B) are read as
+// 16-byte chunks; a row-major B tile (128 rows of K x 32 columns) is first
+// copied to LDS and each lane gathers its column from there.
+__global__ __launch_bounds__(256) void f6_pack_kernel(F6PackArgs args) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __shared__ uint8_t tile_s[4][kF6Block][16];   // row-major B: K rows x 32 nibbles, per wave
+    const int which = blockIdx.x < args.blocks_a ? 0 : 1;
+    const F6Operand &op = args.op[which];
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)(blockIdx.x - (which ? args.blocks_a : 0)) * 4 + wave;
+    if (unit >= (int64_t)op.groups * args.nkb) return;
+    const int g = (int)(unit / args.nkb);
+    const int b = (int)(unit - (int64_t)g * args.nkb);
+    const int r = lane & 31, h = lane >> 5;
+    const int K = args.K;
+    uint8_t *const dst = op.img + unit * kF6Unit;
+    uint4 w[2];
+    if (!op.rowmajor) {
+        const int row = g * 32 + r;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) sb[j] = lds_scale[BM + wn0 + j * 32 + frow];
-        }
-        auto store_all = [&](auto &&keep) __attribute__((always_inline)) {
+        for (int s = 0; s < 2; ++s) {
+            const int k0 = b * kF6Block + s * 64 + h * 32;   // first value of the fragment
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (row < op.rows && k0 < K) {
+                v = *reinterpret_cast<const uint4 *>(op.src + (int64_t)row * op.ld_bytes + k0 / 2);
+                const int nb = (K - k0) / 2;   // valid bytes (K is even)
+                if (nb < 16) {
+                    uint32_t m[4];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                float4 sa[E == kRaw ? 1 : 4];
-                if constexpr (E != kRaw) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        sa[q] = *reinterpret_cast<const float4 *>(&lds_scale[wm0 + i * 32 + 8 * q + 4 * fhalf]);
-                }
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int r = i * 32 + 8 * (e >> 2) + (e & 3);   // wave-uniform part of the row
-                    char *const row_c = wave_c + r * row_bytes;
-#pragma unroll
-                    for (int j = 0; j < FN; ++j) {
-                        Out v;
-                        if constexpr (E != kRaw) {
-                            // ((float)sum * scale_a) * scale_b, rounded once per step
-                            const int32_t sum = P == kI4 ? acc[i][j][e] >> 8 : acc[i][j][e];
-                            float c = (float)sum;
-                            const float4 a4 = sa[e >> 2];
-                            c = c * ((e & 3) == 0 ? a4.x : (e & 3) == 1 ? a4.y : (e & 3) == 2 ? a4.z : a4.w);
-                            c = c * sb[j];
-                            // The binary16 result is the binary32 product rounded
-                            // again.  The backend would otherwise fold product and
-                            // narrowing into one mixed-precision FMA, which rounds
-                            // once (and turns -0 into +0): the empty asm makes the
-                            // binary32 value opaque to it.
-                            if constexpr (E == kDequantF16) asm("" : "+v"(c));
-                            v = (Out)c;
-                        } else if constexpr (P == kI4) {
-                            v = acc[i][j][e] >> 8;
-                        } else {
-                            v = acc[i][j][e];
-                        }
-                        // non-temporal: C is not read again here, and
-                        // streaming it past the MALL keeps A and B there
-                        // for the later rounds of tiles
-                        if (keep(r, j))
-                            __builtin_nontemporal_store(
-                                v, reinterpret_cast<Out *>(row_c + lane_off + j * 32 * (int)sizeof(Out)));
+                    for (int d = 0; d < 4; ++d) {
+                        const int q = nb - 4 * d;
+                        m[d] = q >= 4 ? 0xFFFFFFFFu : (q <= 0 ? 0u : (1u << (8 * q)) - 1u);
                     }
-                    // dequantized values are converted one row at a time
-                    if constexpr (E != kRaw) __builtin_amdgcn_sched_barrier(0);
+                    v.x &= m[0];
+                    v.y &= m[1];
+                    v.z &= m[2];
+                    v.w &= m[3];
                 }
-                // one row block at a time keeps accumulator reads from piling up
-                __builtin_amdgcn_sched_barrier(0);
             }
-        };
-        if constexpr (E != kRaw) {
-            // one path: with two, more of the accumulators are copied out of
-            // the accumulation registers ahead of the branch
-            store_all([&](int r, int j) { return interior || (r < rows_left && j * 32 < cols_left); });
-        } else if (interior) {
-            store_all([](int, int) { return true; });
-        } else {
-            store_all([&](int r, int j) { return r < rows_left && j * 32 < cols_left; });
+            w[s] = v;
+        }
+    } else {
+        // 128 rows of K (b * 128 ..) x 32 columns (g * 32 ..) = 16 bytes per row;
+        // lane l copies rows l and l + 64 (zeros past K), nibbles past N zeroed
+        const int cbyte = g * 16;
+        const int valid_nib = min(op.rows - g * 32, 32);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int kr = lane + 64 * x;
+            const int k = b * kF6Block + kr;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (k < K) {
+                v = *reinterpret_cast<const uint4 *>(op.src + (int64_t)k * op.ld_bytes + cbyte);
+                if (valid_nib < 32) {
+                    uint32_t m[4];
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const int q = valid_nib - 8 * d;   // valid nibbles in this dword
+                        m[d] = q >= 8 ? 0xFFFFFFFFu : (q <= 0 ? 0u : (1u << (4 * q)) - 1u);
+                    }
+                    v.x &= m[0];
+                    v.y &= m[1];
+                    v.z &= m[2];
+                    v.w &= m[3];
+                }
+            }
+            *reinterpret_cast<uint4 *>(&tile_s[wave][kr][0]) = v;
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        // column r: nibble r % 2 of byte r / 2 of each row; fragment s holds
+        // rows 64 s + 32 h .. + 31, two per byte, the lower row in the low nibble
+        const int sh = 4 * (r & 1);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            uint32_t d[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t acc = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int kr = s * 64 + h * 32 + q * 8 + e;
+                    acc |= (uint32_t)((tile_s[wave][kr][r >> 1] >> sh) & 0xF) << (4 * e);
+                }
+                d[q] = acc;
+            }
+            w[s] = make_uint4(d[0], d[1], d[2], d[3]);
         }
     }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        uint4 m;
+        uint2 t;
+        fragment_to_e2m3(w[s], m, t);
+        const int c = 2 * s + h;
+        *reinterpret_cast<uint4 *>(dst + r * 64 + 16 * (c ^ swizzle(r))) = m;
+        *reinterpret_cast<uint2 *>(dst + kF6Main + r * 32 + 8 * (c ^ tswizzle(r))) = t;
+    }
+#endif
+}
+
+struct F6Args {
+    const uint8_t *A;     // images
+    const uint8_t *B;
+    void *C;
+    const float *scale_a;
+    const float *scale_b;
+    int64_t a_bytes;      // image sizes
+    int64_t b_bytes;
+    int64_t ldc;
+    int M, N, nkb;
+    int tiles_m, tiles_n;
+};
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, in order
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
+// An FP6 fragment: the six code words of a lane.  The MFMA builtin takes
+// eight registers per operand and reads the first six for e2m3.
+typedef int intx6_t __attribute__((ext_vector_type(6)));
+typedef int intx8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ floatx16_t mfma_f6(const intx6_t &a, const intx6_t &b, const floatx16_t &c) {
+    const intx8_t a8 = __builtin_shufflevector(a, a, 0, 1, 2, 3, 4, 5, -1, -1);
+    const intx8_t b8 = __builtin_shufflevector(b, b, 0, 1, 2, 3, 4, 5, -1, -1);
+    // formats 2, 2: e2m3 for both operands; block scales 2^3 each
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 2, 2, 0, kF6Scale, 0, kF6Scale);
+}
+
+// The GEMM on the images: a BM x BN block of C per workgroup of
+// (BM/WM) x (BN/WN) waves, each wave a WM x WN sub-block of 32 x 32 MFMA
+// blocks.  Three LDS stages, each one K block (two k-steps) of the tile's
+// A and B units; stage st is fetched three stages before it is consumed,
+// one barrier per stage, after this wave's DMA of stage st+1 has landed.
+// Launch bounds: two waves per SIMD (8-wave tiles, or two 4-wave workgroups
+// per CU), except for the 128 x 128 wave tile, whose 256 accumulators take a
+// SIMD's registers for one wave.
+template <int BM, int BN, int WM, int WN, int GM, int E, int LA>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave, WM * WN >= 128 * 128 ? 1 : 2) void
+gemm_f6_kernel(F6Args args) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int NW = (BM / WM) * (BN / WN);
+    constexpr int kWavesN = BN / WN;
+    constexpr int FM = WM / 32;
+    constexpr int FN = WN / 32;
+    constexpr int kRows = BM + BN;             // LDS rows of a stage (main: 64 B, tail: 32 B)
+    constexpr int kUnitsA = BM / 32;
+    constexpr int kDma = 3 * (kRows / 32) / NW;  // 1 KB copies per wave per stage
+    static_assert(3 * (kRows / 32) % NW == 0, "a stage's copies must split evenly over the waves");
+    static_assert(kDma <= 31, "vmcnt holds at most 63 outstanding loads");
+    static_assert(LA >= 1 && LA <= FM, "A fragments are read 1 .. FM row blocks ahead");
+    using Stage = uint4[kRows][4];
+    using Tail = uint2[kRows][4];
+    __shared__ uint4 mn0[kRows][4], mn1[kRows][4], mn2[kRows][4];
+    __shared__ uint2 tl0[kRows][4], tl1[kRows][4], tl2[kRows][4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int M = args.M, N = args.N, nkb = args.nkb;
+
+    int tile_m, tile_n;
+    tile_of<GM>(args.tiles_m, args.tiles_n, tile_m, tile_n);
+    const int m0 = tile_m * BM;
+    const int n0 = tile_n * BN;
+
+    // copy j of this wave: unit u = x / 3 of the stage, part x % 3 (main
+    // rows 0-15, main rows 16-31, tail); the stage's buffer resources start
+    // at the tile's first unit of K block st, lane offsets add the unit's
+    // group (nkb units apart), the part and the lane's 16 bytes
+    const int64_t unit_stride = (int64_t)nkb * kF6Unit;
+    const int64_t a_first = (int64_t)tile_m * kUnitsA * unit_stride;
+    const int64_t b_first = (int64_t)tile_n * (BN / 32) * unit_stride;
+    uint32_t voff[kDma];
+#pragma unroll
+    for (int j = 0; j < kDma; ++j) {
+        const int x = j * NW + wave;
+        const int u = x / 3, part = x % 3;
+        const int gl = u < kUnitsA ? u : u - kUnitsA;
+        voff[j] = (uint32_t)(gl * unit_stride) + part * 1024 + lane * 16;
+    }
+    // bytes of each image from the tile's first unit on (capped: every
+    // offset a lane forms stays far below 2^31)
+    const int a_rem =
+        __builtin_amdgcn_readfirstlane((int)max(min(args.a_bytes - a_first, (int64_t)INT32_MAX), (int64_t)0));
+    const int b_rem =
+        __builtin_amdgcn_readfirstlane((int)max(min(args.b_bytes - b_first, (int64_t)INT32_MAX), (int64_t)0));
+    auto stage = [&](int st, Stage &mn, Tail &tl) __attribute__((always_inline)) {
+        const bool live = st < nkb;
+        const int64_t ao = a_first + (int64_t)st * kF6Unit;
+        const int64_t bo = b_first + (int64_t)st * kF6Unit;
+        const int a_range = live ? max(a_rem - st * kF6Unit, 0) : 0;
+        const int b_range = live ? max(b_rem - st * kF6Unit, 0) : 0;
+        const __amdgpu_buffer_rsrc_t ra =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(args.A + ao), (short)0, a_range, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rb =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(args.B + bo), (short)0, b_range, kRsrcWord3);
+#pragma unroll
+        for (int j = 0; j < kDma; ++j) {
+            const int x = j * NW + wave;
+            const int u = x / 3, part = x % 3;
+            void *dst = part < 2 ? (void *)&mn[u * 32 + part * 16][0] : (void *)&tl[u * 32][0];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(u < kUnitsA ? ra : rb, LDS_PTR(dst), 16, voff[j], 0, 0, 0);
+        }
+    };
+
+    const int wm0 = (wave / kWavesN) * WM;
+    const int wn0 = (wave % kWavesN) * WN;
+    const int frow = lane & 31;
+    const int fhalf = lane >> 5;
+    auto frag = [&](const Stage &mn, const Tail &tl, int row, int pm, int pt) __attribute__((always_inline)) {
+        const uint4 m = mn[row][pm];
+        // volatile keeps the tail reads apart: merged in pairs (ds_read2), their
+        // registers would have to be copied next to each fragment's main words
+        typedef unsigned int uintx2_t __attribute__((ext_vector_type(2)));
+        typedef __attribute__((address_space(3))) const volatile uintx2_t lds_tail_t;
+        const uintx2_t t = *(lds_tail_t *)(&tl[row][pt]);
+        intx6_t f;
+        f[0] = (int)m.x;
+        f[1] = (int)m.y;
+        f[2] = (int)m.z;
+        f[3] = (int)m.w;
+        f[4] = (int)t[0];
+        f[5] = (int)t[1];
+        return f;
+    };
+    // fragment of LDS row `row` (A: wm0 + 32 i + frow; B: BM + wn0 + 32 j +
+    // frow) for k-step s: logical chunk / slot 2 s + half
+    auto frag_at = [&](const Stage &mn, const Tail &tl, int row, int s) __attribute__((always_inline)) {
+        const int c = 2 * s + fhalf;
+        return frag(mn, tl, row, c ^ swizzle(frow), c ^ tswizzle(frow));   // rows start at multiples of 32
+    };
+
+    floatx16_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // Fragments in registers: the B fragments of the current k-step, and A
+    // one row block ahead (the INT8 kernels read a whole k-step ahead; here
+    // a fragment takes six registers, and that would not fit two waves per
+    // SIMD).  Row block i of k-step s reads A row block i+1; the last one
+    // reads the next k-step's B fragments and A row block 0, from the next
+    // stage after the stage barrier (kind 1) or not at all (kind 2).
+    intx6_t faq[LA], fb[FN];
+    auto kstep = [&](Stage &mn, Tail &tl, int s, const Stage &nmn, const Tail &ntl, int ns, auto kind_c, int st)
+        __attribute__((always_inline)) {
+        constexpr int kind = decltype(kind_c)::value;
+        intx6_t fbn[FN];
+        static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+            constexpr int i = decltype(i_c)::value;
+            constexpr int t = i + LA;                  // the row block this step reads:
+            constexpr bool here = t < FM;              // of this k-step,
+            constexpr bool next = !here && kind != 2;  // or row t - FM of the next one
+            intx6_t fan;
+            if constexpr (here) {
+                fan = frag_at(mn, tl, wm0 + t * 32 + frow, s);
+            } else if constexpr (next) {
+                if constexpr (t == FM) {
+                    if constexpr (kind == 1) {
+                        // this wave's copies of stage st+1 have landed and its
+                        // reads of this stage are done; after the barrier the
+                        // same holds for every wave, and this stage's buffer
+                        // is free for stage st+3
+                        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDma) : "memory");
+                        stage(st + 3, mn, tl);
+                    }
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) fbn[j] = frag_at(nmn, ntl, BM + wn0 + j * 32 + frow, ns);
+                }
+                fan = frag_at(nmn, ntl, wm0 + (t - FM) * 32 + frow, ns);
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma_f6(faq[0], fb[j], acc[i][j]);
+            // this step's reads (and copies), then its MFMAs, in this order
+            constexpr int reads = here ? 2 : (next ? (t == FM ? 2 * (FN + 1) : 2) : 0);
+            if constexpr (reads > 0) __builtin_amdgcn_sched_group_barrier(0x100, reads, 0);
+            if constexpr (next && t == FM && kind == 1) __builtin_amdgcn_sched_group_barrier(0x020, kDma, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q + 1 < LA; ++q) faq[q] = faq[q + 1];
+            if constexpr (here || next) faq[LA - 1] = fan;
+            if constexpr (i + 1 == FM && kind != 2) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) fb[j] = fbn[j];
+            }
+        });
+    };
+    using K0 = std::integral_constant<int, 0>;
+    using K1 = std::integral_constant<int, 1>;
+    using K2 = std::integral_constant<int, 2>;
+    // stage st (not the last) from (mn, tl), whose k-step 0 fragments are in
+    // registers; refills it with stage st+3 and reads k-step 0 of the next
+    auto full_stage = [&](Stage &mn, Tail &tl, const Stage &nmn, const Tail &ntl, int st)
+        __attribute__((always_inline)) {
+        kstep(mn, tl, 0, mn, tl, 1, K0{}, st);
+        kstep(mn, tl, 1, nmn, ntl, 0, K1{}, st);
+    };
+    auto last_stage = [&](Stage &mn, Tail &tl) __attribute__((always_inline)) {
+        kstep(mn, tl, 0, mn, tl, 1, K0{}, 0);
+        kstep(mn, tl, 1, mn, tl, 0, K2{}, 0);
+    };
+
+    // dequantizing epilogue: the tile's scales staged in LDS (see gemm_kernel)
+    constexpr int kThreads = NW * kWave;
+    constexpr int kScaleLoads = E == kRaw ? 0 : (BM + BN + kThreads - 1) / kThreads;
+    __shared__ __align__(16) float lds_scale[E == kRaw ? 1 : BM + BN];
+    float scale_v[kScaleLoads + 1];
+#pragma unroll
+    for (int x = 0; x < kScaleLoads; ++x) {
+        const int idx = tid + x * kThreads;
+        if (idx < BM + BN)
+            scale_v[x] = idx < BM ? args.scale_a[min(m0 + idx, M - 1)] : args.scale_b[min(n0 + idx - BM, N - 1)];
+    }
+
+    if (nkb > 0) {
+        // nkb is a multiple of 3 (the images are padded with zero blocks), so
+        // every stage's buffer is fixed at compile time and the K loop has
+        // one copy of each step
+        stage(0, mn0, tl0);
+        stage(1, mn1, tl1);
+        stage(2, mn2, tl2);
+#pragma unroll
+        for (int x = 0; x < kScaleLoads; ++x)
+            if (tid + x * kThreads < BM + BN) lds_scale[tid + x * kThreads] = scale_v[x];
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * kDma) : "memory");
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[j] = frag_at(mn0, tl0, BM + wn0 + j * 32 + frow, 0);
+#pragma unroll
+        for (int q = 0; q < LA; ++q) faq[q] = frag_at(mn0, tl0, wm0 + q * 32 + frow, 0);
+        int st = 0;
+        for (; st + 3 < nkb; st += 3) {
+            full_stage(mn0, tl0, mn1, tl1, st);
+            full_stage(mn1, tl1, mn2, tl2, st + 1);
+            full_stage(mn2, tl2, mn0, tl0, st + 2);
+        }
+        full_stage(mn0, tl0, mn1, tl1, st);
+        full_stage(mn1, tl1, mn2, tl2, st + 1);
+        last_stage(mn2, tl2);
+        // no DMA may still be writing this workgroup's LDS when it exits
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else if constexpr (E != kRaw) {
+#pragma unroll
+        for (int x = 0; x < kScaleLoads; ++x)
+            if (tid + x * kThreads < BM + BN) lds_scale[tid + x * kThreads] = scale_v[x];
+        __syncthreads();
+    }
+
+    store_tile<kF6, E, BM, BN, FM, FN>(args.C, args.ldc, M, N, acc, m0, n0, wm0, wn0, lane, lds_scale);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -1162,6 +1663,146 @@ int launch(int prec, int cfg, int epi, int br, int64_t M, int64_t N, int64_t K, 
     return PDGEMM_OK;
 }
 
+// ---- INT4 on the FP6 cores: tiles, workspace, launch ----
+
+// 0: 256 x 256 with 8 waves of 128 x 64; 1: 128 x 128 with 4 waves of
+// 64 x 64.  Three stages of 48 KB (24 KB for 128 x 128, so two workgroups
+// share a CU).  A 256 x 256 tile of 4 waves of 128 x 128 (half the LDS reads
+// per MFMA) measured 10% slower at N = 8192 and is not kept.
+// (the last field: how many row blocks ahead the A fragments are read; one
+// measured fastest, 2-4 were 2-7% slower at N = 8192)
+struct F6Config {
+    int bm, bn, wm, wn, gm, la;
+};
+constexpr F6Config kF6Configs[] = {
+    {256, 256, 128, 64, 4, 1},
+    {128, 128, 64, 64, 8, 1},
+};
+constexpr int kNumF6Configs = sizeof(kF6Configs) / sizeof(kF6Configs[0]);
+
+template <int C, int E>
+const void *f6_kernel_for() {
+    constexpr F6Config c = kF6Configs[C];
+    return reinterpret_cast<const void *>(&gemm_f6_kernel<c.bm, c.bn, c.wm, c.wn, c.gm, E, c.la>);
+}
+
+template <int E>
+const void *f6_kernel_ptr(int cfg) {
+    switch (cfg) {
+    case 0: return f6_kernel_for<0, E>();
+    case 1: return f6_kernel_for<1, E>();
+    default: return nullptr;
+    }
+}
+
+const void *f6_kernel_ptr(int cfg, int epi) {
+    switch (epi) {
+    case kRaw: return f6_kernel_ptr<kRaw>(cfg);
+    case kDequantF32: return f6_kernel_ptr<kDequantF32>(cfg);
+    case kDequantF16: return f6_kernel_ptr<kDequantF16>(cfg);
+    default: return nullptr;
+    }
+}
+
+// K blocks of an image: ceil(K / 128), padded with zero blocks to a multiple
+// of the GEMM's three LDS stages
+int64_t f6_blocks(int64_t K) { return cdiv(cdiv(K, kF6Block), 3) * 3; }
+
+// image of an operand with `rows` rows of K values: 32-row groups x 128-value
+// blocks of 3072 bytes
+int64_t f6_image_bytes(int64_t rows, int64_t K) { return cdiv(rows, 32) * f6_blocks(K) * kF6Unit; }
+
+// the workspace: A's image, then B's at the next multiple of 256 bytes
+int64_t f6_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    return cdiv(f6_image_bytes(M, K), 256) * 256 + f6_image_bytes(N, K);
+}
+
+// The FP6 tile for a shape, or -1 where the INT8-MFMA kernels are the
+// faster choice.  Back-to-back times, FP6 path (pre-pass included) vs INT8
+// MFMA: 8192^3 304 vs 371 us, 4096^3 56.6 vs 61.3 us (256 x 256), but
+// 2048^3 21.4 vs 13.7 us (128 x 128): with one round of tiles or fewer, the
+// pre-pass and its launch do not pay.
+int pick_f6(int64_t M, int64_t N, int64_t K) {
+    if (M == 0 || N == 0 || K < 1024) return -1;
+    if (cdiv(M, 256) * cdiv(N, 256) >= 192) return 0;
+    return -1;
+}
+
+int launch_f6(int cfg, int epi, int br, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+              const void *B, int64_t ldb, const float *scale_a, const float *scale_b, void *C, int64_t ldc,
+              void *ws, int64_t ws_bytes, void *stream) {
+    if (cfg < 0 || cfg >= kNumF6Configs) return PDGEMM_EINVAL_CFG;
+    int rc = validate(kI4, epi, br, M, N, K, A, lda, B, ldb, C, ldc, scale_a, scale_b);
+    if (rc != PDGEMM_OK) return rc;
+    if (M == 0 || N == 0) return PDGEMM_OK;
+    if (K == 0)   // nothing to convert: the K = 0 result of the INT8-MFMA kernels
+        return launch(kI4, pick(kI4, M, N, K), epi, br, M, N, K, A, lda, B, ldb, scale_a, scale_b, C, ldc,
+                      stream);
+    if (ws_bytes < 0) return PDGEMM_EWORKSPACE;
+    if (!ws) return PDGEMM_ENULL;
+    if (((uintptr_t)ws & 15) || ws_bytes < f6_workspace_bytes(M, N, K)) return PDGEMM_EWORKSPACE;
+
+    const F6Config &c = kF6Configs[cfg];
+    const int64_t nkb = f6_blocks(K);
+    const int64_t a_img = f6_image_bytes(M, K);
+    uint8_t *const img_a = static_cast<uint8_t *>(ws);
+    uint8_t *const img_b = img_a + cdiv(a_img, 256) * 256;
+
+    F6PackArgs pk;
+    pk.op[0] = {static_cast<const uint8_t *>(A), img_a, lda / 2, (int)M, (int)cdiv(M, 32), 0};
+    pk.op[1] = {static_cast<const uint8_t *>(B), img_b, ldb / 2, (int)N, (int)cdiv(N, 32), br == kBRow};
+    pk.K = (int)K;
+    pk.nkb = (int)nkb;
+    const int64_t blocks_a = cdiv(cdiv(M, 32) * nkb, 4);
+    const int64_t blocks_b = cdiv(cdiv(N, 32) * nkb, 4);
+    pk.blocks_a = (int)blocks_a;
+    F6Args args;
+    args.A = img_a;
+    args.B = img_b;
+    args.C = C;
+    args.scale_a = scale_a;
+    args.scale_b = scale_b;
+    args.a_bytes = a_img;
+    args.b_bytes = f6_image_bytes(N, K);
+    args.ldc = ldc;
+    args.M = (int)M;
+    args.N = (int)N;
+    args.nkb = (int)nkb;
+    args.tiles_m = (int)cdiv(M, c.bm);
+    args.tiles_n = (int)cdiv(N, c.bn);
+    const int64_t blocks = (int64_t)args.tiles_m * args.tiles_n;
+    const int threads = (c.bm / c.wm) * (c.bn / c.wn) * kWave;
+    // launches count their work-items in 32 bits
+    if (blocks * threads > (int64_t)UINT32_MAX || (blocks_a + blocks_b) * 256 > (int64_t)UINT32_MAX)
+        return PDGEMM_EINVAL_DIM;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *pargs[] = {&pk};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&f6_pack_kernel),
+                                   dim3((unsigned)(blocks_a + blocks_b)), dim3(256), pargs, 0, s);
+    if (e != hipSuccess) return (int)e;
+    void *gargs[] = {&args};
+    e = hipLaunchKernel(f6_kernel_ptr(cfg, epi), dim3((unsigned)blocks), dim3(threads), gargs, 0, s);
+    if (e != hipSuccess) return (int)e;
+    if (sync_check_enabled()) {
+        e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return (int)e;
+    }
+    return PDGEMM_OK;
+}
+
+// the workspace entry points: the FP6 path where it is picked, else the
+// INT8-MFMA kernels (which need no workspace)
+int launch_i4_ws(int epi, int br, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                 int64_t ldb, const float *scale_a, const float *scale_b, void *C, int64_t ldc, void *ws,
+                 int64_t ws_bytes, void *stream) {
+    const int f = pick_f6(M, N, K);
+    if (f < 0)
+        return launch(kI4, pick(kI4, M, N, K), epi, br, M, N, K, A, lda, B, ldb, scale_a, scale_b, C, ldc,
+                      stream);
+    return launch_f6(f, epi, br, M, N, K, A, lda, B, ldb, scale_a, scale_b, C, ldc, ws, ws_bytes, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1237,6 +1878,48 @@ int pdgemm_gemm_rowb_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K, con
                   stream);
 }
 
+int64_t pdgemm_i4_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0 || pick_f6(M, N, K) < 0) return 0;
+    return f6_workspace_bytes(M, N, K);
+}
+
+int pdgemm_i4_f6_pick(int64_t M, int64_t N, int64_t K) { return pick_f6(M, N, K); }
+
+int pdgemm_i4_f6_num_configs(void) { return kNumF6Configs; }
+
+int64_t pdgemm_i4_f6_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return 0;
+    return f6_workspace_bytes(M, N, K);
+}
+
+int gemm_i4_ws(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+               int32_t *C, int64_t ldc, void *workspace, int64_t workspace_bytes, void *stream) {
+    return launch_i4_ws(kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc, workspace,
+                        workspace_bytes, stream);
+}
+
+int gemm_i4_rowb_ws(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda, const uint8_t *B,
+                    int64_t ldb, int32_t *C, int64_t ldc, void *workspace, int64_t workspace_bytes,
+                    void *stream) {
+    return launch_i4_ws(kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc, workspace,
+                        workspace_bytes, stream);
+}
+
+int gemm_i4_dequant_ws(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda, const uint8_t *B,
+                       int64_t ldb, const float *scale_a, const float *scale_b, void *C, int64_t ldc,
+                       int out_f16, void *workspace, int64_t workspace_bytes, void *stream) {
+    return launch_i4_ws(out_f16 ? kDequantF16 : kDequantF32, kBCol, M, N, K, A, lda, B, ldb, scale_a, scale_b,
+                        C, ldc, workspace, workspace_bytes, stream);
+}
+
+int pdgemm_i4_f6_cfg(int cfg, int b_rowmajor, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                     const void *B, int64_t ldb, const float *scale_a, const float *scale_b, void *C,
+                     int64_t ldc, int out_f16, void *workspace, int64_t workspace_bytes, void *stream) {
+    const int epi = (scale_a || scale_b) ? (out_f16 ? kDequantF16 : kDequantF32) : kRaw;
+    return launch_f6(cfg, epi, b_rowmajor ? kBRow : kBCol, M, N, K, A, lda, B, ldb, scale_a, scale_b, C, ldc,
+                     workspace, workspace_bytes, stream);
+}
+
 int pdgemm_num_configs(void) { return kNumConfigs; }
 
 int pdgemm_pick_config(int prec, int64_t M, int64_t N, int64_t K) {
@@ -1265,10 +1948,11 @@ const char *pdgemm_strerror(int code) {
     case PDGEMM_EINVAL_I4: return "INT4 K, lda and ldb must be even";
     case PDGEMM_EALIGN: return "A and B must be 16-byte aligned, A and B rows must span a multiple of 16 bytes, C and the scales must be element-aligned";
     case PDGEMM_EINVAL_CFG: return "unknown precision or tile configuration, or a dequantizing epilogue for FP16";
+    case PDGEMM_EWORKSPACE: return "workspace smaller than pdgemm_i4_workspace_size(), negative, or not 16-byte aligned";
     default: return code > 0 ? hipGetErrorString((hipError_t)code) : "unknown error";
     }
 }
 
-int pdgemm_version(void) { return 100; }
+int pdgemm_version(void) { return 200; }
 
 }  // extern "C"

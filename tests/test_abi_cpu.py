@@ -60,7 +60,10 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("gemm_f16", "gemm_i8", "gemm_i4", "gemm_i8_dequant", "gemm_i4_dequant",
               "gemm_f16_rowb", "gemm_i8_rowb", "gemm_i4_rowb", "pdgemm_gemm_rowb_cfg",
-              "pdgemm_gemm_cfg", "pdgemm_dequant_cfg", "pdgemm_strerror", "pdgemm_version"):
+              "pdgemm_gemm_cfg", "pdgemm_dequant_cfg", "pdgemm_strerror", "pdgemm_version",
+              "gemm_i4_ws", "gemm_i4_rowb_ws", "gemm_i4_dequant_ws", "pdgemm_i4_workspace_size",
+              "pdgemm_i4_f6_cfg", "pdgemm_i4_f6_pick", "pdgemm_i4_f6_num_configs",
+              "pdgemm_i4_f6_workspace_bytes"):
         assert n in names
 
 
@@ -243,7 +246,7 @@ def test_strerror_and_version(lib):
         msg = lib.pdgemm_strerror(code)
         assert msg and len(msg) > 3, name
     assert lib.pdgemm_strerror(-999)
-    assert lib.pdgemm_version() >= 100
+    assert lib.pdgemm_version() >= 200
 
 
 def test_binding_imports_and_marshals_without_gpu():
@@ -319,3 +322,70 @@ def test_pick_weighs_the_last_partial_round(lib):
                 bm, bn = tile(prec, m, n, 4096)
                 if -(-m // 64) * -(-n // 64) >= 256:
                     assert -(-m // bm) * -(-n // bn) >= 192, (prec, m, n)
+
+
+@pytest.fixture(scope="module")
+def wslib(lib):
+    i64, p, i = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    for name in ("gemm_i4_ws", "gemm_i4_rowb_ws"):
+        getattr(lib, name).argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p]
+        getattr(lib, name).restype = i
+    lib.gemm_i4_dequant_ws.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, p, i64, i, p, i64, p]
+    lib.gemm_i4_dequant_ws.restype = i
+    lib.pdgemm_i4_f6_cfg.argtypes = [i, i, i64, i64, i64, p, i64, p, i64, p, p, p, i64, i, p, i64, p]
+    lib.pdgemm_i4_f6_cfg.restype = i
+    for name in ("pdgemm_i4_workspace_size", "pdgemm_i4_f6_workspace_bytes"):
+        getattr(lib, name).argtypes = [i64, i64, i64]
+        getattr(lib, name).restype = i64
+    lib.pdgemm_i4_f6_pick.argtypes = [i64, i64, i64]
+    lib.pdgemm_i4_f6_pick.restype = i
+    return lib
+
+
+def f6_bytes(M, N, K):
+    """The workspace size rule the header states, restated: two images of
+    32-row groups x 128-value K blocks (padded to a multiple of 3) of 3072
+    bytes, B's starting at the next multiple of 256 bytes after A's."""
+    cd = lambda a, b: -(-a // b)
+    blocks = cd(cd(K, 128), 3) * 3
+    img = lambda rows: cd(rows, 32) * blocks * 3072
+    return cd(img(M), 256) * 256 + img(N)
+
+
+def test_workspace_sizes(wslib):
+    L = wslib
+    for M, N, K in ((8192, 8192, 8192), (4096, 4096, 4096), (4000, 3000, 1030), (5000, 777, 131070)):
+        assert L.pdgemm_i4_f6_workspace_bytes(M, N, K) == f6_bytes(M, N, K)
+        want = f6_bytes(M, N, K) if L.pdgemm_i4_f6_pick(M, N, K) >= 0 else 0
+        assert L.pdgemm_i4_workspace_size(M, N, K) == want
+    # the FP6 path takes large products only; small ones need no workspace
+    assert L.pdgemm_i4_f6_pick(8192, 8192, 8192) == 0 and L.pdgemm_i4_f6_pick(4096, 4096, 4096) == 0
+    for shape in ((2048, 2048, 2048), (64, 8192, 8192), (8192, 8192, 512), (0, 10, 10)):
+        assert L.pdgemm_i4_f6_pick(*shape) == -1 and L.pdgemm_i4_workspace_size(*shape) == 0
+    assert L.pdgemm_i4_workspace_size(-1, 5, 5) == 0
+
+
+def test_workspace_errors_before_any_hip_call(wslib):
+    L, c = wslib, codes()
+    M = N = K = 4096
+    need = L.pdgemm_i4_workspace_size(M, N, K)
+    A, B, C, ws = 0x10000, 0x20000, 0x30000, 0x100000
+    args = lambda w, n: (M, N, K, A, K, B, K, C, N, w, n, None)
+    assert L.gemm_i4_ws(*args(None, need)) == c["PDGEMM_ENULL"]
+    assert L.gemm_i4_ws(*args(ws, need - 1)) == c["PDGEMM_EWORKSPACE"]
+    assert L.gemm_i4_ws(*args(ws + 8, need)) == c["PDGEMM_EWORKSPACE"]
+    assert L.gemm_i4_ws(*args(ws, -5)) == c["PDGEMM_EWORKSPACE"]
+    assert L.gemm_i4_rowb_ws(*args(ws, need - 16)) == c["PDGEMM_EWORKSPACE"]
+    # argument errors come first, as for gemm_i4
+    assert L.gemm_i4_ws(M, N, K + 1, A, K + 1, B, K + 1, C, N, ws, need, None) == c["PDGEMM_EINVAL_I4"]
+    assert L.gemm_i4_ws(M, N, K, A, K, B, K, C, N - 1, ws, need, None) == c["PDGEMM_EINVAL_LD"]
+    assert L.gemm_i4_dequant_ws(M, N, K, A, K, B, K, None, None, C, N, 0, ws, need, None) == c["PDGEMM_ENULL"]
+    assert L.gemm_i4_dequant_ws(M, N, K, A, K, B, K, 0x40000, 0x50000, C, N, 1, ws, 16, None) == \
+        c["PDGEMM_EWORKSPACE"]
+    # the explicit FP6 tiles: unknown tile, then the workspace rule for any shape
+    assert L.pdgemm_i4_f6_cfg(7, 0, M, N, K, A, K, B, K, None, None, C, N, 0, ws, need, None) == \
+        c["PDGEMM_EINVAL_CFG"]
+    small = f6_bytes(300, 200, 1030)
+    assert L.pdgemm_i4_f6_cfg(1, 0, 300, 200, 1030, A, 1056, B, 1056, None, None, C, 200, 0, ws, small - 1,
+                              None) == c["PDGEMM_EWORKSPACE"]
+    assert L.pdgemm_strerror(c["PDGEMM_EWORKSPACE"]).decode().startswith("workspace")

@@ -311,3 +311,45 @@ def test_operand_offsets_fit_32_bits(prec, cfg):
     cpr_bytes = ld                            # a row of B: every chunk of it may be addressed
     assert (slice_rows - 1) * ld + cpr_bytes <= limit + 1
     assert slice_rows * ld <= 2 ** 30, "a slice of a row-major B stage spans at most 1 GiB"
+
+
+# ---- INT4 on the FP6 cores ----
+
+def e2m3_value(code: int) -> float:
+    """The OCP e2m3 (FP6) value of a 6-bit code: sign, 2 exponent bits of bias 1, 3 mantissa bits;
+    exponent 0 holds the subnormals m / 8."""
+    sign = -1.0 if code & 0x20 else 1.0
+    e, m = (code >> 3) & 3, code & 7
+    return sign * (m / 8.0 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 1))
+
+
+def test_int4_values_are_exact_e2m3_codes():
+    # the code of v / 8 for an INT4 value v is sign << 5 | |v|: |v| = 0..7 are the
+    # subnormals, |v| = 8 is exponent 1 with mantissa 0 (1.0)
+    for v in range(-8, 8):
+        code = (0x20 if v < 0 else 0) | abs(v)
+        assert code < 64 and e2m3_value(code) == v / 8.0
+    # and with block scales 2^3 on both operands, a product is the integer a * b
+    for a in range(-8, 8):
+        for b in range(-8, 8):
+            ca, cb = (0x20 if a < 0 else 0) | abs(a), (0x20 if b < 0 else 0) | abs(b)
+            assert e2m3_value(ca) * 8 * e2m3_value(cb) * 8 == a * b
+
+
+def tswizzle(r: int) -> int:
+    return (r >> 3) & 3
+
+
+def test_fp6_tail_reads_are_bank_conflict_free():
+    # the 32 lanes of a half-wave read one 8-byte slot of 32 consecutive rows of 32 bytes;
+    # row r at position p covers the 4-byte banks 8 (r % 8) + 2 p and + 1 of 64
+    for base in range(0, 512, 32):
+        for c in range(4):
+            banks = set()
+            for r in range(base, base + 32):
+                p = c ^ tswizzle(r)
+                banks |= {(8 * (r % 8) + 2 * p) % 64, (8 * (r % 8) + 2 * p + 1) % 64}
+            assert len(banks) == 64
+    # and each row's four slots are a permutation of its positions
+    for r in range(64):
+        assert sorted(c ^ tswizzle(r) for c in range(4)) == [0, 1, 2, 3]
