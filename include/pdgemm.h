@@ -216,6 +216,24 @@ int pdgemm_i4_f6_num_configs(void);
 int pdgemm_i4_f6_pick(int64_t M, int64_t N, int64_t K);
 int64_t pdgemm_i4_f6_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+/* gemm_i4 for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * It is gemm_i4_ws with the workspace taken from a fixed file-scope device
+ * array of pdgemm_i4_noalloc_max_bytes() bytes (128 MiB, enough for
+ * M = N = K = 8192), of which each GPU the library runs on holds one copy
+ * until the process ends; nothing is allocated or freed by the call.
+ * Shapes that the workspace entry points run on the INT8-MFMA kernels do not
+ * touch the array.  A shape whose FP6 workspace would exceed the array
+ * returns PDGEMM_EWORKSPACE, before any launch.  Every call on a GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, other
+ * threads) race and give undefined results; calls ordered on one stream are
+ * safe.  The first call on a device looks the array's address up
+ * (hipGetSymbolAddress) and may return its hipError_t.  Arguments, results
+ * and other errors as gemm_i4. */
+int gemm_i4_noalloc(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+                    const uint8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream);
+int64_t pdgemm_i4_noalloc_max_bytes(void);
+
 /* Precision ids and tile configurations, for the calls below. */
 #define PDGEMM_PREC_F16 0
 #define PDGEMM_PREC_I8 1

@@ -85,6 +85,10 @@ lib.gemm_i4_dequant_ws.restype = _i
 lib.pdgemm_i4_f6_cfg.argtypes = [_i, _i, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i64, _i, _p,
                                  _i64, _p]
 lib.pdgemm_i4_f6_cfg.restype = _i
+lib.gemm_i4_noalloc.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+lib.gemm_i4_noalloc.restype = _i
+lib.pdgemm_i4_noalloc_max_bytes.argtypes = []
+lib.pdgemm_i4_noalloc_max_bytes.restype = _i64
 lib.pdgemm_strerror.argtypes = [_i]
 lib.pdgemm_strerror.restype = ctypes.c_char_p
 lib.pdgemm_version.argtypes = []
@@ -311,6 +315,33 @@ def gemm_i4(A: torch.Tensor, Bt: torch.Tensor, K: int | None = None,
     elif out.dtype != torch.int32:
         raise TypeError("gemm_i4 writes an int32 output")
     return _call(PREC_I4, A, Bt, out, K, lda, ldb, stream, cfg, workspace=workspace, f6cfg=f6cfg)
+
+
+def gemm_i4_noalloc(A: torch.Tensor, Bt: torch.Tensor, K: int | None = None,
+                    out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """gemm_i4 through the allocation-free entry point (the library's own fixed
+    workspace; calls that overlap on one GPU race)."""
+    if A.dtype != torch.uint8 or Bt.dtype != torch.uint8:
+        raise TypeError("gemm_i4_noalloc takes uint8 tensors of packed 4-bit values")
+    if K is None:
+        K = 2 * A.shape[1]
+    if A.shape[1] * 2 < K or Bt.shape[1] * 2 < K:
+        raise ValueError("packed operands hold fewer than K values per row")
+    lda, ldb = 2 * _row_major_2d(A, "A"), 2 * _row_major_2d(Bt, "Bt")
+    if out is None:
+        out = torch.empty((A.shape[0], Bt.shape[0]), dtype=torch.int32, device=A.device)
+    elif out.dtype != torch.int32:
+        raise TypeError("gemm_i4_noalloc writes an int32 output")
+    M, N = A.shape[0], Bt.shape[0]
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must have shape {(M, N)}")
+    if A.device != out.device or Bt.device != out.device:
+        raise ValueError("operands and out must be on the same GPU")
+    rc = lib.gemm_i4_noalloc(M, N, K, A.data_ptr(), lda, Bt.data_ptr(), ldb, out.data_ptr(),
+                             _row_major_2d(out, "out"), _stream(stream))
+    if rc != 0:
+        raise PdgemmError(rc)
+    return out
 
 
 _DTYPES = {"f16": (torch.float16, torch.float32, PREC_F16), "i8": (torch.int8, torch.int32, PREC_I8),

@@ -63,6 +63,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "pdgemm.h"
@@ -1803,6 +1804,49 @@ int launch_i4_ws(int epi, int br, int64_t M, int64_t N, int64_t K, const void *A
     return launch_f6(f, epi, br, M, N, K, A, lda, B, ldb, scale_a, scale_b, C, ldc, ws, ws_bytes, stream);
 }
 
+// ---- the allocation-free INT4 entry point ----
+//
+// gemm_i4_noalloc serves callers that cannot allocate (code under graph
+// capture, serving loops, harnesses that forbid it): its workspace is a
+// fixed file-scope device array, one copy per GPU, held until the process
+// ends.  Host code never passes the array's name to a kernel (in host code
+// it is a stand-in, not a device address): each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr int64_t kScratchBytes = int64_t(128) << 20;   // 128 MiB: enough for 8192^3
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// This device's copy of `scratch` (its address), looked up on first use.
+int scratch_for(void *stream, void **out) {
+    int dev = 0;
+    hipError_t e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxDevices) return PDGEMM_EINVAL_CFG;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return (int)e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return (int)e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return (int)e;
+        if (e2 != hipSuccess) return (int)e2;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return PDGEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1919,6 +1963,24 @@ int pdgemm_i4_f6_cfg(int cfg, int b_rowmajor, int64_t M, int64_t N, int64_t K, c
     return launch_f6(cfg, epi, b_rowmajor ? kBRow : kBCol, M, N, K, A, lda, B, ldb, scale_a, scale_b, C, ldc,
                      workspace, workspace_bytes, stream);
 }
+
+int gemm_i4_noalloc(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda, const uint8_t *B,
+                    int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
+    // shapes the INT8-MFMA kernels take need no workspace
+    if (pick_f6(M, N, K) < 0)
+        return launch(kI4, pick(kI4, M, N, K), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
+                      stream);
+    const int rc = validate(kI4, kRaw, kBCol, M, N, K, A, lda, B, ldb, C, ldc, nullptr, nullptr);
+    if (rc != PDGEMM_OK) return rc;
+    if (f6_workspace_bytes(M, N, K) > kScratchBytes) return PDGEMM_EWORKSPACE;
+    void *ws = nullptr;
+    const int e = scratch_for(stream, &ws);
+    if (e != PDGEMM_OK) return e;
+    return launch_f6(pick_f6(M, N, K), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc, ws,
+                     kScratchBytes, stream);
+}
+
+int64_t pdgemm_i4_noalloc_max_bytes(void) { return kScratchBytes; }
 
 int pdgemm_num_configs(void) { return kNumConfigs; }
 
