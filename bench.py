@@ -105,6 +105,9 @@ def parse():
                     help="skip the non-square (small M) measurement")
     ap.add_argument("--no-layout", action="store_true",
                     help="skip the row-major-B measurement")
+    ap.add_argument("--cfg", type=int, default=None,
+                    help="run every GEMM on this INT8-MFMA-path tile configuration (INT4 without the "
+                         "FP6 path), e.g. 8 for the 4-wave form of the 256 x 256 tile (for profiling)")
     ap.add_argument("--no-c3", action="store_true",
                     help="skip the FP16 8192^3 N(0,1)/sqrt(K) workload")
     ap.add_argument("--detail", metavar="PATH",
@@ -251,7 +254,7 @@ def shape_roofline(prec, M, N, K, ms):
             "gbs": round(gbs, 1)}
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_n8192_hbm_counters.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_n4096_n8192_hbm_counters.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "precision_dense_gemm_amd", "csrc", "pdgemm.hip")
 
 
@@ -352,13 +355,15 @@ def main():
     # INT4 runs through the workspace entry point: on the FP6 cores where the
     # library picks that path (large products), else on the INT8 MFMA; the
     # workspace is allocated here, once, outside any timed region
-    workspaces = {(prec, n): pd.i4_workspace(n, n, n, dev) for prec, n, *_ in work if prec == "i4"}
-    i4_path = {n: ("fp6" if pd.i4_f6_pick(n, n, n) >= 0 else "i8-mfma") for p_, n, *_ in work if p_ == "i4"}
+    workspaces = {} if args.cfg is not None else {
+        (prec, n): pd.i4_workspace(n, n, n, dev) for prec, n, *_ in work if prec == "i4"}
+    i4_path = {n: ("fp6" if (args.cfg is None and pd.i4_f6_pick(n, n, n) >= 0) else "i8-mfma")
+               for p_, n, *_ in work if p_ == "i4"}
 
     def ws_of(prec, n):
         return workspaces.get((prec, n))
 
-    launchers = {(prec, n): pd.prepare(prec, Ad, Bd, C, K=n, workspace=ws_of(prec, n))
+    launchers = {(prec, n): pd.prepare(prec, Ad, Bd, C, K=n, workspace=ws_of(prec, n), cfg=args.cfg)
                  for prec, n, Ad, Bd, C in work}
     torch.cuda.synchronize()
 
@@ -463,7 +468,7 @@ def main():
         return float(np.median(times))
 
     def plain(prec, n, Ad, Bd, C):
-        return lambda: pd.prepare(prec, Ad, Bd, C, K=n, workspace=ws_of(prec, n))
+        return lambda: pd.prepare(prec, Ad, Bd, C, K=n, workspace=ws_of(prec, n), cfg=args.cfg)
 
     # Cold-cache timing of the small GEMMs (outside the step): before each
     # launch a 512 MiB fill evicts the L2s and the 256 MB MALL, so the operands

@@ -1481,6 +1481,7 @@ constexpr Config kConfigs[] = {
     {128, 64, 64, 32, 8, 1, 3},     // 5: between 1 and 2 (e.g. M = 256)
     {64, 32, 64, 32, 8, 4, 3},      // 6: K split over 4 waves, 64 rows (e.g. M = 64 of a wide product)
     {128, 128, 64, 64, 8, 1, 3},    // 7: 1 with three stages, for at most one round of tiles
+    {256, 256, 128, 128, 4, 1, 2},  // 8: 0 with 4 waves of 128 x 128 (never picked: kept to compare)
 };
 
 // Tiles without K split, largest first: the order in which pick() tries them.
@@ -1504,6 +1505,7 @@ const void *kernel_ptr(int cfg) {
     case 5: return kernel_for<P, 5, E, BR>();
     case 6: return kernel_for<P, 6, E, BR>();
     case 7: return kernel_for<P, 7, E, BR>();
+    case 8: return kernel_for<P, 8, E, BR>();
     default: return nullptr;
     }
 }
@@ -1550,11 +1552,12 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // (INT8, INT4): the median of five alternated back-to-back timings on a
 // product that gives every one of them whole rounds of workgroups
 // (M = K = 8192, N = 6144); only the ratios within a row matter.  0 = not a
-// candidate (the K-split tiles, and 7, which stands in for 1).
+// candidate (the K-split tiles, 7, which stands in for 1, and 8, the 4-wave
+// form of 0, slower on INT4 and within noise of 0 otherwise).
 constexpr int kTileRate[3][kNumConfigs] = {
-    {1299, 1113, 686, 0, 1189, 855, 0, 0},    // FP16
-    {2541, 2178, 1374, 0, 2293, 1669, 0, 0},  // INT8
-    {2789, 2563, 1868, 0, 2610, 2033, 0, 0},  // INT4
+    {1299, 1113, 686, 0, 1189, 855, 0, 0, 0},    // FP16
+    {2541, 2178, 1374, 0, 2293, 1669, 0, 0, 0},  // INT8
+    {2789, 2563, 1868, 0, 2610, 2033, 0, 0, 0},  // INT4
 };
 
 // When the 64 x 64 tile fills the chip (at least one workgroup per CU), a
