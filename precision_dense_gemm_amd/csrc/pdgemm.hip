@@ -1549,28 +1549,32 @@ bool sync_check_enabled() {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Steady throughput of each tile without K split, in TFLOP/s (FP16) or TOP/s
-// (INT8, INT4): the median of five alternated back-to-back timings on a
-// product that gives every one of them whole rounds of workgroups
-// (M = K = 8192, N = 6144); only the ratios within a row matter.  0 = not a
-// candidate (the K-split tiles, 7, which stands in for 1, and 8, the 4-wave
-// form of 0, slower on INT4 and within noise of 0 otherwise).
+// (INT8, INT4): back-to-back timings (HIP graphs of at least 20 ms, medians of
+// three alternated rounds, mean of two GPUs) on a product that gives every
+// one of them whole rounds of workgroups (M = K = 8192, N = 6144); only the
+// ratios within a row matter.  0 = not a candidate (the K-split tiles, 7,
+// which stands in for 1, and 8, the 4-wave form of 0, slower than 0 at
+// N = 8192).
 constexpr int kTileRate[3][kNumConfigs] = {
-    {1299, 1113, 686, 0, 1189, 855, 0, 0, 0},    // FP16
-    {2541, 2178, 1374, 0, 2293, 1669, 0, 0, 0},  // INT8
-    {2789, 2563, 1868, 0, 2610, 2033, 0, 0, 0},  // INT4
+    {1267, 1019, 703, 0, 1126, 778, 0, 0, 0},    // FP16
+    {2449, 2060, 1329, 0, 2171, 1616, 0, 0, 0},  // INT8
+    {2824, 2440, 1863, 0, 2499, 2021, 0, 0, 0},  // INT4
 };
 
 // When the 64 x 64 tile fills the chip (at least one workgroup per CU), a
-// time model chooses among the tiles that give at least three quarters of
-// the CUs one: the busiest CU sets the time, so a product of T tiles takes
-// T / 256 rounds, each of which costs the tile's area over its throughput.
-// A partial last round costs 0.6 + 0.4 * (its fill) of a full one, since the
-// fewer CUs run, the higher their clock.  The cheapest tile wins, the larger
-// one on a tie.  (E.g. 196 tiles of 256 x 256 rather than 392 of 256 x 128
-// at 3584^3, and 128 x 128 for INT4 at 6144^3, where 256 x 256 would leave a
-// last round a quarter full.)  When even the 64 x 64 tile leaves CUs idle
-// (small M or N), a K-split tile puts 4 waves on each of up to 4 times as
-// many tiles.  128 x 128 with at most one tile per CU takes configuration 7.
+// time model chooses among the tiles that give at least half of the CUs
+// one: the busiest CU sets the time, so a product of T tiles takes T / 256
+// rounds, each of which costs the tile's area over its throughput.  A
+// partial last round costs 0.35 + 0.65 * (its fill) of a full one: the fewer
+// CUs run, the higher their clock and the more L2 and HBM bandwidth each
+// gets.  The cheapest tile wins, the larger one on a tie.  (E.g. 144 tiles of
+// 256 x 256 rather than 576 of 128 x 128 at 3072^3, 384 of 256 x 256 rather
+// than 768 of 256 x 128 at 8192 x 3072 x 8192.)  Fitted to 69 shapes from
+// 1024^3 to 12288 x 4096 x 4096 in three precisions on two GPUs: 0.2-0.3%
+// slower than the fastest tile on average, at most 7.5% (INT4 1536^3).  When
+// even the 64 x 64 tile leaves CUs idle (small M or N), a K-split tile puts
+// 4 waves on each of up to 4 times as many tiles.  128 x 128 with at most
+// one tile per CU takes configuration 7.
 int pick(int prec, int64_t M, int64_t N, int64_t K) {
     (void)K;
     auto tiles = [&](int c) { return cdiv(M, kConfigs[c].bm) * cdiv(N, kConfigs[c].bn); };
@@ -1579,9 +1583,9 @@ int pick(int prec, int64_t M, int64_t N, int64_t K) {
         double best_cost = 0;
         for (int c : kPickOrder) {
             const int64_t t = tiles(c);
-            if (kTileRate[prec][c] == 0 || t < 192) continue;
+            if (kTileRate[prec][c] == 0 || t < 128) continue;
             const double partial = double(t % 256) / 256;
-            const double rounds = double(t / 256) + (partial > 0 ? 0.6 + 0.4 * partial : 0.0);
+            const double rounds = double(t / 256) + (partial > 0 ? 0.35 + 0.65 * partial : 0.0);
             const double cost = rounds * kConfigs[c].bm * kConfigs[c].bn / kTileRate[prec][c];
             if (best < 0 || cost < best_cost) {
                 best = c;

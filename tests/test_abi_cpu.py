@@ -304,24 +304,28 @@ def test_pick_weighs_the_last_partial_round(lib):
         return info[lib.pdgemm_pick_config(prec, m, n, k)]
     for prec in range(3):
         assert tile(prec, 3584, 3584, 3584) == (256, 256)     # 196 tiles, not 392 of 256 x 128
+        assert tile(prec, 3072, 3072, 3072) == (256, 256)     # 144 tiles, not 2.25 rounds of 128 x 128
         assert tile(prec, 1792, 8192, 8192) == (256, 256)     # 224 tiles
         assert tile(prec, 8192, 8192, 8192) == (256, 256)
         assert tile(prec, 12288, 4096, 4096) == (256, 256)
-        assert tile(prec, 8192, 3072, 8192) == (256, 128)     # 384 tiles of 256 x 256: 1.5 rounds
-        assert tile(prec, 1024, 8192, 8192) == (256, 128)
-    assert tile(0, 6144, 6144, 6144) == (256, 128)            # 576 tiles of 256 x 256: 2.25 rounds
-    for n in (5120, 6144, 7168):
-        assert tile(2, n, n, n) == (128, 128)                 # INT4: two workgroups per CU
+        assert tile(prec, 5120, 5120, 5120) == (256, 256)     # 400 tiles: 1.56 rounds
+        assert tile(prec, 7168, 7168, 7168) == (256, 256)
+        assert tile(prec, 1024, 8192, 8192) == (256, 128)     # 128 tiles of 256 x 256 would idle half the CUs
+        assert tile(prec, 1536, 4096, 8192) == (256, 128)
+    for prec in (0, 1):
+        assert tile(prec, 6144, 6144, 6144) == (256, 256)     # 2.25 rounds beat 4.5 of 256 x 128
     # 128 x 128 at one tile per CU takes its three-stage variant; with more tiles, two stages
     three_stage = lib.pdgemm_pick_config(0, 2048, 2048, 2048)
-    assert info[three_stage] == (128, 128) and three_stage != lib.pdgemm_pick_config(2, 6144, 6144, 6144)
-    # whenever the 64 x 64 tile fills the chip, the pick gives at least three quarters of the CUs a tile
+    assert info[three_stage] == (128, 128)
+    assert info[lib.pdgemm_pick_config(2, 10240, 2048, 4096)] == (128, 128)   # INT4: 1280 tiles
+    assert lib.pdgemm_pick_config(2, 10240, 2048, 4096) != three_stage
+    # whenever the 64 x 64 tile fills the chip, the pick gives at least half of the CUs a tile
     for prec in range(3):
         for m in range(512, 12289, 448):
             for n in range(512, 12289, 704):
                 bm, bn = tile(prec, m, n, 4096)
                 if -(-m // 64) * -(-n // 64) >= 256:
-                    assert -(-m // bm) * -(-n // bn) >= 192, (prec, m, n)
+                    assert -(-m // bm) * -(-n // bn) >= 128, (prec, m, n)
 
 
 @pytest.fixture(scope="module")
