@@ -116,10 +116,76 @@ def parse():
                     help="rows of C per GEMM for the CPU baseline (default 192)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device copy, the reference for HBM counter scaling")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="time every non-split tile configuration on 23 shapes x 3 precisions "
+                         "(back to back, alternated) and report the picker's loss, then exit")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="summarise a rocprofv3 kernel_trace.csv (or counter_collection.csv) "
                          "per kernel and grid size, then exit (no GPU needed)")
     return ap.parse_args()
+
+
+TILE_SWEEP_SHAPES = [(n, n, n) for n in (1024, 1536, 2048, 2560, 3072, 3584, 4096, 5120, 6144, 7168, 8192)] + [
+    (8192, 6144, 8192), (4096, 8192, 4096), (12288, 4096, 4096), (2048, 8192, 8192), (1024, 8192, 8192),
+    (6144, 4096, 8192), (3072, 8192, 4096), (8192, 3072, 8192), (1536, 4096, 8192), (5120, 3072, 4096),
+    (10240, 2048, 4096), (2560, 6144, 4096)]
+
+
+def tile_sweep():
+    """Every tile configuration without K split (and the picker's choice) on
+    the shapes the picker's time model was fitted to: back-to-back time of a
+    HIP graph of at least 20 ms of launches, medians of three alternated
+    rounds.  Prints one line per shape and the picker's mean and worst loss."""
+    import torch
+    import precision_dense_gemm_amd as pd
+    dev = torch.device("cuda:0")
+    cfgs = [0, 4, 1, 5, 2, 7, 8]
+
+    def graph_time(make, reps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            go = make()   # binds the capture stream
+            for _ in range(reps):
+                go()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) / reps * 1e3
+
+    losses = []
+    for prec in ("f16", "i8", "i4"):
+        for (M, N, K) in TILE_SWEEP_SHAPES:
+            if prec == "f16":
+                A = (torch.rand((M, K), device=dev) * 2 - 1).half()
+                B = (torch.rand((N, K), device=dev) * 2 - 1).half()
+                C = torch.empty((M, N), dtype=torch.float32, device=dev)
+            elif prec == "i8":
+                A = torch.randint(-128, 128, (M, K), dtype=torch.int8, device=dev)
+                B = torch.randint(-128, 128, (N, K), dtype=torch.int8, device=dev)
+                C = torch.empty((M, N), dtype=torch.int32, device=dev)
+            else:
+                A = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device=dev)
+                B = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=dev)
+                C = torch.empty((M, N), dtype=torch.int32, device=dev)
+            reps = max(10, min(200, int(3e13 / (2.0 * M * N * K))))
+            ts = {c: [] for c in cfgs}
+            for _ in range(3):
+                for c in cfgs:
+                    ts[c].append(graph_time(lambda c=c: pd.prepare(prec, A, B, C, K=K, cfg=c), reps))
+            med = {c: sorted(v)[1] for c, v in ts.items()}
+            pick = pd.pick_config({"f16": 0, "i8": 1, "i4": 2}[prec], M, N, K)
+            best = min((c for c in cfgs if c != 8), key=med.get)
+            loss = med[pick] / med[best] - 1
+            losses.append(loss)
+            print(f"{prec} {M}x{N}x{K} pick={pick} best={best} loss={100 * loss:.1f}% | "
+                  + " ".join(f"{c}:{med[c]:.2f}" for c in cfgs), flush=True)
+            del A, B, C
+    print(f"picker loss over {len(losses)} shapes: mean {100 * sum(losses) / len(losses):.2f}%, "
+          f"worst {100 * max(losses):.1f}%", flush=True)
 
 
 def trace_summary(path):
@@ -301,6 +367,9 @@ def main():
     args = parse()
     if args.trace_summary:
         trace_summary(args.trace_summary)
+        return
+    if args.tile_sweep:
+        tile_sweep()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
