@@ -134,8 +134,8 @@ TILE_SWEEP_SHAPES = [(n, n, n) for n in (1024, 1536, 2048, 2560, 3072, 3584, 409
 def tile_sweep():
     """Every tile configuration without K split (and the picker's choice) on
     the shapes the picker's time model was fitted to: back-to-back time of a
-    HIP graph of at least 20 ms of launches, medians of three alternated
-    rounds.  Prints one line per shape and the picker's mean and worst loss."""
+    HIP graph of 10-200 launches (about 3e13 flops, at least 10), medians of
+    three alternated rounds.  Prints one line per shape and the picker's mean and worst loss."""
     import torch
     import precision_dense_gemm_amd as pd
     dev = torch.device("cuda:0")

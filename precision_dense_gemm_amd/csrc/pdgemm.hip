@@ -1549,7 +1549,7 @@ bool sync_check_enabled() {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Steady throughput of each tile without K split, in TFLOP/s (FP16) or TOP/s
-// (INT8, INT4): back-to-back timings (HIP graphs of at least 20 ms, medians of
+// (INT8, INT4): back-to-back timings (HIP graphs of about 25 ms, medians of
 // three alternated rounds, mean of two GPUs) on a product that gives every
 // one of them whole rounds of workgroups (M = K = 8192, N = 6144); only the
 // ratios within a row matter.  0 = not a candidate (the K-split tiles, 7,
