@@ -1836,7 +1836,7 @@ int scratch_for(void *stream, void **out) {
     int dev = 0;
     hipError_t e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev);
     if (e != hipSuccess) return (int)e;
-    if (dev < 0 || dev >= kMaxDevices) return PDGEMM_EINVAL_CFG;
+    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;   // beyond the address table
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (!g_scratch_ptr[dev]) {
         int cur = 0;
