@@ -228,8 +228,9 @@ int64_t pdgemm_i4_f6_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * that GPU's array: calls that overlap on one GPU (other streams, other
  * threads) race and give undefined results; calls ordered on one stream are
  * safe.  The first call on a device looks the array's address up
- * (hipGetSymbolAddress) and may return its hipError_t.  Arguments, results
- * and other errors as gemm_i4. */
+ * (hipGetSymbolAddress) and may return its hipError_t; devices with an index
+ * of 64 or more return hipErrorInvalidDevice.  Arguments, results and other
+ * errors as gemm_i4. */
 int gemm_i4_noalloc(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
                     const uint8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream);
 int64_t pdgemm_i4_noalloc_max_bytes(void);
