@@ -1482,6 +1482,7 @@ constexpr Config kConfigs[] = {
     {64, 32, 64, 32, 8, 4, 3},      // 6: K split over 4 waves, 64 rows (e.g. M = 64 of a wide product)
     {128, 128, 64, 64, 8, 1, 3},    // 7: 1 with three stages, for at most one round of tiles
     {256, 256, 128, 128, 4, 1, 2},  // 8: 0 with 4 waves of 128 x 128 (never picked: kept to compare)
+    {64, 64, 64, 64, 8, 4, 2},      // 9: 2 with K split over 4 waves, for one round of tiles and long K
 };
 
 // Tiles without K split, largest first: the order in which pick() tries them.
@@ -1506,6 +1507,7 @@ const void *kernel_ptr(int cfg) {
     case 6: return kernel_for<P, 6, E, BR>();
     case 7: return kernel_for<P, 7, E, BR>();
     case 8: return kernel_for<P, 8, E, BR>();
+    case 9: return kernel_for<P, 9, E, BR>();
     default: return nullptr;
     }
 }
@@ -1553,12 +1555,12 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // three alternated rounds, mean of two GPUs) on a product that gives every
 // one of them whole rounds of workgroups (M = K = 8192, N = 6144); only the
 // ratios within a row matter.  0 = not a candidate (the K-split tiles, 7,
-// which stands in for 1, and 8, the 4-wave form of 0, slower than 0 at
-// N = 8192).
+// which stands in for 1, 9, which stands in for 2, and 8, the 4-wave form
+// of 0, slower than 0 at N = 8192).
 constexpr int kTileRate[3][kNumConfigs] = {
-    {1267, 1019, 703, 0, 1126, 778, 0, 0, 0},    // FP16
-    {2449, 2060, 1329, 0, 2171, 1616, 0, 0, 0},  // INT8
-    {2824, 2440, 1863, 0, 2499, 2021, 0, 0, 0},  // INT4
+    {1267, 1019, 703, 0, 1126, 778, 0, 0, 0, 0},    // FP16
+    {2449, 2060, 1329, 0, 2171, 1616, 0, 0, 0, 0},  // INT8
+    {2824, 2440, 1863, 0, 2499, 2021, 0, 0, 0, 0},  // INT4
 };
 
 // When the 64 x 64 tile fills the chip (at least one workgroup per CU), a
@@ -1576,7 +1578,6 @@ constexpr int kTileRate[3][kNumConfigs] = {
 // 4 waves on each of up to 4 times as many tiles.  128 x 128 with at most
 // one tile per CU takes configuration 7.
 int pick(int prec, int64_t M, int64_t N, int64_t K) {
-    (void)K;
     auto tiles = [&](int c) { return cdiv(M, kConfigs[c].bm) * cdiv(N, kConfigs[c].bn); };
     if (tiles(2) >= 256) {
         int best = -1;
@@ -1594,7 +1595,15 @@ int pick(int prec, int64_t M, int64_t N, int64_t K) {
         }
         // the 64 x 64 tile is always a candidate here.  At most one 128 x 128
         // tile per CU: the three-stage variant (7), as a CU holds one anyway
-        return best == 1 && tiles(1) <= 256 ? 7 : best;
+        if (best == 1 && tiles(1) <= 256) return 7;
+        // One round of 64 x 64 tiles over a long K (e.g. 128 x 8192 x 8192):
+        // four waves on K slices of each tile, with no stage barrier, beat
+        // four waves on its quarters by 8-23% when a row of K values is a
+        // whole number of 128-byte lines; at K <= 4096, or with rows that end
+        // inside a line, the reduction of the partial tiles costs more.
+        const int64_t k_bytes = prec == kF16 ? 2 * K : (prec == kI8 ? K : K / 2);
+        if (best == 2 && tiles(2) <= 288 && K >= 8192 && k_bytes % 128 == 0) return 9;
+        return best;
     }
     // K split: 64 x 32 when more than 32 rows still fill the chip (each B
     // panel is then staged once rather than once per 32 rows), else 32 x 32

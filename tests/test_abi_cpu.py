@@ -314,6 +314,13 @@ def test_pick_weighs_the_last_partial_round(lib):
         assert tile(prec, 1536, 4096, 8192) == (256, 128)
     for prec in (0, 1):
         assert tile(prec, 6144, 6144, 6144) == (256, 256)     # 2.25 rounds beat 4.5 of 256 x 128
+    # one round of 64 x 64 tiles over a long K splits K over the four waves of each tile
+    for prec in range(3):
+        assert lib.pdgemm_pick_config(prec, 128, 8192, 8192) == 9
+        assert lib.pdgemm_pick_config(prec, 8192, 128, 8192) == 9
+        assert tile(prec, 128, 8192, 4096) == (64, 64) and lib.pdgemm_pick_config(prec, 128, 8192, 4096) == 2
+        assert lib.pdgemm_pick_config(prec, 1024, 1024, 1024) == 2
+        assert lib.pdgemm_pick_config(prec, 128, 8192, 8224) == 2   # rows of K end inside a 128-byte line
     # 128 x 128 at one tile per CU takes its three-stage variant; with more tiles, two stages
     three_stage = lib.pdgemm_pick_config(0, 2048, 2048, 2048)
     assert info[three_stage] == (128, 128)

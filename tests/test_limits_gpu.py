@@ -98,9 +98,9 @@ LD = {"f16": MAX_ROW_BYTES // 2, "i8": MAX_ROW_BYTES, "i4": MAX_ROW_BYTES * 2}  
 
 
 @pytest.mark.parametrize("prec", ["f16", "i8", "i4"])
-@pytest.mark.parametrize("cfg", [0, 3])
+@pytest.mark.parametrize("cfg", [0, 3, 9])
 def test_largest_leading_dimensions(pd, dev, prec, cfg):
-    # 256 x 256 tiles (configuration 0) and the K-split 32 x 32 tiles (3), with rows of
+    # 256 x 256 tiles (configuration 0) and the K-split 32 x 32 and 64 x 64 tiles (3, 9), with rows of
     # A, B and C of 4 MiB; M, N and K ragged
     M, N, K = 250, 70, 200
     ld = LD[prec]
@@ -137,10 +137,10 @@ def test_largest_leading_dimensions(pd, dev, prec, cfg):
 
 
 @pytest.mark.parametrize("prec", ["f16", "i8", "i4"])
-@pytest.mark.parametrize("cfg", [0, 3, 6])
+@pytest.mark.parametrize("cfg", [0, 3, 6, 9])
 def test_largest_leading_dimension_row_major_b(pd, dev, prec, cfg):
     # B row-major with rows of 4 MiB, on the 256 x 256 tile (0) and on the K-split
-    # tiles (3: 32 x 32, 6: 64 x 32), whose waves each stage their own slice of
+    # tiles (3: 32 x 32, 6: 64 x 32, 9: 64 x 64), whose waves each stage their own slice of
     # rows of B; K reaches the last slice of a stage (a 64 x 32 INT4 stage spans
     # 1024 rows of B, 4 GiB at this row size)
     M, N, K = 50, 70, 1000

@@ -106,7 +106,7 @@ CFG_SHAPES = [(520, 600, 520), (300, 260, 1030), (64, 700, 130)]
 
 
 @pytest.mark.parametrize("prec", PRECS)
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6, 7, 8, 9])
 @pytest.mark.parametrize("shape", CFG_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in CFG_SHAPES])
 def test_every_config(pd, dev, prec, cfg, shape):
     if cfg >= pd.num_configs():
@@ -326,6 +326,21 @@ def test_ksplit_small_m(pd, dev, prec, shape, cfg):
     check_full(prec, A, Bt, K, C, f"ksplit {prec} {shape}")
 
 
+# one round of 64 x 64 tiles over a long K: configuration 9, four waves per
+# tile on K slices (ragged in M, N and K), compared in full
+LONG_K_SHAPES = [(128, 8192, 8192), (8192, 128, 8192), (120, 8190, 8448)]
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("shape", LONG_K_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in LONG_K_SHAPES])
+def test_one_round_long_k(pd, dev, prec, shape):
+    M, N, K = shape
+    pnum = {"f16": 0, "i8": 1, "i4": 2}[prec]
+    assert pd.pick_config(pnum, M, N, K) == 9, "one round of 64 x 64 tiles with K >= 8192 takes the K split"
+    A, Bt, C = run_case(pd, dev, prec, M, N, K, 5000 + M + N + K)
+    gu.check_whole(prec, A, Bt, K, C, f"long K {prec} {shape}")
+
+
 def test_configs_without_k_split_give_the_same_fp16_bits(pd, dev):
     # every tile without a K split sums each element over K in the same order
     M, N, K = 300, 260, 1030
@@ -342,7 +357,7 @@ def test_configs_without_k_split_give_the_same_fp16_bits(pd, dev):
         assert torch.equal(o, outs[0]), f"configuration {c} differs from {plain[0]}"
 
 
-@pytest.mark.parametrize("cfg", [3, 6])
+@pytest.mark.parametrize("cfg", [3, 6, 9])
 def test_ksplit_f16_is_deterministic(pd, dev, cfg):
     # the partial tiles of the K split are summed in a fixed wave order
     M, N, K = 48, 2048, 4100
