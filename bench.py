@@ -45,7 +45,9 @@ detail line ("kind": "bench_detail"; also written to --detail PATH)
                 N = 8192 operands, timed back to back and placed on their own
                 roofline (HBM-bound below about M = 315 for f16 and i8, 157 for
                 i4), with a sampled parity check; also timed with the
-                dequantizing epilogue (i8, i4) and with B row-major
+                dequantizing epilogue (i8, i4), with B row-major, and (i4)
+                with B converted once into its FP6 image (gemm_i4_packed_b,
+                checked bit-equal to the plain call)
 
 Usage: python bench.py [--steps K] [--warmup W] [--case f16:8192] [--calib-copy]
 """
@@ -716,6 +718,9 @@ def main():
         for prec, n, Ad, Bd, C in work:
             if n != 8192:
                 continue
+            # INT4 with B converted once into its FP6 image (weights packed ahead
+            # of the calls); each call converts only A
+            img_b = pd.i4_f6_pack(Bd, n) if prec == "i4" else None
             for M in SHAPE_MS:
                 Cm = torch.empty((M, n), dtype=C.dtype, device=dev)
                 def shape_go():
@@ -751,6 +756,18 @@ def main():
                     entry["dequant_f16_ms_back_to_back"] = round(time_b2b(
                         lambda: pd.prepare(prec, Ad[:M], Bd, Ch, K=n, scales=scl), 0.05), 5)
                     del Ch, scl
+                if img_b is not None:
+                    Cp = torch.empty((M, n), dtype=torch.int32, device=dev)
+                    wsp = torch.empty(max(pd.i4_f6_image_bytes(M, n), 16), dtype=torch.uint8, device=dev)
+                    def packed_go():
+                        go = lambda: pd.gemm_i4_packed_b(Ad[:M], img_b, n, n, out=Cp, workspace=wsp)
+                        go()
+                        return go
+                    packed_go()
+                    torch.cuda.synchronize()
+                    entry["packed_b_same_bits"] = bool(torch.equal(Cp, Cm))
+                    entry["packed_b_ms_back_to_back"] = round(time_b2b(packed_go, 0.05), 5)
+                    del Cp, wsp
                 if prec in brow_dev:
                     # the same product with B row-major
                     entry["rowb_ms_back_to_back"] = round(time_b2b(

@@ -216,6 +216,45 @@ int pdgemm_i4_f6_num_configs(void);
 int pdgemm_i4_f6_pick(int64_t M, int64_t N, int64_t K);
 int64_t pdgemm_i4_f6_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+/* INT4 with B converted once: the FP6 route for a B that serves many calls
+ * (the weights of an inference layer, say), so that a call converts only A.
+ *
+ * pdgemm_i4_f6_pack() converts one INT4 operand into its FP6 image (the
+ * format the *_ws entry points build in their workspace; 3/4 of a byte per
+ * value, pdgemm_i4_f6_image_bytes(rows, K) bytes): `rows` rows of K values
+ * packed along K (a column-major B given as its N rows, i.e. Bt; src_rowmajor
+ * = 0), or a row-major B, K rows of `rows` values packed along the row
+ * (src_rowmajor = 1).  ld counts 4-bit elements as in gemm_i4 / gemm_i4_rowb
+ * and the same alignment rules hold.  The image is device memory owned by the
+ * caller, 16-byte aligned; it depends only on the operand's values and K.
+ *
+ * gemm_i4_packed_b() computes the same C as gemm_i4 (bit for bit) from A and
+ * the image of B, which must have been packed from N rows of B with the same
+ * K.  A's image is built in the workspace (pdgemm_i4_f6_image_bytes(M, K)
+ * bytes, 16-byte aligned, caller-owned; contents undefined on return).  B's
+ * image is only read, so calls may share it; calls sharing a workspace must
+ * not overlap.  gemm_i4_dequant_packed_b() is the dequantizing form (as
+ * gemm_i4_dequant), pdgemm_i4_packed_b_cfg() takes an explicit FP6 tile
+ * configuration (0 <= cfg < pdgemm_i4_f6_num_configs(); with scale_a and
+ * scale_b non-NULL the dequantizing epilogue).  Both kernels are enqueued on
+ * `stream`; nothing is allocated or synchronized.  Errors as gemm_i4; an
+ * image or workspace that is too small or misaligned returns
+ * PDGEMM_EWORKSPACE, a NULL one PDGEMM_ENULL. */
+int64_t pdgemm_i4_f6_image_bytes(int64_t rows, int64_t K);
+int pdgemm_i4_f6_pack(int64_t rows, int64_t K, const uint8_t *src, int64_t ld, int src_rowmajor,
+                      void *image, int64_t image_bytes, void *stream);
+int gemm_i4_packed_b(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+                     const void *image_b, int64_t image_b_bytes, int32_t *C, int64_t ldc,
+                     void *workspace, int64_t workspace_bytes, void *stream);
+int gemm_i4_dequant_packed_b(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+                             const void *image_b, int64_t image_b_bytes, const float *scale_a,
+                             const float *scale_b, void *C, int64_t ldc, int out_f16,
+                             void *workspace, int64_t workspace_bytes, void *stream);
+int pdgemm_i4_packed_b_cfg(int cfg, int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+                           const void *image_b, int64_t image_b_bytes, const float *scale_a,
+                           const float *scale_b, void *C, int64_t ldc, int out_f16,
+                           void *workspace, int64_t workspace_bytes, void *stream);
+
 /* gemm_i4 for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation.
  * It is gemm_i4_ws with the workspace taken from a fixed file-scope device

@@ -85,6 +85,18 @@ lib.gemm_i4_dequant_ws.restype = _i
 lib.pdgemm_i4_f6_cfg.argtypes = [_i, _i, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i64, _i, _p,
                                  _i64, _p]
 lib.pdgemm_i4_f6_cfg.restype = _i
+lib.pdgemm_i4_f6_image_bytes.argtypes = [_i64, _i64]
+lib.pdgemm_i4_f6_image_bytes.restype = _i64
+lib.pdgemm_i4_f6_pack.argtypes = [_i64, _i64, _p, _i64, _i, _p, _i64, _p]
+lib.pdgemm_i4_f6_pack.restype = _i
+lib.gemm_i4_packed_b.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+lib.gemm_i4_packed_b.restype = _i
+lib.gemm_i4_dequant_packed_b.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i64, _i, _p,
+                                         _i64, _p]
+lib.gemm_i4_dequant_packed_b.restype = _i
+lib.pdgemm_i4_packed_b_cfg.argtypes = [_i, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i64, _i, _p,
+                                       _i64, _p]
+lib.pdgemm_i4_packed_b_cfg.restype = _i
 lib.gemm_i4_noalloc.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
 lib.gemm_i4_noalloc.restype = _i
 lib.pdgemm_i4_noalloc_max_bytes.argtypes = []
@@ -339,6 +351,83 @@ def gemm_i4_noalloc(A: torch.Tensor, Bt: torch.Tensor, K: int | None = None,
         raise ValueError("operands and out must be on the same GPU")
     rc = lib.gemm_i4_noalloc(M, N, K, A.data_ptr(), lda, Bt.data_ptr(), ldb, out.data_ptr(),
                              _row_major_2d(out, "out"), _stream(stream))
+    if rc != 0:
+        raise PdgemmError(rc)
+    return out
+
+
+def i4_f6_image_bytes(rows: int, K: int) -> int:
+    """Bytes of the FP6 image of an INT4 operand of `rows` rows of K values."""
+    return int(lib.pdgemm_i4_f6_image_bytes(rows, K))
+
+
+def i4_f6_pack(src: torch.Tensor, K: int | None = None, rowmajor: bool = False, N: int | None = None,
+               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The FP6 image (a uint8 tensor) of an INT4 operand, for gemm_i4_packed_b:
+    src (rows, K/2) packed along K (A, or a column-major B as Bt), or with
+    rowmajor a row-major B (K, N/2) packed along N (N defaults to 2 * src.shape[1])."""
+    if src.dtype != torch.uint8:
+        raise TypeError("i4_f6_pack takes a uint8 tensor of packed 4-bit values")
+    ld = 2 * _row_major_2d(src, "src")
+    if rowmajor:
+        K = src.shape[0] if K is None else K
+        rows = 2 * src.shape[1] if N is None else N
+        if src.shape[0] < K or 2 * src.shape[1] < rows:
+            raise ValueError("src holds fewer than K rows of N values")
+    else:
+        K = 2 * src.shape[1] if K is None else K
+        rows = src.shape[0]
+        if 2 * src.shape[1] < K:
+            raise ValueError("src holds fewer than K values per row")
+    need = i4_f6_image_bytes(rows, K)
+    if out is None:
+        out = torch.empty(max(need, 16), dtype=torch.uint8, device=src.device)
+    ptr, nbytes = _workspace(out, src.device)
+    rc = lib.pdgemm_i4_f6_pack(rows, K, src.data_ptr(), ld, 1 if rowmajor else 0, ptr, nbytes, _stream(stream))
+    if rc != 0:
+        raise PdgemmError(rc)
+    return out
+
+
+def gemm_i4_packed_b(A: torch.Tensor, image_b: torch.Tensor, K: int, N: int, out: torch.Tensor | None = None,
+                     scales=None, workspace: torch.Tensor | None = None, f6cfg: int | None = None,
+                     stream=None) -> torch.Tensor:
+    """C = A * B with B given as its FP6 image (i4_f6_pack of N rows, same K): int32 C,
+    or with scales = (scale_a, scale_b) the dequantized float32 / float16 C."""
+    if A.dtype != torch.uint8:
+        raise TypeError("gemm_i4_packed_b takes a uint8 A of packed 4-bit values")
+    if 2 * A.shape[1] < K:
+        raise ValueError("A holds fewer than K values per row")
+    M = A.shape[0]
+    lda = 2 * _row_major_2d(A, "A")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.int32 if scales is None else torch.float32, device=A.device)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must have shape {(M, N)}")
+    if scales is None and out.dtype != torch.int32:
+        raise TypeError("gemm_i4_packed_b writes an int32 output")
+    if scales is not None and out.dtype not in (torch.float32, torch.float16):
+        raise TypeError("a dequantizing GEMM writes float32 or float16")
+    if A.device != out.device:
+        raise ValueError("A and out must be on the same GPU")
+    if workspace is None:
+        workspace = torch.empty(max(i4_f6_image_bytes(M, K), 16), dtype=torch.uint8, device=A.device)
+    ws, ws_bytes = _workspace(workspace, out.device)
+    img, img_bytes = _workspace(image_b, out.device)
+    ldc = _row_major_2d(out, "out")
+    sa = sb = None
+    if scales is not None:
+        sa, sb = _scale(scales[0], M, "scale_a"), _scale(scales[1], N, "scale_b")
+    half = 1 if out.dtype == torch.float16 else 0
+    if f6cfg is not None:
+        rc = lib.pdgemm_i4_packed_b_cfg(f6cfg, M, N, K, A.data_ptr(), lda, img, img_bytes, sa, sb,
+                                        out.data_ptr(), ldc, half, ws, ws_bytes, _stream(stream))
+    elif scales is not None:
+        rc = lib.gemm_i4_dequant_packed_b(M, N, K, A.data_ptr(), lda, img, img_bytes, sa, sb, out.data_ptr(),
+                                          ldc, half, ws, ws_bytes, _stream(stream))
+    else:
+        rc = lib.gemm_i4_packed_b(M, N, K, A.data_ptr(), lda, img, img_bytes, out.data_ptr(), ldc, ws,
+                                  ws_bytes, _stream(stream))
     if rc != 0:
         raise PdgemmError(rc)
     return out

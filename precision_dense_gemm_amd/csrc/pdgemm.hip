@@ -1745,6 +1745,35 @@ int pick_f6(int64_t M, int64_t N, int64_t K) {
     return -1;
 }
 
+// The FP6 GEMM's arguments for two images of K values (A's M rows, B's N).
+F6Args f6_gemm_args(int cfg, int64_t M, int64_t N, int64_t K, const uint8_t *img_a, const uint8_t *img_b,
+                    const float *scale_a, const float *scale_b, void *C, int64_t ldc) {
+    const F6Config &c = kF6Configs[cfg];
+    F6Args args;
+    args.A = img_a;
+    args.B = img_b;
+    args.C = C;
+    args.scale_a = scale_a;
+    args.scale_b = scale_b;
+    args.a_bytes = f6_image_bytes(M, K);
+    args.b_bytes = f6_image_bytes(N, K);
+    args.ldc = ldc;
+    args.M = (int)M;
+    args.N = (int)N;
+    args.nkb = (int)f6_blocks(K);
+    args.tiles_m = (int)cdiv(M, c.bm);
+    args.tiles_n = (int)cdiv(N, c.bn);
+    return args;
+}
+
+int64_t f6_threads(int cfg) {
+    const F6Config &c = kF6Configs[cfg];
+    return (c.bm / c.wm) * (c.bn / c.wn) * kWave;
+}
+
+// pre-pass workgroups for one operand (four 32-row x 128-value units each)
+int64_t f6_pack_blocks(int64_t rows, int64_t K) { return cdiv(cdiv(rows, 32) * f6_blocks(K), 4); }
+
 int launch_f6(int cfg, int epi, int br, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
               const void *B, int64_t ldb, const float *scale_a, const float *scale_b, void *C, int64_t ldc,
               void *ws, int64_t ws_bytes, void *stream) {
@@ -1759,8 +1788,6 @@ int launch_f6(int cfg, int epi, int br, int64_t M, int64_t N, int64_t K, const v
     if (!ws) return PDGEMM_ENULL;
     if (((uintptr_t)ws & 15) || ws_bytes < f6_workspace_bytes(M, N, K)) return PDGEMM_EWORKSPACE;
 
-    const F6Config &c = kF6Configs[cfg];
-    const int64_t nkb = f6_blocks(K);
     const int64_t a_img = f6_image_bytes(M, K);
     uint8_t *const img_a = static_cast<uint8_t *>(ws);
     uint8_t *const img_b = img_a + cdiv(a_img, 256) * 256;
@@ -1769,26 +1796,13 @@ int launch_f6(int cfg, int epi, int br, int64_t M, int64_t N, int64_t K, const v
     pk.op[0] = {static_cast<const uint8_t *>(A), img_a, lda / 2, (int)M, (int)cdiv(M, 32), 0};
     pk.op[1] = {static_cast<const uint8_t *>(B), img_b, ldb / 2, (int)N, (int)cdiv(N, 32), br == kBRow};
     pk.K = (int)K;
-    pk.nkb = (int)nkb;
-    const int64_t blocks_a = cdiv(cdiv(M, 32) * nkb, 4);
-    const int64_t blocks_b = cdiv(cdiv(N, 32) * nkb, 4);
+    pk.nkb = (int)f6_blocks(K);
+    const int64_t blocks_a = f6_pack_blocks(M, K);
+    const int64_t blocks_b = f6_pack_blocks(N, K);
     pk.blocks_a = (int)blocks_a;
-    F6Args args;
-    args.A = img_a;
-    args.B = img_b;
-    args.C = C;
-    args.scale_a = scale_a;
-    args.scale_b = scale_b;
-    args.a_bytes = a_img;
-    args.b_bytes = f6_image_bytes(N, K);
-    args.ldc = ldc;
-    args.M = (int)M;
-    args.N = (int)N;
-    args.nkb = (int)nkb;
-    args.tiles_m = (int)cdiv(M, c.bm);
-    args.tiles_n = (int)cdiv(N, c.bn);
+    F6Args args = f6_gemm_args(cfg, M, N, K, img_a, img_b, scale_a, scale_b, C, ldc);
     const int64_t blocks = (int64_t)args.tiles_m * args.tiles_n;
-    const int threads = (c.bm / c.wm) * (c.bn / c.wn) * kWave;
+    const int64_t threads = f6_threads(cfg);
     // launches count their work-items in 32 bits
     if (blocks * threads > (int64_t)UINT32_MAX || (blocks_a + blocks_b) * 256 > (int64_t)UINT32_MAX)
         return PDGEMM_EINVAL_DIM;
@@ -1799,7 +1813,94 @@ int launch_f6(int cfg, int epi, int br, int64_t M, int64_t N, int64_t K, const v
                                    dim3((unsigned)(blocks_a + blocks_b)), dim3(256), pargs, 0, s);
     if (e != hipSuccess) return (int)e;
     void *gargs[] = {&args};
-    e = hipLaunchKernel(f6_kernel_ptr(cfg, epi), dim3((unsigned)blocks), dim3(threads), gargs, 0, s);
+    e = hipLaunchKernel(f6_kernel_ptr(cfg, epi), dim3((unsigned)blocks), dim3((unsigned)threads), gargs, 0, s);
+    if (e != hipSuccess) return (int)e;
+    if (sync_check_enabled()) {
+        e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return (int)e;
+    }
+    return PDGEMM_OK;
+}
+
+// One operand into its FP6 image: `rows` rows of K values packed along K
+// (A, or a column-major B given as its N rows), or (rowmajor) the K x rows
+// row-major B packed along its rows.  The same checks, in the same order,
+// as the GEMM's for that operand, then the image's.
+int pack_f6(int64_t rows, int64_t K, const void *src, int64_t ld, int rowmajor, void *img, int64_t img_bytes,
+            void *stream) {
+    if (rows < 0 || K < 0) return PDGEMM_EINVAL_DIM;
+    if (rows > INT32_MAX || K > PDGEMM_I4_MAX_K) return PDGEMM_EINVAL_DIM;
+    if (ld < (rowmajor ? rows : K)) return PDGEMM_EINVAL_LD;
+    if ((K & 1) || (ld & 1)) return PDGEMM_EINVAL_I4;
+    if (img_bytes < 0) return PDGEMM_EWORKSPACE;
+    if (rows == 0 || K == 0) return PDGEMM_OK;   // an empty image
+    if (!src || !img) return PDGEMM_ENULL;
+    if (ld > kMaxRowBytes * 2) return PDGEMM_EINVAL_LD;
+    if (((ld / 2) & 15) || ((uintptr_t)src & 15)) return PDGEMM_EALIGN;
+    if (((uintptr_t)img & 15) || img_bytes < f6_image_bytes(rows, K)) return PDGEMM_EWORKSPACE;
+    const int64_t blocks = f6_pack_blocks(rows, K);
+    if (blocks * 256 > (int64_t)UINT32_MAX) return PDGEMM_EINVAL_DIM;
+    F6PackArgs pk;
+    pk.op[0] = {static_cast<const uint8_t *>(src), static_cast<uint8_t *>(img), ld / 2, (int)rows,
+                (int)cdiv(rows, 32), rowmajor ? 1 : 0};
+    pk.op[1] = pk.op[0];   // unused: every workgroup converts op[0]
+    pk.K = (int)K;
+    pk.nkb = (int)f6_blocks(K);
+    pk.blocks_a = (int)blocks;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *pargs[] = {&pk};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&f6_pack_kernel), dim3((unsigned)blocks),
+                                   dim3(256), pargs, 0, s);
+    if (e != hipSuccess) return (int)e;
+    if (sync_check_enabled()) {
+        e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return (int)e;
+    }
+    return PDGEMM_OK;
+}
+
+// The FP6 tile for a GEMM whose B image is given: no B pre-pass to pay for,
+// so the FP6 cores win down to one round of 128 x 128 tiles; 256 x 256 where
+// it gives most CUs a tile.  (M x 8192 x 8192: M = 2048 75.8 us on 256 x 256
+// against 89.0 on 128 x 128; M = 1024 45.6 against 60.0.)
+int pick_f6_packed(int64_t M, int64_t N) { return cdiv(M, 256) * cdiv(N, 256) >= 192 ? 0 : 1; }
+
+// A GEMM with B given as its FP6 image (packed with the same K): A is
+// converted into the workspace, then the GEMM runs on the two images.
+int launch_f6_packed_b(int cfg, int epi, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                       const void *img_b, int64_t img_b_bytes, const float *scale_a, const float *scale_b,
+                       void *C, int64_t ldc, void *ws, int64_t ws_bytes, void *stream) {
+    if (cfg < -1 || cfg >= kNumF6Configs) return PDGEMM_EINVAL_CFG;
+    if (M < 0 || N < 0 || K < 0) return PDGEMM_EINVAL_DIM;
+    if (M > INT32_MAX || N > INT32_MAX || K > PDGEMM_I4_MAX_K) return PDGEMM_EINVAL_DIM;
+    if (lda < K || ldc < N) return PDGEMM_EINVAL_LD;
+    if ((K & 1) || (lda & 1)) return PDGEMM_EINVAL_I4;
+    if (ws_bytes < 0 || img_b_bytes < 0) return PDGEMM_EWORKSPACE;
+    if (M == 0 || N == 0) return PDGEMM_OK;
+    if (!C || (K > 0 && (!A || !img_b || !ws))) return PDGEMM_ENULL;
+    if (epi != kRaw && (!scale_a || !scale_b)) return PDGEMM_ENULL;
+    const int64_t c_size = epi == kDequantF16 ? 2 : 4;
+    if (lda > kMaxRowBytes * 2 || ldc > kMaxRowBytes / c_size) return PDGEMM_EINVAL_LD;
+    if (((lda / 2) & 15) || ((uintptr_t)A & 15) || ((uintptr_t)C & (c_size - 1))) return PDGEMM_EALIGN;
+    if (epi != kRaw && (((uintptr_t)scale_a & 3) || ((uintptr_t)scale_b & 3))) return PDGEMM_EALIGN;
+    if (K > 0 && (((uintptr_t)img_b & 15) || img_b_bytes < f6_image_bytes(N, K) || ((uintptr_t)ws & 15) ||
+                  ws_bytes < f6_image_bytes(M, K)))
+        return PDGEMM_EWORKSPACE;
+    if (cfg < 0) cfg = pick_f6_packed(M, N);
+    F6Args args = f6_gemm_args(cfg, M, N, K, static_cast<const uint8_t *>(ws),
+                               static_cast<const uint8_t *>(img_b), scale_a, scale_b, C, ldc);
+    const int64_t blocks = (int64_t)args.tiles_m * args.tiles_n;
+    const int64_t threads = f6_threads(cfg);
+    if (blocks * threads > (int64_t)UINT32_MAX || f6_pack_blocks(M, K) * 256 > (int64_t)UINT32_MAX)
+        return PDGEMM_EINVAL_DIM;
+    if (K > 0) {
+        const int rc = pack_f6(M, K, A, lda, 0, ws, ws_bytes, stream);
+        if (rc != PDGEMM_OK) return rc;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *gargs[] = {&args};
+    hipError_t e = hipLaunchKernel(f6_kernel_ptr(cfg, epi), dim3((unsigned)blocks), dim3((unsigned)threads),
+                                   gargs, 0, s);
     if (e != hipSuccess) return (int)e;
     if (sync_check_enabled()) {
         e = hipStreamSynchronize(s);
@@ -1997,6 +2098,41 @@ int gemm_i4_noalloc(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t l
 }
 
 int64_t pdgemm_i4_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int64_t pdgemm_i4_f6_image_bytes(int64_t rows, int64_t K) {
+    if (rows < 0 || K < 0) return 0;
+    return f6_image_bytes(rows, K);
+}
+
+int pdgemm_i4_f6_pack(int64_t rows, int64_t K, const uint8_t *src, int64_t ld, int src_rowmajor, void *image,
+                      int64_t image_bytes, void *stream) {
+    return pack_f6(rows, K, src, ld, src_rowmajor, image, image_bytes, stream);
+}
+
+int gemm_i4_packed_b(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda, const void *image_b,
+                     int64_t image_b_bytes, int32_t *C, int64_t ldc, void *workspace, int64_t workspace_bytes,
+                     void *stream) {
+    return launch_f6_packed_b(-1, kRaw, M, N, K, A, lda, image_b, image_b_bytes, nullptr, nullptr, C, ldc,
+                              workspace, workspace_bytes, stream);
+}
+
+int gemm_i4_dequant_packed_b(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+                             const void *image_b, int64_t image_b_bytes, const float *scale_a,
+                             const float *scale_b, void *C, int64_t ldc, int out_f16, void *workspace,
+                             int64_t workspace_bytes, void *stream) {
+    return launch_f6_packed_b(-1, out_f16 ? kDequantF16 : kDequantF32, M, N, K, A, lda, image_b, image_b_bytes,
+                              scale_a, scale_b, C, ldc, workspace, workspace_bytes, stream);
+}
+
+int pdgemm_i4_packed_b_cfg(int cfg, int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+                           const void *image_b, int64_t image_b_bytes, const float *scale_a,
+                           const float *scale_b, void *C, int64_t ldc, int out_f16, void *workspace,
+                           int64_t workspace_bytes, void *stream) {
+    if (cfg < 0) return PDGEMM_EINVAL_CFG;
+    const int epi = (scale_a || scale_b) ? (out_f16 ? kDequantF16 : kDequantF32) : kRaw;
+    return launch_f6_packed_b(cfg, epi, M, N, K, A, lda, image_b, image_b_bytes, scale_a, scale_b, C, ldc,
+                              workspace, workspace_bytes, stream);
+}
 
 int pdgemm_num_configs(void) { return kNumConfigs; }
 

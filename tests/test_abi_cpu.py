@@ -63,7 +63,9 @@ def test_header_declares_the_entry_points():
               "pdgemm_gemm_cfg", "pdgemm_dequant_cfg", "pdgemm_strerror", "pdgemm_version",
               "gemm_i4_ws", "gemm_i4_rowb_ws", "gemm_i4_dequant_ws", "pdgemm_i4_workspace_size",
               "pdgemm_i4_f6_cfg", "pdgemm_i4_f6_pick", "pdgemm_i4_f6_num_configs",
-              "pdgemm_i4_f6_workspace_bytes"):
+              "pdgemm_i4_f6_workspace_bytes", "pdgemm_i4_f6_image_bytes", "pdgemm_i4_f6_pack",
+              "gemm_i4_packed_b", "gemm_i4_dequant_packed_b", "pdgemm_i4_packed_b_cfg",
+              "gemm_i4_noalloc", "pdgemm_i4_noalloc_max_bytes"):
         assert n in names
 
 
@@ -350,6 +352,16 @@ def wslib(lib):
         getattr(lib, name).restype = i64
     lib.pdgemm_i4_f6_pick.argtypes = [i64, i64, i64]
     lib.pdgemm_i4_f6_pick.restype = i
+    lib.pdgemm_i4_f6_image_bytes.argtypes = [i64, i64]
+    lib.pdgemm_i4_f6_image_bytes.restype = i64
+    lib.pdgemm_i4_f6_pack.argtypes = [i64, i64, p, i64, i, p, i64, p]
+    lib.pdgemm_i4_f6_pack.restype = i
+    lib.gemm_i4_packed_b.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p]
+    lib.gemm_i4_packed_b.restype = i
+    lib.gemm_i4_dequant_packed_b.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, p, i64, i, p, i64, p]
+    lib.gemm_i4_dequant_packed_b.restype = i
+    lib.pdgemm_i4_packed_b_cfg.argtypes = [i, i64, i64, i64, p, i64, p, i64, p, p, p, i64, i, p, i64, p]
+    lib.pdgemm_i4_packed_b_cfg.restype = i
     return lib
 
 
@@ -400,3 +412,54 @@ def test_workspace_errors_before_any_hip_call(wslib):
     assert L.pdgemm_i4_f6_cfg(1, 0, 300, 200, 1030, A, 1056, B, 1056, None, None, C, 200, 0, ws, small - 1,
                               None) == c["PDGEMM_EWORKSPACE"]
     assert L.pdgemm_strerror(c["PDGEMM_EWORKSPACE"]).decode().startswith("workspace")
+
+
+def test_image_sizes(wslib):
+    # one operand's image: 32-row groups x 128-value K blocks (padded to a multiple of 3) of 3072
+    # bytes; the workspace holds A's image, then B's at the next multiple of 256 bytes
+    L = wslib
+    cd = lambda a, b: -(-a // b)
+    for rows, K in ((1, 2), (31, 130), (8192, 8192), (5000, 131070)):
+        assert L.pdgemm_i4_f6_image_bytes(rows, K) == cd(rows, 32) * cd(cd(K, 128), 3) * 3 * 3072
+    for M, N, K in ((8192, 8192, 8192), (4000, 3000, 1030)):
+        a = L.pdgemm_i4_f6_image_bytes(M, K)
+        assert L.pdgemm_i4_f6_workspace_bytes(M, N, K) == cd(a, 256) * 256 + L.pdgemm_i4_f6_image_bytes(N, K)
+    assert L.pdgemm_i4_f6_image_bytes(-1, 8) == 0 and L.pdgemm_i4_f6_image_bytes(8, 0) == 0
+
+
+def test_packed_b_errors_before_any_hip_call(wslib):
+    L, c = wslib, codes()
+    M, N, K = 1024, 8192, 8192
+    A, B, C, img, ws = 0x10000, 0x20000, 0x30000, 0x100000, 0x200000
+    nb, na = L.pdgemm_i4_f6_image_bytes(N, K), L.pdgemm_i4_f6_image_bytes(M, K)
+    # pack: argument rules as for the operand of a GEMM, then the image
+    assert L.pdgemm_i4_f6_pack(-1, K, B, K, 0, img, nb, None) == c["PDGEMM_EINVAL_DIM"]
+    assert L.pdgemm_i4_f6_pack(N, 131072, B, 131072, 0, img, nb, None) == c["PDGEMM_EINVAL_DIM"]
+    assert L.pdgemm_i4_f6_pack(N, K, B, K - 2, 0, img, nb, None) == c["PDGEMM_EINVAL_LD"]
+    assert L.pdgemm_i4_f6_pack(N, K, B, N - 2, 1, img, nb, None) == c["PDGEMM_EINVAL_LD"]
+    assert L.pdgemm_i4_f6_pack(N, K + 1, B, K + 2, 0, img, nb, None) == c["PDGEMM_EINVAL_I4"]
+    assert L.pdgemm_i4_f6_pack(N, K, None, K, 0, img, nb, None) == c["PDGEMM_ENULL"]
+    assert L.pdgemm_i4_f6_pack(N, K, B, K, 0, None, nb, None) == c["PDGEMM_ENULL"]
+    assert L.pdgemm_i4_f6_pack(N, K, B + 8, K, 0, img, nb, None) == c["PDGEMM_EALIGN"]
+    assert L.pdgemm_i4_f6_pack(N, K, B, K + 2, 0, img, nb, None) == c["PDGEMM_EALIGN"]
+    assert L.pdgemm_i4_f6_pack(N, K, B, K, 0, img, nb - 1, None) == c["PDGEMM_EWORKSPACE"]
+    assert L.pdgemm_i4_f6_pack(N, K, B, K, 0, img + 8, nb, None) == c["PDGEMM_EWORKSPACE"]
+    assert L.pdgemm_i4_f6_pack(0, K, None, K, 0, None, 0, None) == c["PDGEMM_OK"]   # an empty image
+    # the GEMM from A and B's image
+    args = lambda ib, nbb, w, nw: (M, N, K, A, K, ib, nbb, C, N, w, nw, None)
+    assert L.gemm_i4_packed_b(*args(img, nb, None, na)) == c["PDGEMM_ENULL"]
+    assert L.gemm_i4_packed_b(*args(None, nb, ws, na)) == c["PDGEMM_ENULL"]
+    assert L.gemm_i4_packed_b(*args(img, nb - 1, ws, na)) == c["PDGEMM_EWORKSPACE"]
+    assert L.gemm_i4_packed_b(*args(img, nb, ws, na - 1)) == c["PDGEMM_EWORKSPACE"]
+    assert L.gemm_i4_packed_b(*args(img + 8, nb, ws, na)) == c["PDGEMM_EWORKSPACE"]
+    assert L.gemm_i4_packed_b(M, N, K, A, K - 2, img, nb, C, N, ws, na, None) == c["PDGEMM_EINVAL_LD"]
+    assert L.gemm_i4_packed_b(M, N, K, A, K, img, nb, C, N - 1, ws, na, None) == c["PDGEMM_EINVAL_LD"]
+    assert L.gemm_i4_packed_b(M, N, K + 1, A, K + 2, img, nb, C, N, ws, na, None) == c["PDGEMM_EINVAL_I4"]
+    assert L.gemm_i4_packed_b(M, N, K, A + 8, K, img, nb, C, N, ws, na, None) == c["PDGEMM_EALIGN"]
+    assert L.gemm_i4_packed_b(0, N, K, None, K, None, 0, None, N, None, 0, None) == c["PDGEMM_OK"]
+    assert L.gemm_i4_dequant_packed_b(M, N, K, A, K, img, nb, None, None, C, N, 0, ws, na, None) == \
+        c["PDGEMM_ENULL"]
+    assert L.pdgemm_i4_packed_b_cfg(-1, M, N, K, A, K, img, nb, None, None, C, N, 0, ws, na, None) == \
+        c["PDGEMM_EINVAL_CFG"]
+    assert L.pdgemm_i4_packed_b_cfg(2, M, N, K, A, K, img, nb, None, None, C, N, 0, ws, na, None) == \
+        c["PDGEMM_EINVAL_CFG"]

@@ -194,3 +194,88 @@ def test_repeat_and_reuse_workspace(pd, dev):
         Ad, Bd = device_operands(A, Bt, K, dev)
         C = pd.gemm_i4(Ad, Bd, K, workspace=ws, f6cfg=1).cpu().numpy()
         check(A, Bt, K, C, f"reuse {M}x{N}x{K}")
+
+
+# ---------------------------------------------------------------------------
+# B converted once (i4_f6_pack), then GEMMs from A and B's image
+
+def packed_case(pd, dev, M, N, K, seed, rowb=False, cfg=None, scales=None, out_dtype=torch.int32):
+    gu.note(f"[case] packed B M={M} N={N} K={K} seed={seed} rowb={rowb} cfg={cfg} scales={scales is not None}")
+    A = synth.pack_int4(synth.int4_values(M, K, seed))
+    Ad = gu.to_device_padded(torch, A, gu.round_up(K // 2, 16) + 16, POISON, dev)
+    if rowb:
+        Bv = synth.int4_values(N, K, seed + 1).T
+        if N % 2:
+            Bv = np.hstack([Bv, np.zeros((K, 1), np.int8)])
+        B = synth.pack_int4(np.ascontiguousarray(Bv))
+        nb = B.shape[1]
+        Bbuf = synth.with_leading_dim(np.vstack([B, np.full((2, nb), POISON, np.uint8)]),
+                                      gu.round_up(nb, 16) + 16, POISON)
+        img = pd.i4_f6_pack(torch.from_numpy(Bbuf).to(dev)[:K, :nb], K, rowmajor=True, N=N)
+    else:
+        B = synth.pack_int4(synth.int4_values(N, K, seed + 1))
+        Bd = gu.to_device_padded(torch, B, gu.round_up(K // 2, 16) + 32, POISON, dev)
+        img = pd.i4_f6_pack(Bd, K)
+    buf, out = gu.guarded_out(torch, M, N, gu.round_up(N, 4) + 4, out_dtype, dev)
+    sc = None if scales is None else tuple(torch.from_numpy(x).to(dev) for x in scales)
+    pd.gemm_i4_packed_b(Ad, img, K, N, out=out, scales=sc, f6cfg=cfg)
+    torch.cuda.synchronize()
+    gu.check_guard(torch, buf, M, N)
+    return A, B, out.cpu().numpy()
+
+
+PACKED_SHAPES = [(1, 1, 2), (31, 33, 18), (65, 63, 256), (255, 257, 384), (300, 17, 1000), (520, 600, 520)]
+
+
+@pytest.mark.parametrize("cfg", [None, 0, 1])
+@pytest.mark.parametrize("rowb", [False, True], ids=["colB", "rowB"])
+@pytest.mark.parametrize("shape", PACKED_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in PACKED_SHAPES])
+def test_packed_b(pd, dev, cfg, rowb, shape):
+    M, N, K = shape
+    A, B, C = packed_case(pd, dev, M, N, K, 12000 + M + N + K, rowb=rowb, cfg=cfg)
+    check(A, B, K, C, f"packed B {shape} rowb={rowb} cfg={cfg}", rowb=rowb)
+
+
+@pytest.mark.parametrize("out", ["f32", "f16"])
+def test_packed_b_dequant(pd, dev, out):
+    M, N, K = 300, 260, 1030
+    sa, sb = synth.f32_scales(M, 93), synth.f32_scales(N, 94)
+    dt = torch.float32 if out == "f32" else torch.float16
+    A, B, C = packed_case(pd, dev, M, N, K, 13000, scales=(sa, sb), out_dtype=dt)
+    want = oracle.dequant(oracle.gemm_i4(A, B, K=K), sa, sb, half_out=(out == "f16"))
+    got = C.view(np.uint32 if out == "f32" else np.uint16)
+    assert np.array_equal(got, want.view(got.dtype)), f"packed dequant {out}"
+
+
+def test_packed_b_image_serves_many_calls(pd, dev):
+    """One image of an 8192 x 8192 B (as for a layer's weights) and GEMMs with
+    A of 1024 and 2048 rows: bit-equal to gemm_i4 on the raw operands, and the
+    first compared in full with the oracle."""
+    N = K = 8192
+    gu.note("[case] packed B 8192 x 8192 image, M = 1024 and 2048")
+    Bt = synth.pack_int4(synth.int4_values(N, K, 14001))
+    Bd = torch.from_numpy(Bt).to(dev)
+    img = pd.i4_f6_pack(Bd, K)
+    for M, seed in ((1024, 14002), (2048, 14003)):
+        A = synth.pack_int4(synth.int4_values(M, K, seed))
+        Ad = torch.from_numpy(A).to(dev)
+        C = pd.gemm_i4_packed_b(Ad, img, K, N)
+        ref = pd.gemm_i4(Ad, Bd, K)
+        torch.cuda.synchronize()
+        assert torch.equal(C, ref), f"packed B differs from gemm_i4 at M = {M}"
+        if M == 1024:
+            gu.check_whole("i4", A, Bt, K, C.cpu().numpy(), "packed B 1024 x 8192 x 8192")
+
+
+def test_packed_b_errors(pd, dev):
+    gu.note("[case] packed B errors")
+    M, N, K = 64, 96, 256
+    Bd = torch.zeros((N, K // 2), dtype=torch.uint8, device=dev)
+    img = pd.i4_f6_pack(Bd, K)
+    Ad = torch.zeros((M, K // 2), dtype=torch.uint8, device=dev)
+    with pytest.raises(pd.PdgemmError) as e:
+        pd.gemm_i4_packed_b(Ad, img[:img.numel() - 16], K, N)     # image for fewer rows or K
+    assert e.value.code == -7
+    with pytest.raises(pd.PdgemmError) as e:
+        pd.i4_f6_pack(Bd, K, out=torch.empty(64, dtype=torch.uint8, device=dev))
+    assert e.value.code == -7
