@@ -102,3 +102,49 @@ def test_prepared_launches_captured_in_a_graph(pd, dev, prec):
         ref = oracle.gemm_i8(A, Bt) if prec == "i8" else oracle.gemm_i4(A, Bt, K)
         gu.assert_int_equal(eager.cpu().numpy(), ref, f"graph prepare {prec}")
     del g
+
+
+@pytest.mark.parametrize("route", ["workspace", "noalloc", "packed_b"])
+def test_captured_fp6_routes_replay(pd, dev, route):
+    """INT4 on the FP6 cores under capture: the pre-pass and the GEMM (two
+    kernels) recorded together, with the caller's workspace, the library's
+    static one, or a B image made beforehand; each replay follows eager work
+    that overwrites the output, and must give the oracle's result."""
+    M, N, K = 4096, 3072, 1056   # 192 tiles of 256 x 256: the FP6 route is taken
+    gu.note(f"[case] graph fp6 {route} {M}x{N}x{K}")
+    A, Bt = synth.operands("i4", M, N, K, 95, 96)
+    Ad, Bd = torch.from_numpy(A).to(dev), torch.from_numpy(Bt).to(dev)
+    out = torch.empty((M, N), dtype=torch.int32, device=dev)
+    ws = pd.i4_workspace(M, N, K, dev, f6=True)
+    img = pd.i4_f6_pack(Bd, K) if route == "packed_b" else None
+    torch.cuda.synchronize()
+
+    def call():
+        if route == "workspace":
+            pd.gemm_i4(Ad, Bd, K, out=out, workspace=ws, f6cfg=1)
+        elif route == "noalloc":
+            pd.gemm_i4_noalloc(Ad, Bd, K, out=out)
+        else:
+            pd.gemm_i4_packed_b(Ad, img, K, N, out=out, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    assert pd.i4_f6_pick(M, N, K) >= 0
+    ref = gu.oracle_whole("i4", A, Bt, K)
+    gu.assert_int_equal(out.cpu().numpy(), ref, f"graph fp6 {route} eager")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for replay in range(3):
+        out.view(torch.int32).fill_(gu.C_SENTINEL_BITS)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        gu.assert_int_equal(out.cpu().numpy(), ref, f"graph fp6 {route} replay {replay}")
+    del g
