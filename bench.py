@@ -141,7 +141,7 @@ def tile_sweep():
     import torch
     import precision_dense_gemm_amd as pd
     dev = torch.device("cuda:0")
-    cfgs = [0, 4, 1, 5, 2, 7, 8]
+    cfgs = [0, 4, 1, 5, 2, 7, 8, 9]
 
     def graph_time(make, reps):
         g = torch.cuda.CUDAGraph()
