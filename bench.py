@@ -865,14 +865,13 @@ def main():
         log("[bench] calibration copy: 3 x 1 GiB device-to-device")
 
     # the headline line carries the metric for every GEMM of the sweep in a
-    # compact form: in-step and back-to-back ms, TOPS, fraction of peak
+    # compact form: in-step ms, TOPS and fraction of peak, back-to-back ms and
+    # fraction of peak (cold times and the rest are on the detail line)
     compact = {}
     for key, e in per.items():
         c = {"ms": e["ms"], "tops": round(e["tops"], 1), "frac": e["frac_of_peak"],
-             "ms_b2b": e["ms_back_to_back"], "tops_b2b": round(e["tops_back_to_back"], 1),
+             "ms_b2b": e["ms_back_to_back"],
              "frac_b2b": round(e["tops_back_to_back"] / PEAK[key.split(":")[0]], 4)}
-        if "ms_cold" in e:
-            c["ms_cold"] = e["ms_cold"]
         if key.startswith("i4:"):
             c["path"] = i4_path[int(key.split(":")[1])]
         if "parity" in e:
@@ -919,7 +918,7 @@ def main():
         "detail": "per-GEMM medians and minima, HBM rates, the dequantizing epilogue, row-major B, "
                   "non-square shapes and power telemetry are on the preceding bench_detail line",
     }
-    print(json.dumps(out), flush=True)
+    print(json.dumps(out, separators=(",", ":")), flush=True)
     if parity and not all(parity.values()):
         sys.exit(1)
 
