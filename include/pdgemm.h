@@ -103,8 +103,9 @@ extern "C" {
                                    epilogue for FP16; reported before any other check.  Every
                                    configuration, the K-split ones included, serves both B layouts */
 
-#define PDGEMM_EWORKSPACE (-7)  /* *_ws entry points: workspace smaller than pdgemm_i4_workspace_size(),
-                                   a negative size, or a workspace not 16-byte aligned */
+#define PDGEMM_EWORKSPACE (-7)  /* a workspace or FP6 image smaller than its entry point needs
+                                   (pdgemm_i4_workspace_size(), pdgemm_i4_f6_image_bytes()),
+                                   a negative size, or one not 16-byte aligned */
 
 #define PDGEMM_I4_MAX_K 131071
 

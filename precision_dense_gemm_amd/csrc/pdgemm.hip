@@ -2162,7 +2162,9 @@ const char *pdgemm_strerror(int code) {
     case PDGEMM_EINVAL_I4: return "INT4 K, lda and ldb must be even";
     case PDGEMM_EALIGN: return "A and B must be 16-byte aligned, A and B rows must span a multiple of 16 bytes, C and the scales must be element-aligned";
     case PDGEMM_EINVAL_CFG: return "unknown precision or tile configuration, or a dequantizing epilogue for FP16";
-    case PDGEMM_EWORKSPACE: return "workspace smaller than pdgemm_i4_workspace_size(), negative, or not 16-byte aligned";
+    case PDGEMM_EWORKSPACE:
+        return "workspace or FP6 image smaller than the entry point needs, of negative size, or not 16-byte "
+               "aligned";
     default: return code > 0 ? hipGetErrorString((hipError_t)code) : "unknown error";
     }
 }
