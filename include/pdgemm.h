@@ -38,10 +38,13 @@
  * carry fp32 rounding only: every element satisfies
  * |C - sum_k a_ik b_kj| <= 1e-3 * sum_k |a_ik b_kj| for K up to 16384 (the
  * worst-case bound of K fp32 additions, K * 2^-24, stays below 1e-3).
- * Each FP16 sum runs in a fixed order (no atomics), so a call gives the same
- * bits every time for a given shape and tile configuration.  The
- * configurations without a K split share one order and give the same bits
- * as each other; the K-split configurations group K differently.
+ * Each FP16 sum runs in a fixed order, so a call gives the same bits every
+ * time for a given shape and tile configuration.  The configurations without
+ * a K split share one order and give the same bits as each other; the K-split
+ * configurations group K differently.  Where K is split across workgroups
+ * (pdgemm_pick_splits below), FP16 takes two ranges whose binary32 partial
+ * sums are added atomically into a zeroed C: 0 + x + y and 0 + y + x round
+ * alike, so the bits still do not depend on which range finishes first.
  *
  * Alignment (checked): A and B 16-byte aligned, with lda and ldb spanning a
  * multiple of 16 bytes (f16: lda, ldb % 8 == 0; i8: % 16; i4: % 32); C
@@ -55,7 +58,10 @@
  *
  * Ownership and execution: every pointer is device memory owned by the
  * caller, on the device the stream belongs to.  C must not overlap A, B or
- * the scales (the result is then undefined).  The library never allocates,
+ * the scales (the result is then undefined).  Where K is split across
+ * workgroups, C is first zeroed and then receives the partial sums as
+ * device-scope atomic adds, so it must be memory that supports them
+ * (ordinary device allocations do).  The library never allocates,
  * frees, copies or synchronizes.  The call enqueues work on `stream` (a
  * hipStream_t passed as void*; NULL is the default stream) and returns once
  * it is enqueued.  Entry points are thread-safe and keep no state between
@@ -293,6 +299,34 @@ int pdgemm_gemm_rowb_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K, con
                          int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc,
                          void *stream);
 
+/* K split across workgroups.  The entry points that return raw sums
+ * (gemm_f16, gemm_i8, gemm_i4 and their _rowb, _ws and _noalloc forms, where
+ * those run the INT8-MFMA kernels) split K into `splits` ranges when the
+ * shape has too few tiles to fill the GPU and K is long: a kernel zeroes the
+ * M x N block of C, then each range, a row of the launch grid, adds its
+ * partial tile with atomic adds.  Integer results are exact in any order;
+ * FP16 takes at most two ranges (see Semantics).  The pages describe no such
+ * split; it serves the few-tile shapes whose small-N regime the paper studies
+ * ("Hand-Written PTX Tensor-Core GEMM Kernels ...", Section IV, the 3-stage
+ * INT4 kernel at small N).  The dequantizing entry points never split.
+ *
+ * pdgemm_pick_splits: the split the raw-sum entry points use for a shape and
+ * B layout (b_rowmajor 0 or 1): returns the number of ranges (1 = no split,
+ * -1 for an unknown precision) and stores the tile configuration in *cfg
+ * (may be NULL).
+ *
+ * pdgemm_gemm_splitk_cfg: the GEMM with an explicit tile configuration and
+ * split.  cfg must be one of the tiles a split runs on (2 or 5), splits >= 1;
+ * K is cut into ranges of ceil(K / splits) values rounded up to a whole
+ * 128-byte stage, so fewer ranges may result; for FP16 more than two ranges
+ * give PDGEMM_EINVAL_CFG.  splits == 1 or K == 0 runs the plain kernel of cfg.
+ * Other arguments, layouts and errors as pdgemm_gemm_cfg (b_rowmajor 0) or
+ * pdgemm_gemm_rowb_cfg (b_rowmajor 1). */
+int pdgemm_pick_splits(int prec, int b_rowmajor, int64_t M, int64_t N, int64_t K, int *cfg);
+int pdgemm_gemm_splitk_cfg(int prec, int cfg, int b_rowmajor, int splits, int64_t M, int64_t N, int64_t K,
+                           const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc,
+                           void *stream);
+
 /* The dequantizing GEMM with an explicit tile configuration (prec is
  * PDGEMM_PREC_I8 or PDGEMM_PREC_I4; FP16 returns PDGEMM_EINVAL_CFG). */
 int pdgemm_dequant_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K, const void *A,
@@ -300,7 +334,8 @@ int pdgemm_dequant_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K, const
                        const float *scale_b, void *C, int64_t ldc, int out_f16, void *stream);
 
 /* Number of tile configurations, and the one the entry points pick for a
- * shape (-1 for an unknown precision). */
+ * shape (-1 for an unknown precision) when they do not split K across
+ * workgroups. */
 int pdgemm_num_configs(void);
 int pdgemm_pick_config(int prec, int64_t M, int64_t N, int64_t K);
 

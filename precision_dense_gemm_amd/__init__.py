@@ -62,6 +62,10 @@ lib.pdgemm_dequant_cfg.argtypes = [_i, _i, _i64, _i64, _i64, _p, _i64, _p, _i64,
 lib.pdgemm_dequant_cfg.restype = _i
 lib.pdgemm_gemm_cfg.argtypes = [_i, _i, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
 lib.pdgemm_gemm_cfg.restype = _i
+lib.pdgemm_gemm_splitk_cfg.argtypes = [_i, _i, _i, _i, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+lib.pdgemm_gemm_splitk_cfg.restype = _i
+lib.pdgemm_pick_splits.argtypes = [_i, _i, _i64, _i64, _i64, ctypes.POINTER(_i)]
+lib.pdgemm_pick_splits.restype = _i
 lib.pdgemm_num_configs.argtypes = []
 lib.pdgemm_num_configs.restype = _i
 lib.pdgemm_pick_config.argtypes = [_i, _i64, _i64, _i64]
@@ -127,6 +131,14 @@ def num_configs() -> int:
 
 def pick_config(prec: int, M: int, N: int, K: int) -> int:
     return lib.pdgemm_pick_config(prec, M, N, K)
+
+
+def pick_splits(prec: int, M: int, N: int, K: int, rowb: bool = False) -> tuple[int, int]:
+    """(ranges of K, tile configuration) the raw-sum entry points use for a shape;
+    ranges == 1: no K split across workgroups."""
+    cfg = _i()
+    s = lib.pdgemm_pick_splits(prec, 1 if rowb else 0, M, N, K, ctypes.byref(cfg))
+    return s, cfg.value
 
 
 def config_info(cfg: int) -> dict:
@@ -206,11 +218,12 @@ def _workspace(ws, device):
 
 
 def _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None, N=None, rowb=False,
-             workspace=None, f6cfg=None):
+             workspace=None, f6cfg=None, splits=None):
     """The C function and its argument tuple for one GEMM (dequantizing when
     scales = (scale_a, scale_b) is given; B row-major when rowb, with N given;
     INT4 on the FP6 cores with a workspace, by the library's choice or with
-    the FP6 tile f6cfg)."""
+    the FP6 tile f6cfg; K split over `splits` ranges across workgroups on the
+    tile cfg)."""
     M = A.shape[0]
     N = Bt.shape[0] if N is None else N
     ldc = _row_major_2d(out, "out")
@@ -219,6 +232,11 @@ def _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None, N=None, ro
         raise ValueError("operands, scales and out must be on the same GPU")
     if tuple(out.shape) != (M, N):
         raise ValueError(f"out must have shape {(M, N)}")
+    if splits is not None:
+        if cfg is None or scales is not None or workspace is not None or f6cfg is not None:
+            raise ValueError("a K split across workgroups takes a tile cfg and no scales or workspace")
+        return lib.pdgemm_gemm_splitk_cfg, (prec, cfg, 1 if rowb else 0, splits, M, N, K, A.data_ptr(), lda,
+                                            Bt.data_ptr(), ldb, out.data_ptr(), ldc, _stream(stream))
     if workspace is not None or f6cfg is not None:
         if prec != PREC_I4:
             raise ValueError("a workspace serves the INT4 GEMM on the FP6 cores only")
@@ -270,8 +288,8 @@ def _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None, N=None, ro
 
 
 def _call(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None, N=None, rowb=False, workspace=None,
-          f6cfg=None):
-    fn, args = _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales, N, rowb, workspace, f6cfg)
+          f6cfg=None, splits=None):
+    fn, args = _marshal(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales, N, rowb, workspace, f6cfg, splits)
     rc = fn(*args)
     if rc != 0:
         raise PdgemmError(rc)
@@ -279,7 +297,7 @@ def _call(prec, A, Bt, out, K, lda, ldb, stream, cfg, scales=None, N=None, rowb=
 
 
 def gemm_f16(A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor | None = None,
-             stream=None, cfg: int | None = None) -> torch.Tensor:
+             stream=None, cfg: int | None = None, splits: int | None = None) -> torch.Tensor:
     """C = A * B for binary16 A (M, K) and Bt (N, K); fp32 accumulate, fp32 C (M, N)."""
     if A.dtype != torch.float16 or Bt.dtype != torch.float16:
         raise TypeError("gemm_f16 takes float16 operands")
@@ -291,11 +309,11 @@ def gemm_f16(A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor | None = None,
         out = torch.empty((A.shape[0], Bt.shape[0]), dtype=torch.float32, device=A.device)
     elif out.dtype != torch.float32:
         raise TypeError("gemm_f16 writes a float32 output")
-    return _call(PREC_F16, A, Bt, out, K, lda, ldb, stream, cfg)
+    return _call(PREC_F16, A, Bt, out, K, lda, ldb, stream, cfg, splits=splits)
 
 
 def gemm_i8(A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor | None = None,
-            stream=None, cfg: int | None = None) -> torch.Tensor:
+            stream=None, cfg: int | None = None, splits: int | None = None) -> torch.Tensor:
     """C = A * B for int8 A (M, K) and Bt (N, K); int32 accumulate, int32 C (M, N)."""
     if A.dtype != torch.int8 or Bt.dtype != torch.int8:
         raise TypeError("gemm_i8 takes int8 operands")
@@ -307,12 +325,13 @@ def gemm_i8(A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor | None = None,
         out = torch.empty((A.shape[0], Bt.shape[0]), dtype=torch.int32, device=A.device)
     elif out.dtype != torch.int32:
         raise TypeError("gemm_i8 writes an int32 output")
-    return _call(PREC_I8, A, Bt, out, K, lda, ldb, stream, cfg)
+    return _call(PREC_I8, A, Bt, out, K, lda, ldb, stream, cfg, splits=splits)
 
 
 def gemm_i4(A: torch.Tensor, Bt: torch.Tensor, K: int | None = None,
             out: torch.Tensor | None = None, stream=None, cfg: int | None = None,
-            workspace: torch.Tensor | None = None, f6cfg: int | None = None) -> torch.Tensor:
+            workspace: torch.Tensor | None = None, f6cfg: int | None = None,
+            splits: int | None = None) -> torch.Tensor:
     """C = A * B for packed INT4 A (M, K/2) and Bt (N, K/2) bytes; int32 C (M, N).
     With a workspace (see i4_workspace) the library may run it on the FP6 cores."""
     if A.dtype != torch.uint8 or Bt.dtype != torch.uint8:
@@ -326,7 +345,8 @@ def gemm_i4(A: torch.Tensor, Bt: torch.Tensor, K: int | None = None,
         out = torch.empty((A.shape[0], Bt.shape[0]), dtype=torch.int32, device=A.device)
     elif out.dtype != torch.int32:
         raise TypeError("gemm_i4 writes an int32 output")
-    return _call(PREC_I4, A, Bt, out, K, lda, ldb, stream, cfg, workspace=workspace, f6cfg=f6cfg)
+    return _call(PREC_I4, A, Bt, out, K, lda, ldb, stream, cfg, workspace=workspace, f6cfg=f6cfg,
+                 splits=splits)
 
 
 def gemm_i4_noalloc(A: torch.Tensor, Bt: torch.Tensor, K: int | None = None,
@@ -437,7 +457,7 @@ _DTYPES = {"f16": (torch.float16, torch.float32, PREC_F16), "i8": (torch.int8, t
            "i4": (torch.uint8, torch.int32, PREC_I4)}
 
 
-def _gemm_rowb(prec, A, B, K, N, out, stream, cfg, workspace=None, f6cfg=None):
+def _gemm_rowb(prec, A, B, K, N, out, stream, cfg, workspace=None, f6cfg=None, splits=None):
     in_t, out_t, p = _DTYPES[prec]
     if A.dtype != in_t or B.dtype != in_t:
         raise TypeError(f"{prec} with row-major B takes {in_t} operands")
@@ -452,26 +472,27 @@ def _gemm_rowb(prec, A, B, K, N, out, stream, cfg, workspace=None, f6cfg=None):
     elif out.dtype != out_t:
         raise TypeError(f"{prec} writes a {out_t} output")
     return _call(p, A, B, out, K, lda, ldb, stream, cfg, N=N, rowb=True, workspace=workspace,
-                 f6cfg=f6cfg)
+                 f6cfg=f6cfg, splits=splits)
 
 
 def gemm_f16_rowb(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None,
-                  stream=None, cfg: int | None = None) -> torch.Tensor:
+                  stream=None, cfg: int | None = None, splits: int | None = None) -> torch.Tensor:
     """C = A * B for binary16 A (M, K) and row-major B (K, N); fp32 C (M, N)."""
-    return _gemm_rowb("f16", A, B, None, None, out, stream, cfg)
+    return _gemm_rowb("f16", A, B, None, None, out, stream, cfg, splits=splits)
 
 
 def gemm_i8_rowb(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None,
-                 stream=None, cfg: int | None = None) -> torch.Tensor:
+                 stream=None, cfg: int | None = None, splits: int | None = None) -> torch.Tensor:
     """C = A * B for int8 A (M, K) and row-major B (K, N); int32 C (M, N)."""
-    return _gemm_rowb("i8", A, B, None, None, out, stream, cfg)
+    return _gemm_rowb("i8", A, B, None, None, out, stream, cfg, splits=splits)
 
 
 def gemm_i4_rowb(A: torch.Tensor, B: torch.Tensor, K: int | None = None, N: int | None = None,
                  out: torch.Tensor | None = None, stream=None, cfg: int | None = None,
-                 workspace: torch.Tensor | None = None, f6cfg: int | None = None) -> torch.Tensor:
+                 workspace: torch.Tensor | None = None, f6cfg: int | None = None,
+                 splits: int | None = None) -> torch.Tensor:
     """C = A * B for packed INT4 A (M, K/2) and row-major B (K, N/2 bytes, packed along N)."""
-    return _gemm_rowb("i4", A, B, K, N, out, stream, cfg, workspace, f6cfg)
+    return _gemm_rowb("i4", A, B, K, N, out, stream, cfg, workspace, f6cfg, splits)
 
 
 def gemm_i8_dequant(A: torch.Tensor, Bt: torch.Tensor, scale_a: torch.Tensor,

@@ -184,6 +184,7 @@ struct Args {
     int64_t ldc;
     int M, N, K;
     int tiles_m, tiles_n;
+    int kslice;   // K split across workgroups (epilogue kAtomicAdd): K values per split, else 0
 };
 
 // Epilogues: the int32 / fp32 sums as they are, or (integer paths) the
@@ -191,6 +192,10 @@ struct Args {
 constexpr int kRaw = 0;
 constexpr int kDequantF32 = 1;
 constexpr int kDequantF16 = 2;
+// (K split across workgroups) the sums of one range of K added atomically
+// into C, which the host has zeroed
+constexpr int kAtomicAdd = 3;
+constexpr bool is_dequant(int e) { return e == kDequantF32 || e == kDequantF16; }
 
 template <int P, int E> struct OutOf { using type = typename Prec<P>::Out; };
 template <int P> struct OutOf<P, kDequantF32> { using type = float; };
@@ -268,16 +273,16 @@ __device__ __forceinline__ void store_tile(void *C, int64_t ldc, int M, int N, A
 
     // this lane's scales: 4 consecutive rows per quarter of a 32-row
     // block (one 16-byte LDS read each), one column per column block
-    float sb[E == kRaw ? 1 : FN];
-    if constexpr (E != kRaw) {
+    float sb[!is_dequant(E) ? 1 : FN];
+    if constexpr (is_dequant(E)) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) sb[j] = lds_scale[BM + wn0 + j * 32 + frow];
     }
     auto store_all = [&](auto &&keep) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            float4 sa[E == kRaw ? 1 : 4];
-            if constexpr (E != kRaw) {
+            float4 sa[!is_dequant(E) ? 1 : 4];
+            if constexpr (is_dequant(E)) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     sa[q] = *reinterpret_cast<const float4 *>(&lds_scale[wm0 + i * 32 + 8 * q + 4 * fhalf]);
@@ -289,7 +294,7 @@ __device__ __forceinline__ void store_tile(void *C, int64_t ldc, int M, int N, A
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
                     Out v;
-                    if constexpr (E != kRaw) {
+                    if constexpr (is_dequant(E)) {
                         // ((float)sum * scale_a) * scale_b, rounded once per step
                         // (on the FP6 cores the sum already is that binary32 value)
                         float c;
@@ -317,18 +322,22 @@ __device__ __forceinline__ void store_tile(void *C, int64_t ldc, int M, int N, A
                     // non-temporal: C is not read again here, and
                     // streaming it past the MALL keeps A and B there
                     // for the later rounds of tiles
-                    if (keep(r, j))
-                        __builtin_nontemporal_store(
-                            v, reinterpret_cast<Out *>(row_c + lane_off + j * 32 * (int)sizeof(Out)));
+                    if (keep(r, j)) {
+                        Out *const dst = reinterpret_cast<Out *>(row_c + lane_off + j * 32 * (int)sizeof(Out));
+                        if constexpr (E == kAtomicAdd)
+                            __hip_atomic_fetch_add(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        else
+                            __builtin_nontemporal_store(v, dst);
+                    }
                 }
                 // dequantized values are converted one row at a time
-                if constexpr (E != kRaw) __builtin_amdgcn_sched_barrier(0);
+                if constexpr (is_dequant(E)) __builtin_amdgcn_sched_barrier(0);
             }
             // one row block at a time keeps accumulator reads from piling up
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    if constexpr (E != kRaw) {
+    if constexpr (is_dequant(E)) {
         // one path: with two, more of the accumulators are copied out of
         // the accumulation registers ahead of the branch
         store_all([&](int r, int j) { return interior || (r < rows_left && j * 32 < cols_left); });
@@ -377,7 +386,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
 #if defined(__HIP_DEVICE_COMPILE__)
     using Acc = typename Prec<P>::Acc;
     using Out = typename OutOf<P, E>::type;
-    static_assert(E == kRaw || P != kF16, "the dequantizing epilogue is for the integer paths");
+    static_assert(!is_dequant(E) || P != kF16, "the dequantizing epilogues are for the integer paths");
+    static_assert(E != kAtomicAdd || KS == 1, "a K split across workgroups adds whole tiles");
     using RB = RowB<P>;
     constexpr int kCpr = BN / RB::kElemPerChunk;   // row-major B: 16-byte chunks per row of B
     static_assert(BR == kBCol || (kCpr >= 1 && (kCpr & (kCpr - 1)) == 0), "row-major B tile width");
@@ -429,7 +439,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int slice = KS > 1 ? wave : 0;     // this wave's K slice
     const int twave = KS > 1 ? 0 : wave;     // this wave's place in the block tile
-    const int M = args.M, N = args.N, K = args.K;
+    const int M = args.M, N = args.N;
+    // K split across workgroups: blockIdx.y picks the range of K this
+    // workgroup sums (a whole number of stages in, so alignments hold)
+    const int k_first = E == kAtomicAdd ? (int)blockIdx.y * args.kslice : 0;
+    const int K = E == kAtomicAdd ? min(args.K - k_first, args.kslice) : args.K;
+    const int64_t k_first_bytes = (int64_t)k_first * (P == kF16 ? 2 : 1) / (P == kI4 ? 2 : 1);
+    const uint8_t *const op_a = args.A + k_first_bytes;
+    const uint8_t *const op_b = args.B + (BR == kBRow ? (int64_t)k_first * args.ldb_bytes : k_first_bytes);
 
     // ---- block id -> tile, XCD-aware and banded by GM block rows ----
     int tile_m, tile_n;
@@ -450,13 +467,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     const int valid = (P == kF16) ? 2 * K : (P == kI8 ? K : K / 2);  // data bytes per row
     const int n_tiles = (valid + kTileBytes - 1) / kTileBytes;
     const int valid16 = (valid + 15) & ~15;
-    const uint8_t *a_base = args.A + (int64_t)m0 * args.lda_bytes;
+    const uint8_t *a_base = op_a + (int64_t)m0 * args.lda_bytes;
     const int a_end = (int)((min(BM, M - m0) - 1) * args.lda_bytes) + valid16;
     // column-major B: like A, BN rows of K.  Row-major B: the tile's columns
     // start n0 values into every row of B; the range ends at the last chunk
     // of row K-1 that holds a column below N, so rows past K read as zeros.
     const int64_t b_col_bytes = (int64_t)n0 * (P == kF16 ? 2 : 1) / (P == kI4 ? 2 : 1);
-    const uint8_t *b_base = args.B + (BR == kBRow ? b_col_bytes : (int64_t)n0 * args.ldb_bytes);
+    const uint8_t *b_base = op_b + (BR == kBRow ? b_col_bytes : (int64_t)n0 * args.ldb_bytes);
     // bytes of the last row of B that hold columns n0 .. N-1 (INT4: an odd
     // count of columns ends inside a byte, which still counts)
     const int64_t b_row_valid = ((int64_t)min(BN, N - n0) * (P == kF16 ? 16 : (P == kI8 ? 8 : 4)) + 7) / 8;
@@ -703,8 +720,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
     // stored).  The loads are issued before the first DMAs and written to
     // LDS after them; the first barrier makes them visible.
     constexpr int kThreads = NW * kWave;
-    constexpr int kScaleLoads = E == kRaw ? 0 : (BM + BN + kThreads - 1) / kThreads;
-    __shared__ __align__(16) float lds_scale[E == kRaw ? 1 : BM + BN];
+    constexpr int kScaleLoads = !is_dequant(E) ? 0 : (BM + BN + kThreads - 1) / kThreads;
+    __shared__ __align__(16) float lds_scale[!is_dequant(E) ? 1 : BM + BN];
     float scale_v[kScaleLoads + 1];
 #pragma unroll
     for (int x = 0; x < kScaleLoads; ++x) {
@@ -878,7 +895,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
             }
             // no DMA may still be writing this workgroup's LDS when it exits
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        } else if constexpr (E != kRaw) {
+        } else if constexpr (is_dequant(E)) {
             // K == 0: no main loop, so stage the scales here
 #pragma unroll
             for (int x = 0; x < kScaleLoads; ++x)
@@ -918,7 +935,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
             last_tile(last == 0 ? lds0 : last == 1 ? lds1 : last == 2 ? lds2 : lds3, t);
             // no DMA may still be writing this workgroup's LDS when it exits
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        } else if constexpr (E != kRaw) {
+        } else if constexpr (is_dequant(E)) {
             // K == 0: no main loop, so stage the scales here
     #pragma unroll
             for (int x = 0; x < kScaleLoads; ++x)
@@ -963,7 +980,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * KS * kWave) void gemm_kerne
                     if constexpr (P == kI4) v >>= 8;
                     const int r = 8 * (e >> 2) + (e & 3);   // row in the block, less 4*(l/32)
                     Out o;
-                    if constexpr (E != kRaw) {
+                    if constexpr (is_dequant(E)) {
                         // ((float)sum * scale_a) * scale_b, one rounding per step,
                         // then (binary16 output) narrowed as a separate step
                         float c = (float)v;
@@ -1408,8 +1425,8 @@ gemm_f6_kernel(F6Args args) {
 
     // dequantizing epilogue: the tile's scales staged in LDS (see gemm_kernel)
     constexpr int kThreads = NW * kWave;
-    constexpr int kScaleLoads = E == kRaw ? 0 : (BM + BN + kThreads - 1) / kThreads;
-    __shared__ __align__(16) float lds_scale[E == kRaw ? 1 : BM + BN];
+    constexpr int kScaleLoads = !is_dequant(E) ? 0 : (BM + BN + kThreads - 1) / kThreads;
+    __shared__ __align__(16) float lds_scale[!is_dequant(E) ? 1 : BM + BN];
     float scale_v[kScaleLoads + 1];
 #pragma unroll
     for (int x = 0; x < kScaleLoads; ++x) {
@@ -1444,7 +1461,7 @@ gemm_f6_kernel(F6Args args) {
         last_stage(mn2, tl2);
         // no DMA may still be writing this workgroup's LDS when it exits
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    } else if constexpr (E != kRaw) {
+    } else if constexpr (is_dequant(E)) {
 #pragma unroll
         for (int x = 0; x < kScaleLoads; ++x)
             if (tid + x * kThreads < BM + BN) lds_scale[tid + x * kThreads] = scale_v[x];
@@ -1611,6 +1628,39 @@ int pick(int prec, int64_t M, int64_t N, int64_t K) {
     return 3;
 }
 
+// K split across workgroups.  Where even 64 x 64 tiles leave CUs idle
+// (pick() settles on a K-split tile) and K is long, each CU runs one long
+// row of K; splitting K over S grid rows of workgroups that add into a
+// zeroed C multiplies the workgroups by S.  Row-major B gains most, as its
+// K-split tiles read 32-64 bytes of each row of B, while the 64-row tiles
+// read whole 128-byte lines.  The tile is 64 x 64 (128 x 64 for integers
+// past 64 rows of A) and S the largest of 2, 4, 8 with at most 256
+// workgroups; taken for integers when each range still holds 2048 values of
+// K (column-major B: only for at most 32 tiles and 4096 values, as its
+// K-split tiles already read whole lines), for FP16 (two ranges only: see
+// launch_splitk) with row-major B, at most 128 tiles and K >= 16384.
+// Measured at M = 8-512, N = 512-16384, K = 2048-65536: 1.2-1.3x at
+// M <= 64 x 8192 x 8192 (row-major B, integers), up to 3x at 64 x 2048 x
+// 32768; where the rule declines (K <= 4096, or the chip filled), the split
+// lost up to 2x to the zero pass and the atomic adds.
+int pick_splits(int prec, int br, int64_t M, int64_t N, int64_t K, int *cfg) {
+    const int base = pick(prec, M, N, K);
+    *cfg = base;
+    if (base != 3 && base != 6) return 1;
+    const int tile = (prec != kF16 && M > 64) ? 5 : 2;
+    const int64_t t = cdiv(M, kConfigs[tile].bm) * cdiv(N, kConfigs[tile].bn);
+    int s = 1;
+    if (prec == kF16) {
+        if (br == kBRow && t <= 128 && K >= 16384) s = 2;
+    } else {
+        while (s < 8 && t * s * 2 <= 256) s *= 2;
+        const int64_t min_range = br == kBRow ? 2048 : 4096;
+        if ((br == kBCol && t > 32) || K / s < min_range) s = 1;
+    }
+    if (s > 1) *cfg = tile;
+    return s;
+}
+
 int validate(int prec, int epi, int br, int64_t M, int64_t N, int64_t K, const void *A,
              int64_t lda, const void *B, int64_t ldb, const void *C, int64_t ldc,
              const float *scale_a, const float *scale_b) {
@@ -1664,6 +1714,7 @@ int launch(int prec, int cfg, int epi, int br, int64_t M, int64_t N, int64_t K, 
     args.K = (int)K;
     args.tiles_m = (int)cdiv(M, c.bm);
     args.tiles_n = (int)cdiv(N, c.bn);
+    args.kslice = 0;
     const int64_t blocks = (int64_t)args.tiles_m * args.tiles_n;
     const int threads = (c.bm / c.wm) * (c.bn / c.wn) * c.ks * kWave;
     // a launch counts its work-items in 32 bits
@@ -1678,6 +1729,102 @@ int launch(int prec, int cfg, int epi, int br, int64_t M, int64_t N, int64_t K, 
         if (e != hipSuccess) return (int)e;
     }
     return PDGEMM_OK;
+}
+
+// zeroes the M x N block of a 32-bit C (row stride ldc): one column per
+// thread, 256 columns by a stride of rows per workgroup
+__global__ __launch_bounds__(256) void zero_rows_kernel(int32_t *C, int64_t ldc, int M, int N) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= N) return;
+    for (int64_t r = blockIdx.y; r < M; r += gridDim.y) C[r * ldc + c] = 0;
+}
+
+// Tiles a K split across workgroups runs on: 64 x 64 and 128 x 64 (the
+// atomic epilogue needs a tile without an in-workgroup K split)
+template <int P, int BR>
+const void *splitk_kernel_ptr(int cfg) {
+    switch (cfg) {
+    case 2: return kernel_for<P, 2, kAtomicAdd, BR>();
+    case 5: return kernel_for<P, 5, kAtomicAdd, BR>();
+    default: return nullptr;
+    }
+}
+
+const void *splitk_kernel_ptr(int prec, int cfg, int br) {
+    switch (prec * 2 + (br == kBRow)) {
+    case kF16 * 2: return splitk_kernel_ptr<kF16, kBCol>(cfg);
+    case kF16 * 2 + 1: return splitk_kernel_ptr<kF16, kBRow>(cfg);
+    case kI8 * 2: return splitk_kernel_ptr<kI8, kBCol>(cfg);
+    case kI8 * 2 + 1: return splitk_kernel_ptr<kI8, kBRow>(cfg);
+    case kI4 * 2: return splitk_kernel_ptr<kI4, kBCol>(cfg);
+    case kI4 * 2 + 1: return splitk_kernel_ptr<kI4, kBRow>(cfg);
+    default: return nullptr;
+    }
+}
+
+// A GEMM with K split over `splits` ranges of whole stages, each range a
+// grid row of workgroups adding its partial tile into C, which is zeroed
+// first.  Integer sums are exact in any order, so the result is the plain
+// GEMM's.  FP16 takes at most two ranges: 0 + x + y and 0 + y + x round
+// alike (binary32 addition commutes), so the result does not depend on
+// which range lands first, though it may differ from the one-range sum in
+// its last bits.
+int launch_splitk(int prec, int cfg, int br, int splits, int64_t M, int64_t N, int64_t K, const void *A,
+                  int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc, void *stream) {
+    if (cfg < 0 || cfg >= kNumConfigs || splits < 1) return PDGEMM_EINVAL_CFG;
+    const void *fn = splitk_kernel_ptr(prec, cfg, br);
+    if (!fn) return PDGEMM_EINVAL_CFG;
+    int rc = validate(prec, kRaw, br, M, N, K, A, lda, B, ldb, C, ldc, nullptr, nullptr);
+    if (rc != PDGEMM_OK) return rc;
+    if (M == 0 || N == 0) return PDGEMM_OK;
+    if (K == 0 || splits == 1) return launch(prec, cfg, kRaw, br, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
+                                             stream);
+    const Config &c = kConfigs[cfg];
+    const int64_t stage_k = 128 * 8 / elem_bits(prec);            // values of K in a 128-byte stage
+    const int64_t kslice = cdiv(cdiv(K, splits), stage_k) * stage_k;
+    const int64_t ranges = cdiv(K, kslice);
+    if (prec == kF16 && ranges > 2) return PDGEMM_EINVAL_CFG;   // x + y = y + x, but (x + y) + z != x + (y + z)
+    Args args;
+    args.A = static_cast<const uint8_t *>(A);
+    args.B = static_cast<const uint8_t *>(B);
+    args.C = C;
+    args.scale_a = nullptr;
+    args.scale_b = nullptr;
+    args.lda_bytes = lda * elem_bits(prec) / 8;
+    args.ldb_bytes = ldb * elem_bits(prec) / 8;
+    args.ldc = ldc;
+    args.M = (int)M;
+    args.N = (int)N;
+    args.K = (int)K;
+    args.tiles_m = (int)cdiv(M, c.bm);
+    args.tiles_n = (int)cdiv(N, c.bn);
+    args.kslice = (int)kslice;
+    const int64_t blocks = (int64_t)args.tiles_m * args.tiles_n;
+    const int threads = (c.bm / c.wm) * (c.bn / c.wn) * c.ks * kWave;
+    if (blocks * threads > (int64_t)UINT32_MAX || ranges > 65535) return PDGEMM_EINVAL_DIM;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *zargs[] = {&C, &ldc, &args.M, &args.N};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&zero_rows_kernel),
+                                   dim3((unsigned)cdiv(N, 256), (unsigned)std::min<int64_t>(M, 1024)), dim3(256), zargs, 0, s);
+    if (e != hipSuccess) return (int)e;
+    void *kargs[] = {&args};
+    e = hipLaunchKernel(fn, dim3((unsigned)blocks, (unsigned)ranges), dim3(threads), kargs, 0, s);
+    if (e != hipSuccess) return (int)e;
+    if (sync_check_enabled()) {
+        e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return (int)e;
+    }
+    return PDGEMM_OK;
+}
+
+// The GEMM (raw sums) as the entry points without a configuration run it:
+// the picked tile, with K split across workgroups where pick_splits() asks.
+int launch_raw(int prec, int br, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+               int64_t ldb, void *C, int64_t ldc, void *stream) {
+    int cfg = 0;
+    const int splits = pick_splits(prec, br, M, N, K, &cfg);
+    if (splits > 1) return launch_splitk(prec, cfg, br, splits, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return launch(prec, cfg, kRaw, br, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc, stream);
 }
 
 // ---- INT4 on the FP6 cores: tiles, workspace, launch ----
@@ -1916,8 +2063,9 @@ int launch_i4_ws(int epi, int br, int64_t M, int64_t N, int64_t K, const void *A
                  int64_t ws_bytes, void *stream) {
     const int f = pick_f6(M, N, K);
     if (f < 0)
-        return launch(kI4, pick(kI4, M, N, K), epi, br, M, N, K, A, lda, B, ldb, scale_a, scale_b, C, ldc,
-                      stream);
+        return epi == kRaw ? launch_raw(kI4, br, M, N, K, A, lda, B, ldb, C, ldc, stream)
+                           : launch(kI4, pick(kI4, M, N, K), epi, br, M, N, K, A, lda, B, ldb, scale_a, scale_b, C,
+                                    ldc, stream);
     return launch_f6(f, epi, br, M, N, K, A, lda, B, ldb, scale_a, scale_b, C, ldc, ws, ws_bytes, stream);
 }
 
@@ -1970,20 +2118,17 @@ extern "C" {
 
 int gemm_f16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
              const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream) {
-    return launch(kF16, pick(kF16, M, N, K), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
-                  stream);
+    return launch_raw(kF16, kBCol, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
 int gemm_i8(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
             const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
-    return launch(kI8, pick(kI8, M, N, K), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
-                  stream);
+    return launch_raw(kI8, kBCol, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
 int gemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
             const uint8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
-    return launch(kI4, pick(kI4, M, N, K), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
-                  stream);
+    return launch_raw(kI4, kBCol, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
 int gemm_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
@@ -2016,20 +2161,17 @@ int pdgemm_dequant_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K, const
 
 int gemm_f16_rowb(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
                   const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream) {
-    return launch(kF16, pick(kF16, M, N, K), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
-                  C, ldc, stream);
+    return launch_raw(kF16, kBRow, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
 int gemm_i8_rowb(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
                  const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
-    return launch(kI8, pick(kI8, M, N, K), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
-                  C, ldc, stream);
+    return launch_raw(kI8, kBRow, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
 int gemm_i4_rowb(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
                  const uint8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
-    return launch(kI4, pick(kI4, M, N, K), kRaw, kBRow, M, N, K, A, lda, B, ldb, nullptr, nullptr,
-                  C, ldc, stream);
+    return launch_raw(kI4, kBRow, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
 int pdgemm_gemm_rowb_cfg(int prec, int cfg, int64_t M, int64_t N, int64_t K, const void *A,
@@ -2084,9 +2226,7 @@ int pdgemm_i4_f6_cfg(int cfg, int b_rowmajor, int64_t M, int64_t N, int64_t K, c
 int gemm_i4_noalloc(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda, const uint8_t *B,
                     int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
     // shapes the INT8-MFMA kernels take need no workspace
-    if (pick_f6(M, N, K) < 0)
-        return launch(kI4, pick(kI4, M, N, K), kRaw, kBCol, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc,
-                      stream);
+    if (pick_f6(M, N, K) < 0) return launch_raw(kI4, kBCol, M, N, K, A, lda, B, ldb, C, ldc, stream);
     const int rc = validate(kI4, kRaw, kBCol, M, N, K, A, lda, B, ldb, C, ldc, nullptr, nullptr);
     if (rc != PDGEMM_OK) return rc;
     if (f6_workspace_bytes(M, N, K) > kScratchBytes) return PDGEMM_EWORKSPACE;
@@ -2098,6 +2238,12 @@ int gemm_i4_noalloc(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t l
 }
 
 int64_t pdgemm_i4_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int pdgemm_gemm_splitk_cfg(int prec, int cfg, int b_rowmajor, int splits, int64_t M, int64_t N, int64_t K,
+                           const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc,
+                           void *stream) {
+    return launch_splitk(prec, cfg, b_rowmajor ? kBRow : kBCol, splits, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
 
 int64_t pdgemm_i4_f6_image_bytes(int64_t rows, int64_t K) {
     if (rows < 0 || K < 0) return 0;
@@ -2139,6 +2285,13 @@ int pdgemm_num_configs(void) { return kNumConfigs; }
 int pdgemm_pick_config(int prec, int64_t M, int64_t N, int64_t K) {
     if (prec < 0 || prec > 2) return -1;
     return pick(prec, M, N, K);
+}
+
+int pdgemm_pick_splits(int prec, int b_rowmajor, int64_t M, int64_t N, int64_t K, int *cfg) {
+    int c = -1;
+    const int s = (prec < 0 || prec > 2) ? -1 : pick_splits(prec, b_rowmajor ? kBRow : kBCol, M, N, K, &c);
+    if (cfg) *cfg = c;
+    return s;
 }
 
 int pdgemm_config_info(int cfg, int *block_m, int *block_n, int *wave_m, int *wave_n,

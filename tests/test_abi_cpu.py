@@ -338,6 +338,100 @@ def test_pick_weighs_the_last_partial_round(lib):
 
 
 @pytest.fixture(scope="module")
+def sklib(lib):
+    i64, p, i = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.pdgemm_pick_splits.argtypes = [i, i, i64, i64, i64, ctypes.POINTER(i)]
+    lib.pdgemm_pick_splits.restype = i
+    lib.pdgemm_gemm_splitk_cfg.argtypes = [i, i, i, i, i64, i64, i64, p, i64, p, i64, p, i64, p]
+    lib.pdgemm_gemm_splitk_cfg.restype = i
+    return lib
+
+
+def splits_of(lib, prec, rowb, m, n, k):
+    cfg = ctypes.c_int()
+    s = lib.pdgemm_pick_splits(prec, rowb, m, n, k, ctypes.byref(cfg))
+    return s, cfg.value
+
+
+def test_pick_splits_where_measured(sklib):
+    L = sklib
+    # measured gains (row-major B unless noted): 1.2-1.3x, 1.7x, 3x, 1.7x, 1.7x (column-major), 1.2x (FP16)
+    assert splits_of(L, 1, 1, 64, 8192, 8192) == (2, 2)
+    assert splits_of(L, 2, 1, 16, 8192, 8192) == (2, 2)
+    assert splits_of(L, 2, 1, 16, 4096, 16384) == (4, 2)
+    assert splits_of(L, 1, 1, 64, 2048, 32768) == (8, 2)
+    assert splits_of(L, 1, 1, 512, 1024, 32768) == (4, 5)    # 128 x 64 tiles past 64 rows of A
+    assert splits_of(L, 1, 0, 64, 2048, 32768) == (8, 2)
+    assert splits_of(L, 0, 1, 16, 4096, 16384) == (2, 2)
+    # measured losses the rule declines: short K, a chip already filled, the
+    # one-round K-split tile, column-major B over more than 32 tiles, FP16
+    # below K = 16384 or with column-major B
+    for prec, rowb, m, n, k in ((1, 1, 16, 4096, 4096), (2, 1, 16, 2048, 8192), (1, 1, 16, 8192, 2048),
+                                (1, 1, 16, 16384, 4096), (1, 1, 96, 8192, 8192), (2, 1, 1024, 1024, 32768),
+                                (1, 0, 16, 8192, 16384), (2, 0, 16, 4096, 16384), (0, 1, 16, 8192, 8192),
+                                (0, 0, 512, 512, 65536), (1, 0, 8192, 8192, 8192), (0, 1, 2048, 2048, 16384)):
+        s, cfg = splits_of(L, prec, rowb, m, n, k)
+        assert s == 1 and cfg == L.pdgemm_pick_config(prec, m, n, k), (prec, rowb, m, n, k)
+    assert splits_of(L, 3, 0, 64, 64, 64) == (-1, -1)
+    assert L.pdgemm_pick_splits(1, 1, 64, 8192, 8192, None) == 2
+
+
+def test_pick_splits_invariants(sklib):
+    L = sklib
+    info = {}
+    for cfg in range(L.pdgemm_num_configs()):
+        vals = [ctypes.c_int() for _ in range(5)]
+        L.pdgemm_config_info(cfg, *[ctypes.byref(v) for v in vals])
+        info[cfg] = tuple(v.value for v in vals)[:2]
+    seen = set()
+    for prec in range(3):
+        for rowb in (0, 1):
+            for m in (1, 16, 48, 64, 65, 96, 200, 512, 1024, 4096):
+                for n in (64, 500, 2048, 4096, 8192, 16384):
+                    for k in (0, 256, 2048, 4096, 8192, 16384, 65536, 131070):
+                        s, cfg = splits_of(L, prec, rowb, m, n, k)
+                        if s == 1:
+                            assert cfg == L.pdgemm_pick_config(prec, m, n, k)
+                            continue
+                        seen.add(s)
+                        bm, bn = info[cfg]
+                        tiles = -(-m // bm) * -(-n // bn)
+                        assert cfg in (2, 5) and s in (2, 4, 8), (prec, rowb, m, n, k, s, cfg)
+                        assert tiles * s <= 256
+                        if prec == 0:
+                            assert s == 2 and rowb and k >= 16384
+                        else:   # the largest split with at most 256 workgroups
+                            assert s == 8 or tiles * s * 2 > 256
+                            assert k // s >= (2048 if rowb else 4096)
+                        if cfg == 5:
+                            assert prec != 0 and m > 64
+    assert seen == {2, 4, 8}
+
+
+def test_splitk_errors_before_any_hip_call(sklib):
+    L = sklib
+    c = codes()
+    n = L.pdgemm_num_configs()
+    def sk(prec=1, cfg=2, rowb=0, splits=2, M=64, N=64, K=4096, A=PA, lda=None, B=PB, ldb=None):
+        lda = K if lda is None else lda
+        ldb = (N if rowb else K) if ldb is None else ldb
+        return L.pdgemm_gemm_splitk_cfg(prec, cfg, rowb, splits, M, N, K, A, lda, B, ldb, PC, N, None)
+    for cfg in (-1, 0, 1, 3, 4, 6, 7, 8, 9, n):   # only the tiles without an in-workgroup K split, 2 and 5
+        assert sk(cfg=cfg) == c["PDGEMM_EINVAL_CFG"], cfg
+    assert sk(prec=3) == c["PDGEMM_EINVAL_CFG"]
+    assert sk(splits=0) == c["PDGEMM_EINVAL_CFG"]
+    assert sk(prec=0, splits=3) == c["PDGEMM_EINVAL_CFG"]          # FP16: at most two ranges
+    assert sk(prec=0, splits=4, rowb=1) == c["PDGEMM_EINVAL_CFG"]
+    assert sk(lda=4000) == c["PDGEMM_EINVAL_LD"]
+    assert sk(rowb=1, ldb=32) == c["PDGEMM_EINVAL_LD"]
+    assert sk(B=None) == c["PDGEMM_ENULL"]
+    assert sk(A=PA + 8) == c["PDGEMM_EALIGN"]
+    assert sk(prec=2, K=4095, lda=4096, ldb=4096) == c["PDGEMM_EINVAL_I4"]
+    assert sk(M=-1) == c["PDGEMM_EINVAL_DIM"]
+    assert sk(M=0) == 0 and sk(N=0, rowb=0) == 0
+
+
+@pytest.fixture(scope="module")
 def wslib(lib):
     i64, p, i = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     for name in ("gemm_i4_ws", "gemm_i4_rowb_ws"):
