@@ -769,7 +769,21 @@ def main():
                     entry["packed_b_ms_back_to_back"] = round(time_b2b(packed_go, 0.05), 5)
                     del Cp, wsp
                 if prec in brow_dev:
-                    # the same product with B row-major
+                    # the same product with B row-major (integers: K split across
+                    # workgroups where pick_splits asks), checked on the same entries
+                    entry["rowb_splits"] = list(pd.pick_splits({"f16": 0, "i8": 1, "i4": 2}[prec], M, n, n,
+                                                               rowb=True))
+                    rowb_go = pd.prepare(prec, Ad[:M], brow_dev[prec], Cm, K=n, rowb=True)
+                    rowb_go()
+                    torch.cuda.synchronize()
+                    if not args.no_parity:
+                        got = Cm.cpu().numpy()[rows, cols]
+                        if prec == "f16":
+                            ok = bool(np.all(np.abs(got.astype(np.float64) - R) <= 1e-3 * S))
+                        else:
+                            ok = bool(np.array_equal(got.astype(np.int64), ref))
+                        entry["rowb_parity"] = ok
+                        parity[f"{prec}:{M}x{n}x{n}:rowb"] = ok
                     entry["rowb_ms_back_to_back"] = round(time_b2b(
                         lambda: pd.prepare(prec, Ad[:M], brow_dev[prec], Cm, K=n, rowb=True), 0.05), 5)
                 shapes[f"{prec}:{M}x{n}x{n}"] = entry
