@@ -97,15 +97,22 @@ def test_f16_long_k_ones(pd, dev, M, N):
 LD = {"f16": MAX_ROW_BYTES // 2, "i8": MAX_ROW_BYTES, "i4": MAX_ROW_BYTES * 2}   # in elements
 
 
+# (tile configuration, ranges of K split across workgroups): the 64 x 64 and
+# 128 x 64 tiles split two (FP16) or three ways start each range's A and B
+# at an offset of whole stages into rows of 4 MiB
+SPLITS = {"f16": 2, "i8": 3, "i4": 3}
+
+
 @pytest.mark.parametrize("prec", ["f16", "i8", "i4"])
-@pytest.mark.parametrize("cfg", [0, 3, 9])
-def test_largest_leading_dimensions(pd, dev, prec, cfg):
-    # 256 x 256 tiles (configuration 0) and the K-split 32 x 32 and 64 x 64 tiles (3, 9), with rows of
-    # A, B and C of 4 MiB; M, N and K ragged
-    M, N, K = 250, 70, 200
+@pytest.mark.parametrize("cfg,split", [(0, False), (3, False), (9, False), (2, True), (5, True)])
+def test_largest_leading_dimensions(pd, dev, prec, cfg, split):
+    # 256 x 256 tiles (configuration 0), the K-split 32 x 32 and 64 x 64 tiles (3, 9), and
+    # K split across workgroups (2, 5), with rows of A, B and C of 4 MiB; M, N and K ragged
+    M, N, K = 250, 70, 200 if not split else 1000
+    splits = SPLITS[prec] if split else None
     ld = LD[prec]
     ldc = MAX_ROW_BYTES // 4
-    gu.note(f"[case] largest ld {prec} cfg={cfg} lda=ldb={ld} ldc={ldc}")
+    gu.note(f"[case] largest ld {prec} cfg={cfg} splits={splits} lda=ldb={ld} ldc={ldc}")
     A, Bt = synth.operands(prec, M, N, K, 77, 78)
     cols = K // 2 if prec == "i4" else K
     ld_cols = ld // 2 if prec == "i4" else ld
@@ -119,11 +126,11 @@ def test_largest_leading_dimensions(pd, dev, prec, cfg):
     Cbuf = torch.zeros((M, ldc), dtype=out_dtype, device=dev)
     out = Cbuf[:, :N]
     if prec == "f16":
-        pd.gemm_f16(Ad[:, :cols], Bd[:, :cols], out=out, cfg=cfg)
+        pd.gemm_f16(Ad[:, :cols], Bd[:, :cols], out=out, cfg=cfg, splits=splits)
     elif prec == "i8":
-        pd.gemm_i8(Ad[:, :cols], Bd[:, :cols], out=out, cfg=cfg)
+        pd.gemm_i8(Ad[:, :cols], Bd[:, :cols], out=out, cfg=cfg, splits=splits)
     else:
-        pd.gemm_i4(Ad[:, :cols], Bd[:, :cols], K, out=out, cfg=cfg)
+        pd.gemm_i4(Ad[:, :cols], Bd[:, :cols], K, out=out, cfg=cfg, splits=splits)
     torch.cuda.synchronize()
     C = out.cpu().numpy()
     assert torch.count_nonzero(Cbuf[:, N:]) == 0, "stores past column N"
@@ -137,16 +144,19 @@ def test_largest_leading_dimensions(pd, dev, prec, cfg):
 
 
 @pytest.mark.parametrize("prec", ["f16", "i8", "i4"])
-@pytest.mark.parametrize("cfg", [0, 3, 6, 9])
-def test_largest_leading_dimension_row_major_b(pd, dev, prec, cfg):
+@pytest.mark.parametrize("cfg,split", [(0, False), (3, False), (6, False), (9, False), (2, True), (5, True)])
+def test_largest_leading_dimension_row_major_b(pd, dev, prec, cfg, split):
     # B row-major with rows of 4 MiB, on the 256 x 256 tile (0) and on the K-split
     # tiles (3: 32 x 32, 6: 64 x 32, 9: 64 x 64), whose waves each stage their own slice of
     # rows of B; K reaches the last slice of a stage (a 64 x 32 INT4 stage spans
     # 1024 rows of B, 4 GiB at this row size)
+    # (2, 5: K split across workgroups, each range's B starting whole stages of
+    # 4 MiB rows in)
     M, N, K = 50, 70, 1000
+    splits = SPLITS[prec] if split else None
     ld = LD[prec]
     ldc = MAX_ROW_BYTES // 4
-    gu.note(f"[case] largest ldb row-major B {prec} cfg={cfg} ldb={ld} ldc={ldc} K={K}")
+    gu.note(f"[case] largest ldb row-major B {prec} cfg={cfg} splits={splits} ldb={ld} ldc={ldc} K={K}")
     if prec == "i4":
         A = synth.pack_int4(synth.int4_values(M, K, 91))
         B = synth.pack_int4(np.ascontiguousarray(synth.int4_values(N, K, 92).T))   # (K, N/2)
@@ -167,11 +177,11 @@ def test_largest_leading_dimension_row_major_b(pd, dev, prec, cfg):
     out = Cbuf[:, :N]
     Bv = Bd[:K, :cols_b]
     if prec == "f16":
-        pd.gemm_f16_rowb(Ad[:, :cols_a], Bv, out=out, cfg=cfg)
+        pd.gemm_f16_rowb(Ad[:, :cols_a], Bv, out=out, cfg=cfg, splits=splits)
     elif prec == "i8":
-        pd.gemm_i8_rowb(Ad[:, :cols_a], Bv, out=out, cfg=cfg)
+        pd.gemm_i8_rowb(Ad[:, :cols_a], Bv, out=out, cfg=cfg, splits=splits)
     else:
-        pd.gemm_i4_rowb(Ad[:, :cols_a], Bv, K, N, out=out, cfg=cfg)
+        pd.gemm_i4_rowb(Ad[:, :cols_a], Bv, K, N, out=out, cfg=cfg, splits=splits)
     torch.cuda.synchronize()
     C = out.cpu().numpy()
     assert torch.count_nonzero(Cbuf[:, N:]) == 0, "stores past column N"
