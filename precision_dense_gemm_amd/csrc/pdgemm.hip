@@ -1731,12 +1731,16 @@ int launch(int prec, int cfg, int epi, int br, int64_t M, int64_t N, int64_t K, 
     return PDGEMM_OK;
 }
 
-// zeroes the M x N block of a 32-bit C (row stride ldc): one column per
-// thread, 256 columns by a stride of rows per workgroup
+// zeroes the M x N block of a 32-bit C (row stride ldc): a workgroup clears
+// 1024 columns (four coalesced passes of 256) of every gridDim.y-th row
 __global__ __launch_bounds__(256) void zero_rows_kernel(int32_t *C, int64_t ldc, int M, int N) {
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= N) return;
-    for (int64_t r = blockIdx.y; r < M; r += gridDim.y) C[r * ldc + c] = 0;
+    const int c0 = blockIdx.x * 1024 + threadIdx.x;
+    for (int64_t r = blockIdx.y; r < M; r += gridDim.y) {
+        int32_t *const row = C + r * ldc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (c0 + 256 * j < N) row[c0 + 256 * j] = 0;
+    }
 }
 
 // Tiles a K split across workgroups runs on: 64 x 64 and 128 x 64 (the
@@ -1805,7 +1809,7 @@ int launch_splitk(int prec, int cfg, int br, int splits, int64_t M, int64_t N, i
     hipStream_t s = static_cast<hipStream_t>(stream);
     void *zargs[] = {&C, &ldc, &args.M, &args.N};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&zero_rows_kernel),
-                                   dim3((unsigned)cdiv(N, 256), (unsigned)std::min<int64_t>(M, 1024)), dim3(256), zargs, 0, s);
+                                   dim3((unsigned)cdiv(N, 1024), (unsigned)std::min<int64_t>(M, 1024)), dim3(256), zargs, 0, s);
     if (e != hipSuccess) return (int)e;
     void *kargs[] = {&args};
     e = hipLaunchKernel(fn, dim3((unsigned)blocks, (unsigned)ranges), dim3(threads), kargs, 0, s);
