@@ -1,7 +1,8 @@
 """Seeded random parity sweep on the GPU: for every precision and entry-point family
-(plain, row-major B, dequantizing to fp32 or binary16), shapes, padded leading
-dimensions and a tile configuration (the entry points' own choice or any of them) are
-drawn from a fixed seed, and every output is compared in full with the oracle (integers
+(plain, row-major B, dequantizing to fp32 or binary16, and the plain and row-major
+GEMMs with K split across workgroups), shapes, padded leading dimensions and a tile
+configuration (the entry points' own choice or any of them; for the split families a
+split tile and 1-8 ranges, 1-2 for FP16) are drawn from a fixed seed, and every output is compared in full with the oracle (integers
 and dequantized outputs bit for bit, FP16 within 1e-3 * sum |a*b|).  Operands sit in
 poison-padded buffers and outputs in sentinel-guarded ones."""
 from __future__ import annotations
@@ -47,30 +48,38 @@ def padded(host, width, fill, dev):
     return gu.to_device_padded(torch, host, width, fill, dev)
 
 
-@pytest.mark.parametrize("family", ["plain", "rowb", "dequant32", "dequant16"])
+FAMILIES = ["plain", "rowb", "dequant32", "dequant16", "split", "split_rowb"]
+
+
+@pytest.mark.parametrize("family", FAMILIES)
 @pytest.mark.parametrize("prec", ["f16", "i8", "i4"])
 def test_random_shapes(pd, dev, prec, family):
     if family.startswith("dequant") and prec == "f16":
         pytest.skip("the dequantizing epilogue is for the integer paths")
-    rng = np.random.default_rng({"f16": 1, "i8": 2, "i4": 3}[prec] * 100 +
-                                ["plain", "rowb", "dequant32", "dequant16"].index(family))
+    rng = np.random.default_rng({"f16": 1, "i8": 2, "i4": 3}[prec] * 100 + FAMILIES.index(family))
     poison = gu.POISON[prec]
+    base = {"split": "plain", "split_rowb": "rowb"}.get(family, family)
     for case in range(CASES):
         M, N, K, cfg, pad = draw(rng, prec, pd.num_configs())
+        splits = None
+        if family.startswith("split"):
+            cfg = int(rng.choice([2, 5]))
+            splits = int(rng.integers(1, 3 if prec == "f16" else 9))
         seed = int(rng.integers(0, 2 ** 31))
-        gu.note(f"[case] random {prec} {family} #{case}: M={M} N={N} K={K} cfg={cfg} pad={pad} seed={seed}")
+        gu.note(f"[case] random {prec} {family} #{case}: M={M} N={N} K={K} cfg={cfg} splits={splits} "
+                f"pad={pad} seed={seed}")
         A, Bt = synth.operands(prec, M, N, K, seed, seed + 1)
         a_w = gu.round_up(A.shape[1], 16 // (2 if prec == "f16" else 1)) + pad * 16 // (2 if prec == "f16" else 1)
         Ad = padded(A, max(a_w, 16 // (2 if prec == "f16" else 1)), poison, dev)
         odt = {"plain": torch.float32 if prec == "f16" else torch.int32, "rowb": torch.float32 if prec == "f16"
-               else torch.int32, "dequant32": torch.float32, "dequant16": torch.float16}[family]
+               else torch.int32, "dequant32": torch.float32, "dequant16": torch.float16}[base]
         ldc = N + int(rng.integers(0, 5))
         if odt == torch.float16:
             buf = torch.full((M + 2, ldc), 0x7DAD, dtype=torch.int16, device=dev).view(torch.float16)
         else:
             buf = torch.empty((M + 2, ldc), dtype=torch.int32, device=dev).fill_(gu.C_SENTINEL_BITS).view(odt)
         out = buf[:M, :N]
-        if family == "rowb":
+        if base == "rowb":
             if prec == "i4":
                 vals = synth.unpack_int4(Bt)[:, :K].T        # (K, N)
                 if N % 2:
@@ -83,26 +92,26 @@ def test_random_shapes(pd, dev, prec, family):
             Bbuf[:K, :B.shape[1]] = B
             Bd = torch.from_numpy(Bbuf).to(dev)[:K, :B.shape[1]]
             if prec == "f16":
-                pd.gemm_f16_rowb(Ad, Bd, out=out, cfg=cfg)
+                pd.gemm_f16_rowb(Ad, Bd, out=out, cfg=cfg, splits=splits)
                 R, S = oracle.gemm_f16_rowb(A, B, N=N, K=K)
             elif prec == "i8":
-                pd.gemm_i8_rowb(Ad, Bd, out=out, cfg=cfg)
+                pd.gemm_i8_rowb(Ad, Bd, out=out, cfg=cfg, splits=splits)
                 ref = oracle.gemm_i8_rowb(A, B, N=N, K=K)
             else:
-                pd.gemm_i4_rowb(Ad, Bd, K, N, out=out, cfg=cfg)
+                pd.gemm_i4_rowb(Ad, Bd, K, N, out=out, cfg=cfg, splits=splits)
                 ref = oracle.gemm_i4_rowb(A, B, N=N, K=K)
         else:
             b_w = gu.round_up(Bt.shape[1], 16 // (2 if prec == "f16" else 1)) + pad * 16 // (2 if prec == "f16" else 1)
             Bd = padded(Bt, max(b_w, 16 // (2 if prec == "f16" else 1)), poison, dev)
-            if family == "plain":
+            if base == "plain":
                 if prec == "f16":
-                    pd.gemm_f16(Ad, Bd, out=out, cfg=cfg)
+                    pd.gemm_f16(Ad, Bd, out=out, cfg=cfg, splits=splits)
                     R, S = oracle.gemm_f16(A, Bt, K=K)
                 elif prec == "i8":
-                    pd.gemm_i8(Ad, Bd, out=out, cfg=cfg)
+                    pd.gemm_i8(Ad, Bd, out=out, cfg=cfg, splits=splits)
                     ref = oracle.gemm_i8(A, Bt, K=K)
                 else:
-                    pd.gemm_i4(Ad, Bd, K, out=out, cfg=cfg)
+                    pd.gemm_i4(Ad, Bd, K, out=out, cfg=cfg, splits=splits)
                     ref = oracle.gemm_i4(A, Bt, K=K)
             else:
                 sa, sb = synth.f32_scales(M, seed + 2), synth.f32_scales(N, seed + 3)
@@ -122,7 +131,7 @@ def test_random_shapes(pd, dev, prec, family):
         sentinel = np.int16(0x7DAD) if odt == torch.float16 else np.int32(gu.C_SENTINEL_BITS)
         assert np.all(bits[outside] == sentinel), f"stores outside M x N in case #{case}"
         C = host[:M, :N]
-        what = f"{prec} {family} #{case} M={M} N={N} K={K} cfg={cfg}"
+        what = f"{prec} {family} #{case} M={M} N={N} K={K} cfg={cfg} splits={splits}"
         if family.startswith("dequant"):
             gw = want.view(np.uint16 if family == "dequant16" else np.uint32)
             gc = C.view(np.uint16 if family == "dequant16" else np.uint32)
