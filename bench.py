@@ -305,6 +305,14 @@ COLD_MAX_N, COLD_REPS = 2048, 10   # cold-cache timing: sweep sizes up to this N
 TELEMETRY_S = 3.0                  # seconds of sustained sweep load sampled for power and clock
 
 
+def kernel_name(pd, prec, n, i4_path=None):
+    """The GEMM kernel the library runs for an n^3 GEMM of `prec` with column-major B."""
+    if prec == "i4" and i4_path == "fp6":
+        return "gemm_f6_kernel"
+    cfg = pd.pick_config({"f16": pd.PREC_F16, "i8": pd.PREC_I8, "i4": pd.PREC_I4}[prec], n, n, n)
+    return "gemm_f16_mf16_kernel" if prec == "f16" and cfg == 0 else "gemm_kernel"
+
+
 def shape_roofline(prec, M, N, K, ms):
     """Achieved rate of one M x N x K GEMM against the roof that bounds it: HBM for
     algorithmic bytes / peak bandwidth above flops / peak MFMA, else MFMA."""
@@ -828,7 +836,7 @@ def main():
     per[dom]["ms_timed_steps"] = round(float(np.mean(dom_ms)), 5)
     roofline = {
         "bound": "mfma",
-        "kernel": f"gemm_kernel {dprec} N={dn}",
+        "kernel": f"{kernel_name(pd, dprec, dn, i4_path.get(dn))} {dprec} N={dn}",
         "achieved": round(dom_tops, 2),
         "peak": PEAK[dprec],
         "unit": "TFLOP/s" if dprec == "f16" else "TOPS",

@@ -18,6 +18,9 @@
 //    take, per lane, 16 contiguous bytes of K of one row of A and of one
 //    column of B, so FP16, INT8 and packed INT4 share one LDS geometry: a K
 //    tile is 64 bytes of K per row of A (32 f16, 64 int8, 128 int4 values).
+//    The largest FP16 tile with column-major B runs v_mfma_f32_16x16x32_f16
+//    instead (same per-lane 16 bytes, fewer register accesses per MAC: see
+//    gemm_f16_mf16_kernel).
 //  * INT4: gfx950 has no signed 4-bit MFMA (the paper's m16n8k64.s4 path,
 //    Listing 2, has no equivalent here).  INT4 stays packed in LDS; after a
 //    fragment read each packed dword w is split in registers into two int8
@@ -1473,6 +1476,259 @@ gemm_f6_kernel(F6Args args) {
 }
 
 // ---------------------------------------------------------------------------
+// The 256 x 256 FP16 tile on 16 x 16 MFMAs
+//
+// At the large FP16 shapes the board runs at its power limit, so a GEMM's
+// time follows its energy.  v_mfma_f32_32x32x16_f16 reads 8 operand
+// registers and reads and writes 16 accumulator registers per 16384 MACs;
+// v_mfma_f32_16x16x32_f16 reads 8 operand registers and reads and writes 4
+// accumulator registers per 8192 MACs, a fifth fewer register accesses per
+// MAC for the same LDS traffic and the same number of MFMA cycles.  Measured
+// on configuration 0 (256 x 256, 8 waves of 128 x 64, two whole-line stages)
+// with column-major B: FP16 8192^3 800 against 847 us back to back (4096^3
+// 115 against 117, with bit-identical results); INT8 moved by about 1% either
+// way and keeps the 32 x 32 form, and so do the other tiles and layouts.
+//
+// The stage geometry is that of the whole-line kernel (two stages of 128
+// bytes of K per row, 256 rows of A then 256 of B, chunk c of row r at
+// position c ^ swizzle8(r), each DMA instruction writing 8 whole rows).  The
+// MFMA takes, per lane, 8 f16 values of K: lane l of a 16-row block holds
+// row l % 16 and values 8 (l / 16) .. + 7 of a 32-value k-step, so a k-step
+// is 64 bytes (logical chunks 4 q .. 4 q + 3 of stage k-step q = 0, 1) and
+// the 16 lanes of a quarter-wave read 16 consecutive rows at one logical
+// chunk, the pattern the swizzle keeps free of bank conflicts.  A wave's
+// 128 x 64 block is 8 x 4 MFMA blocks (128 accumulator registers); its A
+// fragments are held in halves of four row blocks, so that the fragments of
+// the next half k-step fit beside the current ones and the accumulators
+// within the 256 registers of two waves per SIMD.  Result of block (i, j),
+// register e of lane l: row 16 i + 4 (l / 16) + e, column 16 j + l % 16.
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4_t mfma16_f16(const uint4 &a, const uint4 &b, const floatx4_t &c) {
+    half8_t av, bv;
+    __builtin_memcpy(&av, &a, 16);
+    __builtin_memcpy(&bv, &b, 16);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(512) void gemm_f16_mf16_kernel(Args args) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int BM = 256, BN = 256, WM = 128, WN = 64, GM = 4;
+    constexpr int NW = (BM / WM) * (BN / WN);   // 8 waves
+    constexpr int kWavesN = BN / WN;
+    constexpr int kRows = BM + BN;              // LDS rows per stage
+    constexpr int kDmaL = kRows / 8 / NW;       // 1 KB DMA instructions per wave per stage
+    constexpr int kDmaLA = BM / 8 / NW;         // ... of which fill A rows
+    constexpr int kStageK = 2 * kRowBytes;      // bytes of K per row per stage
+    constexpr int FM = WM / 16, FN = WN / 16;   // MFMA blocks of a wave
+    constexpr int FH = FM / 2;                  // A fragments per half k-step
+    __shared__ uint4 ln0[kRows][2 * kChunks];
+    __shared__ uint4 ln1[kRows][2 * kChunks];
+    using LStage = uint4[kRows][2 * kChunks];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int M = args.M, N = args.N, K = args.K;
+    int tile_m, tile_n;
+    tile_of<GM>(args.tiles_m, args.tiles_n, tile_m, tile_n);
+    const int m0 = tile_m * BM;
+    const int n0 = tile_n * BN;
+
+    // operand rows past M (N) are clamped to the last valid one; the buffer
+    // range of a stage ends at the last 16-byte chunk of the last valid row
+    // that holds data, and is zero for a stage past K (as in gemm_kernel)
+    const int valid = 2 * K;                        // data bytes per row
+    const int valid16 = (valid + 15) & ~15;
+    const int n_st = (valid + kStageK - 1) / kStageK;
+    const uint8_t *const a_base = args.A + (int64_t)m0 * args.lda_bytes;
+    const int a_end = (int)((min(BM, M - m0) - 1) * args.lda_bytes) + valid16;
+    const uint8_t *const b_base = args.B + (int64_t)n0 * args.ldb_bytes;
+    const int b_end = (int)((min(BN, N - n0) - 1) * args.ldb_bytes) + valid16;
+    // DMA instruction j of this wave fills stage rows (j*NW + wave)*8 .. +7;
+    // lane l fetches logical chunk (l%8) ^ swizzle8(row) of row l/8
+    uint32_t voffl[kDmaL];
+#pragma unroll
+    for (int j = 0; j < kDmaL; ++j) {
+        const int cr = (j * NW + wave) * 8 + (lane >> 3);
+        const int lchunk = (lane & 7) ^ swizzle8(cr);
+        if (j < kDmaLA)
+            voffl[j] = (uint32_t)((min(m0 + cr, M - 1) - m0) * args.lda_bytes) + lchunk * 16;
+        else
+            voffl[j] = (uint32_t)((min(n0 + cr - BM, N - 1) - n0) * args.ldb_bytes) + lchunk * 16;
+    }
+    auto stage_l = [&](int st, LStage &buf) __attribute__((always_inline)) {
+        const int kb = st * kStageK;
+        const bool live = st < n_st;
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a_base + kb), (short)0, live ? a_end - kb : 0, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(b_base + kb), (short)0, live ? b_end - kb : 0, kRsrcWord3);
+#pragma unroll
+        for (int j = 0; j < kDmaL; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kDmaLA ? ra : rb, LDS_PTR(&buf[(j * NW + wave) * 8][0]),
+                                                     16, voffl[j], 0, 0, 0);
+    };
+
+    const int wm0 = (wave / kWavesN) * WM;   // wave's first row / column in the block tile
+    const int wn0 = (wave % kWavesN) * WN;
+    const int frow = lane & 15;              // fragment row (A) / column (B) of this lane
+    const int fq = lane >> 4;                // which 16-byte quarter of a 64-byte k-step
+    // fragment rows start at multiples of 16, so the swizzle of row frow applies
+    // A fragments of k-step q for row blocks hi*FH .. hi*FH + FH-1
+    auto read_a = [&](const LStage &buf, int q, int hi, uint4 (&fa)[FH]) __attribute__((always_inline)) {
+        const int ch = (4 * q + fq) ^ swizzle8(frow);
+#pragma unroll
+        for (int i = 0; i < FH; ++i) fa[i] = buf[wm0 + (hi * FH + i) * 16 + frow][ch];
+    };
+    auto read_b = [&](const LStage &buf, int q, uint4 (&fb)[FN]) __attribute__((always_inline)) {
+        const int ch = (4 * q + fq) ^ swizzle8(frow);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[j] = buf[BM + wn0 + j * 16 + frow][ch];
+    };
+    // zero the bytes of this lane's fragments of k-step q of stage st at or beyond K
+    auto mask = [&](int st, int q, uint4 *f, int n) __attribute__((always_inline)) {
+        const int nb = valid - (st * kStageK + (4 * q + fq) * 16);
+        uint32_t m[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const int r = nb - 4 * d;
+            m[d] = r >= 4 ? 0xFFFFFFFFu : (r <= 0 ? 0u : (1u << (8 * r)) - 1u);
+        }
+#pragma unroll
+        for (int i = 0; i < n; ++i) {
+            f[i].x &= m[0];
+            f[i].y &= m[1];
+            f[i].z &= m[2];
+            f[i].w &= m[3];
+        }
+    };
+
+    floatx4_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = 0;
+    auto mma_half = [&](int hi, const uint4 (&fa)[FH], const uint4 (&fb)[FN]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < FH; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[hi * FH + i][j] = mfma16_f16(fa[i], fb[j], acc[hi * FH + i][j]);
+    };
+    // issue order of a half k-step: its MFMAs with the next fragment reads
+    // (and, after the stage barrier, the DMA of a later stage) slotted one by
+    // one between them
+    constexpr int kMfma = FH * FN;
+    auto interleave = [&](auto reads_c, auto dma_c) __attribute__((always_inline)) {
+        constexpr int reads = decltype(reads_c)::value;
+        constexpr int dma = decltype(dma_c)::value;
+        static_assert(reads <= kMfma && dma <= kMfma, "one read and one DMA per MFMA slot at most");
+#pragma unroll
+        for (int i = 0; i < kMfma; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // 1 MFMA
+            if (i < reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+            if (i < dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // 1 DMA
+        }
+    };
+    using kNone = std::integral_constant<int, 0>;
+    using kHalfA = std::integral_constant<int, FH>;
+    using kHalfAB = std::integral_constant<int, FH + FN>;
+    using kStageDma = std::integral_constant<int, kDmaL>;
+
+    // A fragments of the lower (fL) and upper (fU) row blocks; B fragments of
+    // the even (fbA) and odd (fbB) k-step of a stage
+    uint4 fL[FH], fU[FH], fbA[FN], fbB[FN];
+    // stage st (not the last) from `cur`, whose k-step 0 lower half is in
+    // fL / fbA; refills `cur` with stage st+2 and reads the first fragments
+    // of stage st+1 from `nxt`
+    auto full_stage = [&](LStage &cur, const LStage &nxt, int st) __attribute__((always_inline)) {
+        read_a(cur, 0, 1, fU);
+        mma_half(0, fL, fbA);
+        interleave(kHalfA{}, kNone{});
+        read_a(cur, 1, 0, fL);
+        read_b(cur, 1, fbB);
+        mma_half(1, fU, fbA);
+        interleave(kHalfAB{}, kNone{});
+        read_a(cur, 1, 1, fU);
+        mma_half(0, fL, fbB);
+        interleave(kHalfA{}, kNone{});
+        // this wave's DMA of stage st+1 has landed and its reads of `cur`
+        // are done; after the barrier the same holds for every wave
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        stage_l(st + 2, cur);
+        read_a(nxt, 0, 0, fL);
+        read_b(nxt, 0, fbA);
+        mma_half(1, fU, fbB);
+        interleave(kHalfAB{}, kStageDma{});
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // the last stage, with the bytes at or beyond K masked off
+    auto last_stage = [&](const LStage &cur, int st) __attribute__((always_inline)) {
+        read_a(cur, 0, 1, fU);
+        mask(st, 0, fL, FH);
+        mask(st, 0, fbA, FN);
+        mask(st, 0, fU, FH);
+        mma_half(0, fL, fbA);
+        mma_half(1, fU, fbA);
+        read_a(cur, 1, 0, fL);
+        read_b(cur, 1, fbB);
+        read_a(cur, 1, 1, fU);
+        mask(st, 1, fL, FH);
+        mask(st, 1, fbB, FN);
+        mask(st, 1, fU, FH);
+        mma_half(0, fL, fbB);
+        mma_half(1, fU, fbB);
+    };
+    if (n_st > 0) {
+        stage_l(0, ln0);
+        stage_l(1, ln1);
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaL) : "memory");
+        read_a(ln0, 0, 0, fL);
+        read_b(ln0, 0, fbA);
+        int st = 0;
+        for (; st + 2 < n_st; st += 2) {
+            full_stage(ln0, ln1, st);
+            full_stage(ln1, ln0, st + 1);
+        }
+        if (st + 1 < n_st) full_stage(ln0, ln1, st++);
+        last_stage((st & 1) ? ln1 : ln0, st);
+        // no DMA may still be writing this workgroup's LDS when it exits
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+
+    // ---- epilogue: 16 x 16 MFMA result layout -> row-major C, non-temporal ----
+    char *const wave_c = reinterpret_cast<char *>(args.C) + ((int64_t)(m0 + wm0) * args.ldc + n0 + wn0) * 4;
+    const int64_t row_bytes = args.ldc * 4;
+    const uint32_t lane_off = (uint32_t)(4 * fq * row_bytes) + frow * 4u;
+    const bool interior = m0 + BM <= M && n0 + BN <= N;
+    const int rows_left = M - (m0 + wm0) - 4 * fq;   // rows this lane may write: r < rows_left
+    const int cols_left = N - (n0 + wn0) - frow;     // columns: 16 j < cols_left
+    auto store_all = [&](auto &&keep) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = i * 16 + e;   // wave-uniform part of the row
+                char *const row_c = wave_c + r * row_bytes;
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    if (keep(r, j))
+                        __builtin_nontemporal_store(acc[i][j][e],
+                                                    reinterpret_cast<float *>(row_c + lane_off + j * 64));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    if (interior)
+        store_all([](int, int) { return true; });
+    else
+        store_all([&](int r, int j) { return r < rows_left && j * 16 < cols_left; });
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+// ---------------------------------------------------------------------------
 // host side
 
 // ls: whole-line stages, or 0 for four 64-byte stages.  Only the 32 x 32
@@ -1490,7 +1746,7 @@ struct Config {
 };
 
 constexpr Config kConfigs[] = {
-    {256, 256, 128, 64, 4, 1, 2},   // 0: large shapes (8 waves)
+    {256, 256, 128, 64, 4, 1, 2},   // 0: large shapes (8 waves; FP16 with column-major B on 16 x 16 MFMAs)
     {128, 128, 64, 64, 8, 1, 2},    // 1: medium
     {64, 64, 32, 32, 8, 1, 3},      // 2: small
     {32, 32, 32, 32, 8, 4, 0},      // 3: few tiles (small M or N): K split over 4 waves
@@ -1515,7 +1771,12 @@ const void *kernel_for() {
 template <int P, int E, int BR>
 const void *kernel_ptr(int cfg) {
     switch (cfg) {
-    case 0: return kernel_for<P, 0, E, BR>();
+    case 0:
+        // FP16 with column-major B: the same tile on 16 x 16 MFMAs
+        if constexpr (P == kF16 && E == kRaw && BR == kBCol)
+            return reinterpret_cast<const void *>(&gemm_f16_mf16_kernel);
+        else
+            return kernel_for<P, 0, E, BR>();
     case 1: return kernel_for<P, 1, E, BR>();
     case 2: return kernel_for<P, 2, E, BR>();
     case 3: return kernel_for<P, 3, E, BR>();

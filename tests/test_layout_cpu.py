@@ -52,6 +52,40 @@ def test_line_fragment_reads_are_bank_conflict_free():
                 assert len({c ^ swizzle8(r) for r in rows[o:o + 8]}) == 8
 
 
+def test_mf16_fragment_reads():
+    # The FP16 256 x 256 tile on 16 x 16 MFMAs: in k-step q (0, 1) of a 128-byte stage row,
+    # lane l of a 16-row block reads row l%16 at logical chunk 4q + l//16, i.e. f16 values
+    # 32q + 8(l//16) .. +7, the 8 values of K the MFMA expects in that lane.
+    for base in range(0, 512, 16):
+        covered = {}
+        for q in (0, 1):
+            for quarter in range(4):
+                lanes = range(16 * quarter, 16 * quarter + 16)
+                rows = [base + (l % 16) for l in lanes]
+                chunks = [4 * q + l // 16 for l in lanes]
+                pos = [c ^ swizzle8(r) for r, c in zip(rows, chunks)]
+                # 64 banks: the 16 lanes of a quarter-wave cover distinct 16-byte bank groups
+                assert len({32 * (r % 2) + 4 * p for r, p in zip(rows, pos)}) == 16
+                for l, r, c in zip(lanes, rows, chunks):
+                    assert c * 8 == 32 * q + 8 * (l // 16)   # first f16 value of K in the lane
+                    covered[(r, c)] = covered.get((r, c), 0) + 1
+        # the two k-steps read every 16-byte chunk of the 16 rows exactly once
+        assert covered == {(base + i, c): 1 for i in range(16) for c in range(8)}
+
+
+def test_mf16_result_layout_covers_the_wave_tile():
+    # register e of lane l in block (i, j): row 16i + 4(l//16) + e, column 16j + l%16,
+    # over the 8 x 4 blocks of a 128 x 64 wave tile: each element once
+    seen = set()
+    for i in range(8):
+        for j in range(4):
+            for l in range(64):
+                for e in range(4):
+                    seen.add((16 * i + 4 * (l // 16) + e, 16 * j + l % 16))
+    assert seen == {(r, c) for r in range(128) for c in range(64)}
+    assert 8 * 4 * 64 * 4 == 128 * 64
+
+
 @pytest.mark.parametrize("bm,bn,waves", [(256, 256, 8), (128, 128, 4), (64, 64, 4), (256, 128, 8), (128, 64, 4),
                                          (32, 32, 1), (64, 32, 1)])
 def test_line_dma_fills_every_row_once(bm, bn, waves):
