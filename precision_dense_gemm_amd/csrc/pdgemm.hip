@@ -1756,6 +1756,7 @@ constexpr Config kConfigs[] = {
     {128, 128, 64, 64, 8, 1, 3},    // 7: 1 with three stages, for at most one round of tiles
     {256, 256, 128, 128, 4, 1, 2},  // 8: 0 with 4 waves of 128 x 128 (never picked: kept to compare)
     {64, 64, 64, 64, 8, 4, 2},      // 9: 2 with K split over 4 waves, for one round of tiles and long K
+    {256, 256, 128, 64, 4, 1, 2},   // 10: 0 on 32 x 32 MFMAs for FP16 too (never picked: kept to compare)
 };
 
 // Tiles without K split, largest first: the order in which pick() tries them.
@@ -1786,6 +1787,7 @@ const void *kernel_ptr(int cfg) {
     case 7: return kernel_for<P, 7, E, BR>();
     case 8: return kernel_for<P, 8, E, BR>();
     case 9: return kernel_for<P, 9, E, BR>();
+    case 10: return kernel_for<P, 10, E, BR>();
     default: return nullptr;
     }
 }
@@ -1833,12 +1835,12 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // three alternated rounds, mean of two GPUs) on a product that gives every
 // one of them whole rounds of workgroups (M = K = 8192, N = 6144); only the
 // ratios within a row matter.  0 = not a candidate (the K-split tiles, 7,
-// which stands in for 1, 9, which stands in for 2, and 8, the 4-wave form
-// of 0, slower than 0 at N = 8192).
+// which stands in for 1, 9, which stands in for 2, 8, the 4-wave form of 0,
+// slower than 0 at N = 8192, and 10, 0 on 32 x 32 MFMAs for FP16).
 constexpr int kTileRate[3][kNumConfigs] = {
-    {1267, 1019, 703, 0, 1126, 778, 0, 0, 0, 0},    // FP16
-    {2449, 2060, 1329, 0, 2171, 1616, 0, 0, 0, 0},  // INT8
-    {2824, 2440, 1863, 0, 2499, 2021, 0, 0, 0, 0},  // INT4
+    {1267, 1019, 703, 0, 1126, 778, 0, 0, 0, 0, 0},    // FP16
+    {2449, 2060, 1329, 0, 2171, 1616, 0, 0, 0, 0, 0},  // INT8
+    {2824, 2440, 1863, 0, 2499, 2021, 0, 0, 0, 0, 0},  // INT4
 };
 
 // When the 64 x 64 tile fills the chip (at least one workgroup per CU), a

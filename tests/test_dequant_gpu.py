@@ -136,7 +136,7 @@ CFG_SHAPES = [(520, 600, 520), (300, 260, 1030)]
 
 @pytest.mark.parametrize("out", OUTS)
 @pytest.mark.parametrize("prec", INT_PRECS)
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6, 7, 8, 9])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
 @pytest.mark.parametrize("shape", CFG_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in CFG_SHAPES])
 def test_every_config(pd, dev, prec, out, cfg, shape):
     if cfg >= pd.num_configs():

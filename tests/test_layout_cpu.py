@@ -310,7 +310,7 @@ def test_rowmajor_b_line_layout(prec, cfg):
 # tiles, every other tile whole 128-byte lines.
 TILES = [(256, 256, 1, True), (128, 128, 1, True), (64, 64, 1, True), (32, 32, 4, False),
          (256, 128, 1, True), (128, 64, 1, True), (64, 32, 4, True), (128, 128, 1, True),
-         (256, 256, 1, True), (64, 64, 4, True)]
+         (256, 256, 1, True), (64, 64, 4, True), (256, 256, 1, True)]
 MAX_ROW_BYTES = 1 << 22
 
 

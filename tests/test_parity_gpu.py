@@ -106,7 +106,7 @@ CFG_SHAPES = [(520, 600, 520), (300, 260, 1030), (64, 700, 130)]
 
 
 @pytest.mark.parametrize("prec", PRECS)
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6, 7, 8, 9])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
 @pytest.mark.parametrize("shape", CFG_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in CFG_SHAPES])
 def test_every_config(pd, dev, prec, cfg, shape):
     if cfg >= pd.num_configs():
