@@ -1490,19 +1490,32 @@ gemm_f6_kernel(F6Args args) {
 // way and keeps the 32 x 32 form, and so do the other tiles and layouts.
 //
 // The stage geometry is that of the whole-line kernel (two stages of 128
-// bytes of K per row, 256 rows of A then 256 of B, chunk c of row r at
-// position c ^ swizzle8(r), each DMA instruction writing 8 whole rows).  The
+// bytes of K per row, 256 rows of A then 256 of B, each DMA instruction
+// writing 8 whole rows), with chunk c of row r at position c ^ swizzle16(r).  The
 // MFMA takes, per lane, 8 f16 values of K: lane l of a 16-row block holds
 // row l % 16 and values 8 (l / 16) .. + 7 of a 32-value k-step, so a k-step
 // is 64 bytes (logical chunks 4 q .. 4 q + 3 of stage k-step q = 0, 1) and
-// the 16 lanes of a quarter-wave read 16 consecutive rows at one logical
-// chunk, the pattern the swizzle keeps free of bank conflicts.  A wave's
+// the lanes of a 16-lane phase of the LDS read 8 consecutive rows at two
+// logical chunks, the pattern swizzle16 keeps free of bank conflicts.  A wave's
 // 128 x 64 block is 8 x 4 MFMA blocks (128 accumulator registers); its A
 // fragments are held in halves of four row blocks, so that the fragments of
 // the next half k-step fit beside the current ones and the accumulators
 // within the 256 registers of two waves per SIMD.  Result of block (i, j),
 // register e of lane l: row 16 i + 4 (l / 16) + e, column 16 j + l % 16.
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+// LDS position of logical chunk c of 128-byte stage row r in this kernel:
+// c ^ swizzle16(r).  ds_read_b128 serves a wave in four phases of 16 lanes,
+// lanes 8p .. 8p+7 with lanes 32+8p .. 32+8p+7 (the rocprofv3 bank-conflict
+// counter reads 4 extra cycles per read of this kernel with swizzle8 and none
+// for the 32 x 32 reads, as that grouping predicts).  Here a phase reads 8
+// consecutive rows at logical chunk c and the same rows at c ^ 2; a 128-byte
+// row r at position p covers the 16-byte bank group 8 (r % 2) + p of 16, so
+// the phase is conflict-free iff, among its rows of each parity,
+// swizzle16(r) differs outside bit 1.  Bits: 0 = r0 ^ r1, 1 = r3, 2 = r2;
+// every 16 consecutive rows of one parity also take 8 distinct values, so a
+// read of 16 rows at one chunk is conflict-free too.
+__device__ __forceinline__ int swizzle16(int r) { return ((r ^ (r >> 1)) & 1) | ((r >> 2) & 2) | (r & 4); }
 
 __device__ __forceinline__ floatx4_t mfma16_f16(const uint4 &a, const uint4 &b, const floatx4_t &c) {
     half8_t av, bv;
@@ -1546,12 +1559,12 @@ __global__ __launch_bounds__(512) void gemm_f16_mf16_kernel(Args args) {
     const uint8_t *const b_base = args.B + (int64_t)n0 * args.ldb_bytes;
     const int b_end = (int)((min(BN, N - n0) - 1) * args.ldb_bytes) + valid16;
     // DMA instruction j of this wave fills stage rows (j*NW + wave)*8 .. +7;
-    // lane l fetches logical chunk (l%8) ^ swizzle8(row) of row l/8
+    // lane l fetches logical chunk (l%8) ^ swizzle16(row) of row l/8
     uint32_t voffl[kDmaL];
 #pragma unroll
     for (int j = 0; j < kDmaL; ++j) {
         const int cr = (j * NW + wave) * 8 + (lane >> 3);
-        const int lchunk = (lane & 7) ^ swizzle8(cr);
+        const int lchunk = (lane & 7) ^ swizzle16(cr);
         if (j < kDmaLA)
             voffl[j] = (uint32_t)((min(m0 + cr, M - 1) - m0) * args.lda_bytes) + lchunk * 16;
         else
@@ -1577,12 +1590,12 @@ __global__ __launch_bounds__(512) void gemm_f16_mf16_kernel(Args args) {
     // fragment rows start at multiples of 16, so the swizzle of row frow applies
     // A fragments of k-step q for row blocks hi*FH .. hi*FH + FH-1
     auto read_a = [&](const LStage &buf, int q, int hi, uint4 (&fa)[FH]) __attribute__((always_inline)) {
-        const int ch = (4 * q + fq) ^ swizzle8(frow);
+        const int ch = (4 * q + fq) ^ swizzle16(frow);
 #pragma unroll
         for (int i = 0; i < FH; ++i) fa[i] = buf[wm0 + (hi * FH + i) * 16 + frow][ch];
     };
     auto read_b = [&](const LStage &buf, int q, uint4 (&fb)[FN]) __attribute__((always_inline)) {
-        const int ch = (4 * q + fq) ^ swizzle8(frow);
+        const int ch = (4 * q + fq) ^ swizzle16(frow);
 #pragma unroll
         for (int j = 0; j < FN; ++j) fb[j] = buf[BM + wn0 + j * 16 + frow][ch];
     };

@@ -52,6 +52,39 @@ def test_line_fragment_reads_are_bank_conflict_free():
                 assert len({c ^ swizzle8(r) for r in rows[o:o + 8]}) == 8
 
 
+def swizzle16(r: int) -> int:
+    # rows of 128 bytes in the FP16 16 x 16 MFMA tile: logical chunk c of row r sits at c ^ swizzle16(r)
+    return ((r ^ (r >> 1)) & 1) | ((r >> 2) & 2) | (r & 4)
+
+
+# ds_read_b128 serves a wave in four phases of 16 lanes: lanes 8p .. 8p+7 with 32+8p .. 32+8p+7
+# (the grouping under which rocprofv3's SQ_LDS_BANK_CONFLICT reads 4 extra cycles per read for the
+# 16 x 16 reads on swizzle8, and none for the 32 x 32 reads on swizzle8, as measured)
+READ_PHASES = [list(range(8 * p, 8 * p + 8)) + list(range(32 + 8 * p, 40 + 8 * p)) for p in range(4)]
+
+
+def extra_cycles(rowchunk, swz, phases=READ_PHASES):
+    """Conflict cycles of one ds_read_b128 with 128-byte rows: lane l reads logical chunk c of
+    row r (rowchunk(l) = (r, c)); row r at position p covers 16-byte bank group 8 (r % 2) + p."""
+    extra = 0
+    for ph in phases:
+        groups = {}
+        for lane in ph:
+            r, c = rowchunk(lane)
+            g = 8 * (r % 2) + (c ^ swz(r))
+            groups[g] = groups.get(g, 0) + 1
+        extra += max(groups.values()) - 1
+    return extra
+
+
+def test_read_phase_model_matches_the_counters():
+    for base in range(0, 512, 32):
+        for q in range(4):   # the 32 x 32 reads of the whole-line tiles: no conflicts
+            assert extra_cycles(lambda l: (base + l % 32, 2 * q + l // 32), swizzle8) == 0
+    for q in (0, 1):         # the 16 x 16 reads on swizzle8: 4 extra cycles, as counted
+        assert extra_cycles(lambda l: (l % 16, 4 * q + l // 16), swizzle8) == 4
+
+
 def test_mf16_fragment_reads():
     # The FP16 256 x 256 tile on 16 x 16 MFMAs: in k-step q (0, 1) of a 128-byte stage row,
     # lane l of a 16-row block reads row l%16 at logical chunk 4q + l//16, i.e. f16 values
@@ -59,18 +92,19 @@ def test_mf16_fragment_reads():
     for base in range(0, 512, 16):
         covered = {}
         for q in (0, 1):
-            for quarter in range(4):
-                lanes = range(16 * quarter, 16 * quarter + 16)
-                rows = [base + (l % 16) for l in lanes]
-                chunks = [4 * q + l // 16 for l in lanes]
-                pos = [c ^ swizzle8(r) for r, c in zip(rows, chunks)]
-                # 64 banks: the 16 lanes of a quarter-wave cover distinct 16-byte bank groups
-                assert len({32 * (r % 2) + 4 * p for r, p in zip(rows, pos)}) == 16
-                for l, r, c in zip(lanes, rows, chunks):
-                    assert c * 8 == 32 * q + 8 * (l // 16)   # first f16 value of K in the lane
-                    covered[(r, c)] = covered.get((r, c), 0) + 1
+            rc = lambda l: (base + l % 16, 4 * q + l // 16)
+            assert extra_cycles(rc, swizzle16) == 0
+            # also conflict-free if the phases were plain quarter-waves
+            assert extra_cycles(rc, swizzle16, [list(range(16 * p, 16 * p + 16)) for p in range(4)]) == 0
+            for lane in range(64):
+                r, c = rc(lane)
+                assert c * 8 == 32 * q + 8 * (lane // 16)   # first f16 value of K in the lane
+                covered[(r, c)] = covered.get((r, c), 0) + 1
         # the two k-steps read every 16-byte chunk of the 16 rows exactly once
         assert covered == {(base + i, c): 1 for i in range(16) for c in range(8)}
+    # the swizzle permutes the chunks of every row (DMA writes and reads agree)
+    for r in range(512):
+        assert sorted(c ^ swizzle16(r) for c in range(8)) == list(range(8))
 
 
 def test_mf16_result_layout_covers_the_wave_tile():
