@@ -40,8 +40,8 @@
  * worst-case bound of K fp32 additions, K * 2^-24, stays below 1e-3).
  * Each FP16 sum runs in a fixed order, so a call gives the same bits every
  * time for a given shape and tile configuration.  The configurations without
- * a K split share one order and give the same bits as each other (the FP16
- * 256 x 256 tile with column-major B runs 16 x 16 MFMAs, whose sums were
+ * a K split share one order and give the same bits as each other (the
+ * 256 x 256 tile with column-major B runs 16 x 16 MFMAs, whose FP16 sums were
  * measured to round as those of the 32 x 32 ones, bit for bit); the K-split
  * configurations group K differently.  Where K is split across workgroups
  * (pdgemm_pick_splits below), FP16 takes two ranges whose binary32 partial

@@ -18,9 +18,9 @@
 //    take, per lane, 16 contiguous bytes of K of one row of A and of one
 //    column of B, so FP16, INT8 and packed INT4 share one LDS geometry: a K
 //    tile is 64 bytes of K per row of A (32 f16, 64 int8, 128 int4 values).
-//    The largest FP16 tile with column-major B runs v_mfma_f32_16x16x32_f16
-//    instead (same per-lane 16 bytes, fewer register accesses per MAC: see
-//    gemm_f16_mf16_kernel).
+//    The largest FP16 and INT8 tile with column-major B runs
+//    v_mfma_f32_16x16x32_f16 and v_mfma_i32_16x16x64_i8 instead (the same 16
+//    bytes per lane, fewer register accesses per MAC: see gemm_mf16_kernel).
 //  * INT4: gfx950 has no signed 4-bit MFMA (the paper's m16n8k64.s4 path,
 //    Listing 2, has no equivalent here).  INT4 stays packed in LDS; after a
 //    fragment read each packed dword w is split in registers into two int8
@@ -1476,27 +1476,28 @@ gemm_f6_kernel(F6Args args) {
 }
 
 // ---------------------------------------------------------------------------
-// The 256 x 256 FP16 tile on 16 x 16 MFMAs
+// The 256 x 256 FP16 and INT8 tile on 16 x 16 MFMAs
 //
-// At the large FP16 shapes the board runs at its power limit, so a GEMM's
-// time follows its energy.  v_mfma_f32_32x32x16_f16 reads 8 operand
-// registers and reads and writes 16 accumulator registers per 16384 MACs;
-// v_mfma_f32_16x16x32_f16 reads 8 operand registers and reads and writes 4
-// accumulator registers per 8192 MACs, a fifth fewer register accesses per
-// MAC for the same LDS traffic and the same number of MFMA cycles.  Measured
-// on configuration 0 (256 x 256, 8 waves of 128 x 64, two whole-line stages)
-// with column-major B: FP16 8192^3 800 against 847 us back to back (4096^3
-// 115 against 117, with bit-identical results); INT8 moved by about 1% either
-// way and keeps the 32 x 32 form, and so do the other tiles and layouts.
+// At the large shapes the board runs at its power limit, so a GEMM's time
+// follows its energy.  v_mfma_f32_32x32x16_f16 (v_mfma_i32_32x32x32_i8) reads
+// 8 operand registers and reads and writes 16 accumulator registers per 16384
+// MACs; v_mfma_f32_16x16x32_f16 (v_mfma_i32_16x16x64_i8) reads 8 operand
+// registers and reads and writes 4 accumulator registers per 8192 MACs, a
+// fifth fewer register accesses per MAC for the same LDS traffic and the
+// same number of MFMA cycles.  Configuration 0 (256 x 256, 8 waves of
+// 128 x 64, two whole-line stages) with column-major B runs this kernel;
+// configuration 10 keeps the 32 x 32 form for comparison.  FP16 results are
+// bit-identical to those of the 32 x 32 form.  The other tiles, row-major B,
+// the dequantizing epilogues and INT4 keep the 32 x 32 form.
 //
 // The stage geometry is that of the whole-line kernel (two stages of 128
 // bytes of K per row, 256 rows of A then 256 of B, each DMA instruction
-// writing 8 whole rows), with chunk c of row r at position c ^ swizzle16(r).  The
-// MFMA takes, per lane, 8 f16 values of K: lane l of a 16-row block holds
-// row l % 16 and values 8 (l / 16) .. + 7 of a 32-value k-step, so a k-step
-// is 64 bytes (logical chunks 4 q .. 4 q + 3 of stage k-step q = 0, 1) and
-// the lanes of a 16-lane phase of the LDS read 8 consecutive rows at two
-// logical chunks, the pattern swizzle16 keeps free of bank conflicts.  A wave's
+// writing 8 whole rows), with chunk c of row r at position c ^ swizzle16(r).
+// The MFMA takes 16 bytes of K per lane: lane l of a 16-row block holds row
+// l % 16 and bytes 16 (l / 16) .. + 15 of a 64-byte k-step (8 f16 or 16 int8
+// values; logical chunks 4 q .. 4 q + 3 of stage k-step q = 0, 1), and the
+// lanes of a 16-lane phase of the LDS read 8 consecutive rows at two logical
+// chunks, the pattern swizzle16 keeps free of bank conflicts.  A wave's
 // 128 x 64 block is 8 x 4 MFMA blocks (128 accumulator registers); its A
 // fragments are held in halves of four row blocks, so that the fragments of
 // the next half k-step fit beside the current ones and the accumulators
@@ -1524,7 +1525,15 @@ __device__ __forceinline__ floatx4_t mfma16_f16(const uint4 &a, const uint4 &b, 
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(512) void gemm_f16_mf16_kernel(Args args) {
+__device__ __forceinline__ intx4_t mfma16_i8(const uint4 &a, const uint4 &b, const intx4_t &c) {
+    intx4_t av, bv;
+    __builtin_memcpy(&av, &a, 16);
+    __builtin_memcpy(&bv, &b, 16);
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, c, 0, 0, 0);
+}
+
+template <int P>
+__global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int BM = 256, BN = 256, WM = 128, WN = 64, GM = 4;
     constexpr int NW = (BM / WM) * (BN / WN);   // 8 waves
@@ -1551,7 +1560,8 @@ __global__ __launch_bounds__(512) void gemm_f16_mf16_kernel(Args args) {
     // operand rows past M (N) are clamped to the last valid one; the buffer
     // range of a stage ends at the last 16-byte chunk of the last valid row
     // that holds data, and is zero for a stage past K (as in gemm_kernel)
-    const int valid = 2 * K;                        // data bytes per row
+    static_assert(P == kF16 || P == kI8, "FP16 or INT8");
+    const int valid = P == kF16 ? 2 * K : K;        // data bytes per row
     const int valid16 = (valid + 15) & ~15;
     const int n_st = (valid + kStageK - 1) / kStageK;
     const uint8_t *const a_base = args.A + (int64_t)m0 * args.lda_bytes;
@@ -1617,7 +1627,8 @@ __global__ __launch_bounds__(512) void gemm_f16_mf16_kernel(Args args) {
         }
     };
 
-    floatx4_t acc[FM][FN];
+    using Acc4 = typename std::conditional<P == kF16, floatx4_t, intx4_t>::type;
+    Acc4 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -1628,7 +1639,12 @@ __global__ __launch_bounds__(512) void gemm_f16_mf16_kernel(Args args) {
 #pragma unroll
         for (int i = 0; i < FH; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) acc[hi * FH + i][j] = mfma16_f16(fa[i], fb[j], acc[hi * FH + i][j]);
+            for (int j = 0; j < FN; ++j) {
+                if constexpr (P == kF16)
+                    acc[hi * FH + i][j] = mfma16_f16(fa[i], fb[j], acc[hi * FH + i][j]);
+                else
+                    acc[hi * FH + i][j] = mfma16_i8(fa[i], fb[j], acc[hi * FH + i][j]);
+            }
     };
     // issue order of a half k-step: its MFMAs with the next fragment reads
     // (and, after the stage barrier, the DMA of a later stage) slotted one by
@@ -1712,24 +1728,40 @@ __global__ __launch_bounds__(512) void gemm_f16_mf16_kernel(Args args) {
     }
 
     // ---- epilogue: 16 x 16 MFMA result layout -> row-major C, non-temporal ----
+    // In block (i, j) lane l holds column l % 16 of rows 4 (l / 16) + e, so a
+    // store straight from it writes 64-byte pieces of lines.  v_permlane16_swap
+    // exchanges the odd 16-lane rows of block 2h's register e with the even
+    // 16-lane rows of block 2h+1's; then lanes 0-31 of the first hold columns
+    // 32h .. 32h+31 of row e and lanes 32-63 those of row 8 + e, the second
+    // rows 4 + e and 12 + e: every store writes two whole 128-byte pieces.
+    const int half = lane >> 5;
+    const int hcol = lane & 31;
     char *const wave_c = reinterpret_cast<char *>(args.C) + ((int64_t)(m0 + wm0) * args.ldc + n0 + wn0) * 4;
     const int64_t row_bytes = args.ldc * 4;
-    const uint32_t lane_off = (uint32_t)(4 * fq * row_bytes) + frow * 4u;
+    const uint32_t lane_off = (uint32_t)(8 * half * row_bytes) + hcol * 4u;
     const bool interior = m0 + BM <= M && n0 + BN <= N;
-    const int rows_left = M - (m0 + wm0) - 4 * fq;   // rows this lane may write: r < rows_left
-    const int cols_left = N - (n0 + wn0) - frow;     // columns: 16 j < cols_left
+    const int rows_left = M - (m0 + wm0) - 8 * half;   // rows this lane may write: r < rows_left
+    const int cols_left = N - (n0 + wn0) - hcol;       // columns: 32 h < cols_left
     auto store_all = [&](auto &&keep) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = i * 16 + e;   // wave-uniform part of the row
-                char *const row_c = wave_c + r * row_bytes;
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    if (keep(r, j))
-                        __builtin_nontemporal_store(acc[i][j][e],
-                                                    reinterpret_cast<float *>(row_c + lane_off + j * 64));
+                for (int h = 0; h < FN / 2; ++h) {
+                    // (the elements are copied out first: a bit cast of a
+                    // vector element in place reads element 0 with this compiler)
+                    const auto lo = acc[i][2 * h][e], hi = acc[i][2 * h + 1][e];
+                    const auto xy = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, lo),
+                                                                     __builtin_bit_cast(uint32_t, hi), false, false);
+                    if (keep(r, h))
+                        __builtin_nontemporal_store((uint32_t)xy[0], reinterpret_cast<uint32_t *>(
+                                                                         wave_c + r * row_bytes + lane_off + h * 128));
+                    if (keep(r + 4, h))
+                        __builtin_nontemporal_store((uint32_t)xy[1], reinterpret_cast<uint32_t *>(
+                                                                         wave_c + (r + 4) * row_bytes + lane_off + h * 128));
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1737,7 +1769,7 @@ __global__ __launch_bounds__(512) void gemm_f16_mf16_kernel(Args args) {
     if (interior)
         store_all([](int, int) { return true; });
     else
-        store_all([&](int r, int j) { return r < rows_left && j * 16 < cols_left; });
+        store_all([&](int r, int h) { return r < rows_left && h * 32 < cols_left; });
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -1759,7 +1791,7 @@ struct Config {
 };
 
 constexpr Config kConfigs[] = {
-    {256, 256, 128, 64, 4, 1, 2},   // 0: large shapes (8 waves; FP16 with column-major B on 16 x 16 MFMAs)
+    {256, 256, 128, 64, 4, 1, 2},   // 0: large shapes (8 waves; FP16, INT8 with column-major B on 16 x 16 MFMAs)
     {128, 128, 64, 64, 8, 1, 2},    // 1: medium
     {64, 64, 32, 32, 8, 1, 3},      // 2: small
     {32, 32, 32, 32, 8, 4, 0},      // 3: few tiles (small M or N): K split over 4 waves
@@ -1769,7 +1801,7 @@ constexpr Config kConfigs[] = {
     {128, 128, 64, 64, 8, 1, 3},    // 7: 1 with three stages, for at most one round of tiles
     {256, 256, 128, 128, 4, 1, 2},  // 8: 0 with 4 waves of 128 x 128 (never picked: kept to compare)
     {64, 64, 64, 64, 8, 4, 2},      // 9: 2 with K split over 4 waves, for one round of tiles and long K
-    {256, 256, 128, 64, 4, 1, 2},   // 10: 0 on 32 x 32 MFMAs for FP16 too (never picked: kept to compare)
+    {256, 256, 128, 64, 4, 1, 2},   // 10: 0 on 32 x 32 MFMAs for FP16 and INT8 too (never picked: kept to compare)
 };
 
 // Tiles without K split, largest first: the order in which pick() tries them.
@@ -1786,9 +1818,9 @@ template <int P, int E, int BR>
 const void *kernel_ptr(int cfg) {
     switch (cfg) {
     case 0:
-        // FP16 with column-major B: the same tile on 16 x 16 MFMAs
-        if constexpr (P == kF16 && E == kRaw && BR == kBCol)
-            return reinterpret_cast<const void *>(&gemm_f16_mf16_kernel);
+        // FP16 and INT8 with column-major B: the same tile on 16 x 16 MFMAs
+        if constexpr ((P == kF16 || P == kI8) && E == kRaw && BR == kBCol)
+            return reinterpret_cast<const void *>(&gemm_mf16_kernel<P>);
         else
             return kernel_for<P, 0, E, BR>();
     case 1: return kernel_for<P, 1, E, BR>();
@@ -1849,7 +1881,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // one of them whole rounds of workgroups (M = K = 8192, N = 6144); only the
 // ratios within a row matter.  0 = not a candidate (the K-split tiles, 7,
 // which stands in for 1, 9, which stands in for 2, 8, the 4-wave form of 0,
-// slower than 0 at N = 8192, and 10, 0 on 32 x 32 MFMAs for FP16).
+// slower than 0 at N = 8192, and 10, 0 on 32 x 32 MFMAs).
 constexpr int kTileRate[3][kNumConfigs] = {
     {1267, 1019, 703, 0, 1126, 778, 0, 0, 0, 0, 0},    // FP16
     {2449, 2060, 1329, 0, 2171, 1616, 0, 0, 0, 0, 0},  // INT8

@@ -52,7 +52,8 @@ def test_telemetry_is_absent_without_a_gpu():
 def test_roofline_names_the_kernel_that_runs():
     # the library's host-side tile choice needs no GPU
     import precision_dense_gemm_amd as pd
-    assert bench.kernel_name(pd, "f16", 8192) == "gemm_f16_mf16_kernel"
-    assert bench.kernel_name(pd, "i8", 8192) == "gemm_kernel"
+    assert bench.kernel_name(pd, "f16", 8192) == "gemm_mf16_kernel"
+    assert bench.kernel_name(pd, "i8", 8192) == "gemm_mf16_kernel"
+    assert bench.kernel_name(pd, "i4", 8192) == "gemm_kernel"    # without a workspace: nibble planes
     assert bench.kernel_name(pd, "i4", 8192, "fp6") == "gemm_f6_kernel"
     assert bench.kernel_name(pd, "f16", 512) == "gemm_kernel"   # a smaller tile, 32 x 32 MFMAs

@@ -107,17 +107,30 @@ def test_mf16_fragment_reads():
         assert sorted(c ^ swizzle16(r) for c in range(8)) == list(range(8))
 
 
+def permlane16_swap(x, y):
+    # v_permlane16_swap_b32 x, y: the odd 16-lane rows of x trade places with the even ones of y
+    rows = lambda v: [v[16 * k:16 * k + 16] for k in range(4)]
+    xr, yr = rows(x), rows(y)
+    return xr[0] + yr[0] + xr[2] + yr[2], xr[1] + yr[1] + xr[3] + yr[3]
+
+
 def test_mf16_result_layout_covers_the_wave_tile():
-    # register e of lane l in block (i, j): row 16i + 4(l//16) + e, column 16j + l%16,
-    # over the 8 x 4 blocks of a 128 x 64 wave tile: each element once
-    seen = set()
+    # register e of lane l in block (i, j): row 16i + 4(l//16) + e, column 16j + l%16; the
+    # epilogue swaps blocks 2h and 2h+1 and stores the first result at row 16i + e + 8(l//32),
+    # the second 4 rows below, column 32h + l%32: each element of the 128 x 64 wave tile once,
+    # each store two whole 128-byte rows
+    stored = {}
     for i in range(8):
-        for j in range(4):
-            for l in range(64):
-                for e in range(4):
-                    seen.add((16 * i + 4 * (l // 16) + e, 16 * j + l % 16))
-    assert seen == {(r, c) for r in range(128) for c in range(64)}
-    assert 8 * 4 * 64 * 4 == 128 * 64
+        for e in range(4):
+            for h in range(2):
+                held = [[(16 * i + 4 * (l // 16) + e, 16 * j + l % 16) for l in range(64)] for j in (2 * h, 2 * h + 1)]
+                x, y = permlane16_swap(held[0], held[1])
+                for k, reg in enumerate((x, y)):
+                    for l in range(64):
+                        want = (16 * i + e + 4 * k + 8 * (l // 32), 32 * h + l % 32)
+                        assert reg[l] == want
+                        stored[want] = stored.get(want, 0) + 1
+    assert stored == {(r, c): 1 for r in range(128) for c in range(64)}
 
 
 @pytest.mark.parametrize("bm,bn,waves", [(256, 256, 8), (128, 128, 4), (64, 64, 4), (256, 128, 8), (128, 64, 4),
