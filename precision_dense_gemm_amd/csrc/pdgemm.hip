@@ -1532,7 +1532,7 @@ __device__ __forceinline__ intx4_t mfma16_i8(const uint4 &a, const uint4 &b, con
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, c, 0, 0, 0);
 }
 
-template <int P>
+template <int P, int E>
 __global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int BM = 256, BN = 256, WM = 128, WN = 64, GM = 4;
@@ -1561,6 +1561,18 @@ __global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
     // range of a stage ends at the last 16-byte chunk of the last valid row
     // that holds data, and is zero for a stage past K (as in gemm_kernel)
     static_assert(P == kF16 || P == kI8, "FP16 or INT8");
+    static_assert(E == kRaw || (P == kI8 && is_dequant(E)), "plain, or INT8 dequantized");
+    constexpr bool kDeq = is_dequant(E);
+    // Dequantizing epilogue: the block's 256 row and 256 column scales, one
+    // per thread, loaded now, written to LDS after the first DMAs and
+    // published by the first barrier (rows and columns past the edge take the
+    // last valid scale; their results are not stored)
+    __shared__ __align__(16) float lds_scale[kDeq ? BM + BN : 1];
+    float scale_v = 0.0f;
+    if constexpr (kDeq) {
+        static_assert(BM + BN == NW * kWave, "one scale per thread");
+        scale_v = tid < BM ? args.scale_a[min(m0 + tid, M - 1)] : args.scale_b[min(n0 + tid - BM, N - 1)];
+    }
     const int valid = P == kF16 ? 2 * K : K;        // data bytes per row
     const int valid16 = (valid + 15) & ~15;
     const int n_st = (valid + kStageK - 1) / kStageK;
@@ -1713,6 +1725,7 @@ __global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
     if (n_st > 0) {
         stage_l(0, ln0);
         stage_l(1, ln1);
+        if constexpr (kDeq) lds_scale[tid] = scale_v;
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaL) : "memory");
         read_a(ln0, 0, 0, fL);
         read_b(ln0, 0, fbA);
@@ -1725,6 +1738,10 @@ __global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
         last_stage((st & 1) ? ln1 : ln0, st);
         // no DMA may still be writing this workgroup's LDS when it exits
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else if constexpr (kDeq) {
+        // K == 0: no main loop, so stage the scales here
+        lds_scale[tid] = scale_v;
+        __syncthreads();
     }
 
     // ---- epilogue: 16 x 16 MFMA result layout -> row-major C, non-temporal ----
@@ -1733,43 +1750,125 @@ __global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
     // exchanges the odd 16-lane rows of block 2h's register e with the even
     // 16-lane rows of block 2h+1's; then lanes 0-31 of the first hold columns
     // 32h .. 32h+31 of row e and lanes 32-63 those of row 8 + e, the second
-    // rows 4 + e and 12 + e: every store writes two whole 128-byte pieces.
+    // rows 4 + e and 12 + e: every 32-bit store writes two whole 128-byte
+    // pieces.  A binary16 C takes one more exchange, v_permlane32_swap of the
+    // h = 0 and h = 1 results (upper 32 lanes of the first with the lower 32 of
+    // the second), after which a register holds columns 0 .. 63 of one row.
+    using Out = typename OutOf<P, E>::type;
+    constexpr int kOut = (int)sizeof(Out);
     const int half = lane >> 5;
     const int hcol = lane & 31;
-    char *const wave_c = reinterpret_cast<char *>(args.C) + ((int64_t)(m0 + wm0) * args.ldc + n0 + wn0) * 4;
-    const int64_t row_bytes = args.ldc * 4;
-    const uint32_t lane_off = (uint32_t)(8 * half * row_bytes) + hcol * 4u;
+    char *const wave_c = reinterpret_cast<char *>(args.C) + ((int64_t)(m0 + wm0) * args.ldc + n0 + wn0) * kOut;
+    const int64_t row_bytes = args.ldc * kOut;
     const bool interior = m0 + BM <= M && n0 + BN <= N;
-    const int rows_left = M - (m0 + wm0) - 8 * half;   // rows this lane may write: r < rows_left
-    const int cols_left = N - (n0 + wn0) - hcol;       // columns: 32 h < cols_left
-    auto store_all = [&](auto &&keep) __attribute__((always_inline)) {
+    // this lane's row scales of block row i: rows 16 i + 8 half + 0..3 (x) and + 4..7 (y);
+    // column scales: columns 32 h + hcol
+    float sb[FN / 2];
+    if constexpr (kDeq) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = i * 16 + e;   // wave-uniform part of the row
-#pragma unroll
-                for (int h = 0; h < FN / 2; ++h) {
-                    // (the elements are copied out first: a bit cast of a
-                    // vector element in place reads element 0 with this compiler)
-                    const auto lo = acc[i][2 * h][e], hi = acc[i][2 * h + 1][e];
-                    const auto xy = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, lo),
-                                                                     __builtin_bit_cast(uint32_t, hi), false, false);
-                    if (keep(r, h))
-                        __builtin_nontemporal_store((uint32_t)xy[0], reinterpret_cast<uint32_t *>(
-                                                                         wave_c + r * row_bytes + lane_off + h * 128));
-                    if (keep(r + 4, h))
-                        __builtin_nontemporal_store((uint32_t)xy[1], reinterpret_cast<uint32_t *>(
-                                                                         wave_c + (r + 4) * row_bytes + lane_off + h * 128));
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int h = 0; h < FN / 2; ++h) sb[h] = lds_scale[BM + wn0 + 32 * h + hcol];
+    }
+    // ((float)sum * scale_a) * scale_b, rounded once per step; a binary16 C
+    // rounds that binary32 value again (the empty asm keeps the backend from
+    // fusing the product and the narrowing into one rounding)
+    auto dequant = [&](uint32_t bits, float sa, float sbv) __attribute__((always_inline)) {
+        float c = (float)(int32_t)bits;
+        c = c * sa;
+        c = c * sbv;
+        if constexpr (E == kDequantF16) asm("" : "+v"(c));
+        return c;
     };
-    if (interior)
-        store_all([](int, int) { return true; });
-    else
-        store_all([&](int r, int h) { return r < rows_left && h * 32 < cols_left; });
+    if constexpr (E != kDequantF16) {
+        const uint32_t lane_off = (uint32_t)(8 * half * row_bytes) + hcol * (uint32_t)kOut;
+        const int rows_left = M - (m0 + wm0) - 8 * half;   // rows this lane may write: r < rows_left
+        const int cols_left = N - (n0 + wn0) - hcol;       // columns: 32 h < cols_left
+        auto store_all = [&](auto &&keep) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                float4 sa0, sa1;
+                if constexpr (kDeq) {
+                    sa0 = *reinterpret_cast<const float4 *>(&lds_scale[wm0 + 16 * i + 8 * half]);
+                    sa1 = *reinterpret_cast<const float4 *>(&lds_scale[wm0 + 16 * i + 8 * half + 4]);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = i * 16 + e;   // wave-uniform part of the row
+#pragma unroll
+                    for (int h = 0; h < FN / 2; ++h) {
+                        // (the elements are copied out first: a bit cast of a
+                        // vector element in place reads element 0 with this compiler)
+                        const auto lo = acc[i][2 * h][e], hi = acc[i][2 * h + 1][e];
+                        const auto xy = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, lo),
+                                                                         __builtin_bit_cast(uint32_t, hi), false, false);
+                        uint32_t v0 = xy[0], v1 = xy[1];
+                        if constexpr (kDeq) {
+                            const float e0 = e == 0 ? sa0.x : e == 1 ? sa0.y : e == 2 ? sa0.z : sa0.w;
+                            const float e1 = e == 0 ? sa1.x : e == 1 ? sa1.y : e == 2 ? sa1.z : sa1.w;
+                            v0 = __builtin_bit_cast(uint32_t, dequant(v0, e0, sb[h]));
+                            v1 = __builtin_bit_cast(uint32_t, dequant(v1, e1, sb[h]));
+                        }
+                        if (keep(r, h))
+                            __builtin_nontemporal_store(v0, reinterpret_cast<uint32_t *>(
+                                                                wave_c + r * row_bytes + lane_off + h * 128));
+                        if (keep(r + 4, h))
+                            __builtin_nontemporal_store(v1, reinterpret_cast<uint32_t *>(
+                                                                wave_c + (r + 4) * row_bytes + lane_off + h * 128));
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        if (interior)
+            store_all([](int, int) { return true; });
+        else
+            store_all([&](int r, int h) { return r < rows_left && h * 32 < cols_left; });
+    } else {
+        static_assert(FN == 4, "two column halves per store");
+        // after both exchanges lane l holds column l of a row: 128 bytes per store
+        const uint32_t lane_off = (uint32_t)(lane * kOut);
+        const int rows_left = M - (m0 + wm0);
+        const int cols_left = N - (n0 + wn0) - lane;
+        auto store_all = [&](auto &&keep) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const float4 sa0 = *reinterpret_cast<const float4 *>(&lds_scale[wm0 + 16 * i + 8 * half]);
+                const float4 sa1 = *reinterpret_cast<const float4 *>(&lds_scale[wm0 + 16 * i + 8 * half + 4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = i * 16 + e;
+                    const float e0 = e == 0 ? sa0.x : e == 1 ? sa0.y : e == 2 ? sa0.z : sa0.w;
+                    const float e1 = e == 0 ? sa1.x : e == 1 ? sa1.y : e == 2 ? sa1.z : sa1.w;
+                    uint32_t hv[2][2];   // [rows r (+8) | rows r + 4 (+8)][h]: binary16 bits in the low half
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const auto lo = acc[i][2 * h][e], hi = acc[i][2 * h + 1][e];
+                        const auto xy = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, lo),
+                                                                         __builtin_bit_cast(uint32_t, hi), false, false);
+                        const _Float16 f0 = (_Float16)dequant(xy[0], e0, sb[h]);
+                        const _Float16 f1 = (_Float16)dequant(xy[1], e1, sb[h]);
+                        hv[0][h] = __builtin_bit_cast(uint16_t, f0);
+                        hv[1][h] = __builtin_bit_cast(uint16_t, f1);
+                    }
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        const auto sw = __builtin_amdgcn_permlane32_swap(hv[k][0], hv[k][1], false, false);
+                        const int rr = r + 4 * k;   // sw[0]: row rr, sw[1]: row rr + 8; column = lane
+                        if (keep(rr))
+                            __builtin_nontemporal_store((uint16_t)sw[0], reinterpret_cast<uint16_t *>(
+                                                                             wave_c + rr * row_bytes + lane_off));
+                        if (keep(rr + 8))
+                            __builtin_nontemporal_store((uint16_t)sw[1], reinterpret_cast<uint16_t *>(
+                                                                             wave_c + (rr + 8) * row_bytes + lane_off));
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        if (interior)
+            store_all([](int) { return true; });
+        else
+            store_all([&](int rr) { return rr < rows_left && 0 < cols_left; });
+    }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -1818,9 +1917,10 @@ template <int P, int E, int BR>
 const void *kernel_ptr(int cfg) {
     switch (cfg) {
     case 0:
-        // FP16 and INT8 with column-major B: the same tile on 16 x 16 MFMAs
-        if constexpr ((P == kF16 || P == kI8) && E == kRaw && BR == kBCol)
-            return reinterpret_cast<const void *>(&gemm_mf16_kernel<P>);
+        // FP16 and INT8 with column-major B (INT8 also dequantized): the same
+        // tile on 16 x 16 MFMAs
+        if constexpr ((P == kF16 || P == kI8) && (E == kRaw || (P == kI8 && is_dequant(E))) && BR == kBCol)
+            return reinterpret_cast<const void *>(&gemm_mf16_kernel<P, E>);
         else
             return kernel_for<P, 0, E, BR>();
     case 1: return kernel_for<P, 1, E, BR>();
