@@ -1485,10 +1485,11 @@ gemm_f6_kernel(F6Args args) {
 // registers and reads and writes 4 accumulator registers per 8192 MACs, a
 // fifth fewer register accesses per MAC for the same LDS traffic and the
 // same number of MFMA cycles.  Configuration 0 (256 x 256, 8 waves of
-// 128 x 64, two whole-line stages) with column-major B runs this kernel;
+// 128 x 64, two whole-line stages) runs this kernel for FP16 and INT8 with
+// either B layout and for the INT8 dequantizing epilogues (column-major B);
 // configuration 10 keeps the 32 x 32 form for comparison.  FP16 results are
-// bit-identical to those of the 32 x 32 form.  The other tiles, row-major B,
-// the dequantizing epilogues and INT4 keep the 32 x 32 form.
+// bit-identical to those of the 32 x 32 form.  The other tiles and INT4 keep
+// the 32 x 32 form.
 //
 // The stage geometry is that of the whole-line kernel (two stages of 128
 // bytes of K per row, 256 rows of A then 256 of B, each DMA instruction
@@ -1518,6 +1519,24 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 // read of 16 rows at one chunk is conflict-free too.
 __device__ __forceinline__ int swizzle16(int r) { return ((r ^ (r >> 1)) & 1) | ((r >> 2) & 2) | (r & 4); }
 
+// Row-major B in this kernel: a stage's B part holds its rows of B (64 for
+// FP16, 128 for INT8: the K values of 128 bytes of A) as 256 columns, kCpr
+// 16-byte chunks each (32 for FP16, 16 for INT8, both multiples of the 16
+// bank groups), logical chunk c of B row r at position c ^ bswizzle16(r).  A
+// transposing read gives each 16-lane group g of a k-step the kR rows (FP16
+// 4, INT8 8) starting at row 2 kR g + kR t of its 16 columns (1 chunk of
+// INT8, 2 of FP16), so one read touches 16 (row, chunk) pairs of two groups;
+// they fall in distinct bank groups when the swizzle separates the rows of
+// one read (bits below log2 kR) and the groups g of either pairing, (0, 1)
+// with (2, 3) or (0, 2) with (1, 3) (the bit g0 ^ g1).
+template <int P>
+__device__ __forceinline__ int bswizzle16(int r) {
+    if constexpr (P == kF16)
+        return 2 * ((r & 3) | ((((r >> 3) ^ (r >> 4)) & 1) << 2));
+    else
+        return (r & 7) | ((((r >> 4) ^ (r >> 5)) & 1) << 3);
+}
+
 __device__ __forceinline__ floatx4_t mfma16_f16(const uint4 &a, const uint4 &b, const floatx4_t &c) {
     half8_t av, bv;
     __builtin_memcpy(&av, &a, 16);
@@ -1532,7 +1551,7 @@ __device__ __forceinline__ intx4_t mfma16_i8(const uint4 &a, const uint4 &b, con
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, c, 0, 0, 0);
 }
 
-template <int P, int E>
+template <int P, int E, int BR>
 __global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int BM = 256, BN = 256, WM = 128, WN = 64, GM = 4;
@@ -1561,7 +1580,11 @@ __global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
     // range of a stage ends at the last 16-byte chunk of the last valid row
     // that holds data, and is zero for a stage past K (as in gemm_kernel)
     static_assert(P == kF16 || P == kI8, "FP16 or INT8");
-    static_assert(E == kRaw || (P == kI8 && is_dequant(E)), "plain, or INT8 dequantized");
+    static_assert(E == kRaw || (P == kI8 && is_dequant(E) && BR == kBCol), "plain, or INT8 dequantized");
+    using RB = RowB<P>;
+    constexpr int kEs = P == kF16 ? 2 : 1;                  // bytes per element
+    constexpr int kCpr = BN * kEs / 16;                     // row-major B: chunks per row of B
+    static_assert(BR == kBCol || 2 * RB::kKRows * kCpr == 8 * BN, "row-major B part of a stage");
     constexpr bool kDeq = is_dequant(E);
     // Dequantizing epilogue: the block's 256 row and 256 column scales, one
     // per thread, loaded now, written to LDS after the first DMAs and
@@ -1578,27 +1601,47 @@ __global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
     const int n_st = (valid + kStageK - 1) / kStageK;
     const uint8_t *const a_base = args.A + (int64_t)m0 * args.lda_bytes;
     const int a_end = (int)((min(BM, M - m0) - 1) * args.lda_bytes) + valid16;
-    const uint8_t *const b_base = args.B + (int64_t)n0 * args.ldb_bytes;
-    const int b_end = (int)((min(BN, N - n0) - 1) * args.ldb_bytes) + valid16;
+    // column-major B: like A, BN rows of K.  Row-major B: the tile's columns
+    // start n0 values into every row of B; the range ends at the last chunk
+    // of row K-1 that holds a column below N, so rows past K read as zeros,
+    // and a stage's resource starts at its first row of B (a lane's offset
+    // spans at most 2 kKRows rows: 512 MiB with rows of 4 MiB)
+    const uint8_t *const b_base = args.B + (BR == kBRow ? (int64_t)n0 * kEs : (int64_t)n0 * args.ldb_bytes);
+    const int64_t b_end = BR == kBRow
+                              ? (int64_t)(K - 1) * args.ldb_bytes + (((int64_t)min(BN, N - n0) * kEs + 15) & ~int64_t(15))
+                              : (int64_t)(min(BN, N - n0) - 1) * args.ldb_bytes + valid16;
+    const int64_t b_stage_bytes = BR == kBRow ? (int64_t)2 * RB::kKRows * args.ldb_bytes : kStageK;
     // DMA instruction j of this wave fills stage rows (j*NW + wave)*8 .. +7;
-    // lane l fetches logical chunk (l%8) ^ swizzle16(row) of row l/8
+    // lane l fetches logical chunk (l%8) ^ swizzle16(row) of row l/8.
+    // Row-major B: lane l of a B instruction fills flat chunk f of the B
+    // part: row f / kCpr of B, position f % kCpr
     uint32_t voffl[kDmaL];
 #pragma unroll
     for (int j = 0; j < kDmaL; ++j) {
         const int cr = (j * NW + wave) * 8 + (lane >> 3);
         const int lchunk = (lane & 7) ^ swizzle16(cr);
-        if (j < kDmaLA)
+        if (j < kDmaLA) {
             voffl[j] = (uint32_t)((min(m0 + cr, M - 1) - m0) * args.lda_bytes) + lchunk * 16;
-        else
+        } else if constexpr (BR == kBCol) {
             voffl[j] = (uint32_t)((min(n0 + cr - BM, N - 1) - n0) * args.ldb_bytes) + lchunk * 16;
+        } else {
+            const int f = ((j * NW + wave) - BM / 8) * 64 + lane;
+            const int krow = f / kCpr;
+            const int gchunk = (f % kCpr) ^ bswizzle16<P>(krow);
+            voffl[j] = (uint32_t)(krow * args.ldb_bytes) + gchunk * 16;
+        }
     }
     auto stage_l = [&](int st, LStage &buf) __attribute__((always_inline)) {
         const int kb = st * kStageK;
         const bool live = st < n_st;
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(a_base + kb), (short)0, live ? a_end - kb : 0, kRsrcWord3);
+        const int64_t bt = (int64_t)st * b_stage_bytes;
+        const int b_range = !live ? 0
+                            : BR == kBRow ? (int)max(min(min(b_end - bt, b_stage_bytes), (int64_t)INT32_MAX), (int64_t)0)
+                                          : (int)(b_end - bt);
         const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(b_base + kb), (short)0, live ? b_end - kb : 0, kRsrcWord3);
+            (void *)(b_base + bt), (short)0, b_range, kRsrcWord3);
 #pragma unroll
         for (int j = 0; j < kDmaL; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kDmaLA ? ra : rb, LDS_PTR(&buf[(j * NW + wave) * 8][0]),
@@ -1616,10 +1659,54 @@ __global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
 #pragma unroll
         for (int i = 0; i < FH; ++i) fa[i] = buf[wm0 + (hi * FH + i) * 16 + frow][ch];
     };
-    auto read_b = [&](const LStage &buf, int q, uint4 (&fb)[FN]) __attribute__((always_inline)) {
-        const int ch = (4 * q + fq) ^ swizzle16(frow);
+    // Row-major B: lane i of a 16-lane group points its transposing read at
+    // row i / kQ of the read, bytes 8 (i % kQ) of the group's columns, and
+    // receives the kR values of column i; two reads make the 16 bytes of K the
+    // MFMA takes (group g: values 2 kR g .. 2 kR g + 2 kR - 1 of the k-step)
+    // The swizzle of a lane's rows depends only on the row within a read and
+    // on the group (q and t move the row by multiples of 2 kR that leave
+    // bswizzle16 unchanged), so a lane's byte offset is fixed per column
+    // block and q and t add constants.
+    const int tr_i = lane & 15;
+    const int tr_row = tr_i / RB::kQ;
+    const int tr_byte = 8 * (tr_i % RB::kQ);
+    uint32_t b_off[BR == kBRow ? FN : 1];
+    if constexpr (BR == kBRow) {
+        const int krow0 = fq * (2 * RB::kR) + tr_row;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) fb[j] = buf[BM + wn0 + j * 16 + frow][ch];
+        for (int j = 0; j < FN; ++j) {
+            const int col_bytes = (wn0 + j * 16) * kEs + tr_byte;
+            const int pos = (col_bytes >> 4) ^ bswizzle16<P>(krow0);
+            b_off[j] = (uint32_t)((krow0 * kCpr + pos) * 16 + (col_bytes & 15));
+        }
+    }
+    auto read_b = [&](const LStage &buf, int q, uint4 (&fb)[FN]) __attribute__((always_inline)) {
+        if constexpr (BR == kBCol) {
+            const int ch = (4 * q + fq) ^ swizzle16(frow);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) fb[j] = buf[BM + wn0 + j * 16 + frow][ch];
+        } else {
+            const char *const bpart = reinterpret_cast<const char *>(&buf[BM][0]);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                uint32_t w[4];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const char *const ptr = bpart + b_off[j] + (q * RB::kKRows + t * RB::kR) * kCpr * 16;
+                    if constexpr (P == kF16) {
+                        typedef short v4s __attribute__((ext_vector_type(4)));
+                        const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) v4s *)(ptr));
+                        __builtin_memcpy(&w[2 * t], &v, 8);
+                    } else {
+                        const intx2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                            (__attribute__((address_space(3))) intx2_t *)(ptr));
+                        __builtin_memcpy(&w[2 * t], &v, 8);
+                    }
+                }
+                fb[j] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
     };
     // zero the bytes of this lane's fragments of k-step q of stage st at or beyond K
     auto mask = [&](int st, int q, uint4 *f, int n) __attribute__((always_inline)) {
@@ -1675,7 +1762,7 @@ __global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
     };
     using kNone = std::integral_constant<int, 0>;
     using kHalfA = std::integral_constant<int, FH>;
-    using kHalfAB = std::integral_constant<int, FH + FN>;
+    using kHalfAB = std::integral_constant<int, FH + FN * (BR == kBRow ? 2 : 1)>;
     using kStageDma = std::integral_constant<int, kDmaL>;
 
     // A fragments of the lower (fL) and upper (fU) row blocks; B fragments of
@@ -1917,10 +2004,10 @@ template <int P, int E, int BR>
 const void *kernel_ptr(int cfg) {
     switch (cfg) {
     case 0:
-        // FP16 and INT8 with column-major B (INT8 also dequantized): the same
-        // tile on 16 x 16 MFMAs
-        if constexpr ((P == kF16 || P == kI8) && (E == kRaw || (P == kI8 && is_dequant(E))) && BR == kBCol)
-            return reinterpret_cast<const void *>(&gemm_mf16_kernel<P, E>);
+        // FP16 and INT8, either B layout (INT8 with column-major B also
+        // dequantized): the same tile on 16 x 16 MFMAs
+        if constexpr ((P == kF16 || P == kI8) && (E == kRaw || (P == kI8 && is_dequant(E) && BR == kBCol)))
+            return reinterpret_cast<const void *>(&gemm_mf16_kernel<P, E, BR>);
         else
             return kernel_for<P, 0, E, BR>();
     case 1: return kernel_for<P, 1, E, BR>();

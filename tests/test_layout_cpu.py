@@ -107,6 +107,50 @@ def test_mf16_fragment_reads():
         assert sorted(c ^ swizzle16(r) for c in range(8)) == list(range(8))
 
 
+def bswizzle16(prec: str, r: int) -> int:
+    # row-major B in the 16 x 16 tile: logical chunk c of B row r sits at c ^ bswizzle16(r)
+    if prec == "f16":
+        return 2 * ((r & 3) | ((((r >> 3) ^ (r >> 4)) & 1) << 2))
+    return (r & 7) | ((((r >> 4) ^ (r >> 5)) & 1) << 3)
+
+
+@pytest.mark.parametrize("prec", ["f16", "i8"])
+def test_mf16_rowmajor_b_reads(prec):
+    # transposing reads (ds_read_b64_tr_b16 / _b8): lane i of 16-lane group g addresses row
+    # 2 kR g + kR t + i // kQ of the k-step, bytes 8 (i % kQ) of the group's 16 columns, and
+    # receives kR values of column i; the stage's B part holds rows of kCpr chunks
+    es, kr = (2, 4) if prec == "f16" else (1, 8)
+    kq = 16 // kr
+    kcpr = 256 * es // 16
+    krows = 32 if prec == "f16" else 64          # rows of B per 64-byte k-step
+    for wn0 in (0, 64, 128, 192):
+        for j in range(4):
+            for q in (0, 1):
+                for t in (0, 1):
+                    slots = {}
+                    for lane in range(64):
+                        g, i = lane // 16, lane % 16
+                        row = q * krows + g * 2 * kr + t * kr + i // kq
+                        col_bytes = (wn0 + 16 * j) * es + 8 * (i % kq)
+                        # the lane's swizzle does not depend on q or t (the kernel hoists it)
+                        assert bswizzle16(prec, row) == bswizzle16(prec, g * 2 * kr + i // kq)
+                        pos = (col_bytes >> 4) ^ bswizzle16(prec, row)
+                        assert 0 <= pos < kcpr
+                        slots[lane] = (row * kcpr + pos) * 16 + (col_bytes & 15)
+                        # the DMA put logical chunk (col_bytes >> 4) of this row at that position
+                        assert (pos ^ bswizzle16(prec, row)) == col_bytes >> 4
+                    # 8-byte reads, 256 bytes per cycle: either pairing of 16-lane groups per cycle
+                    # touches 16 distinct 16-byte bank groups with two lanes each
+                    for pairing in (((0, 1), (2, 3)), ((0, 2), (1, 3))):
+                        for pair in pairing:
+                            lanes = [l for l in range(64) if l // 16 in pair]
+                            groups = {}
+                            for l in lanes:
+                                bg = (slots[l] // 16) % 16
+                                groups.setdefault(bg, set()).add(slots[l] // 16)
+                            assert len(groups) == 16 and all(len(v) == 1 for v in groups.values())
+
+
 def permlane16_swap(x, y):
     # v_permlane16_swap_b32 x, y: the odd 16-lane rows of x trade places with the even ones of y
     rows = lambda v: [v[16 * k:16 * k + 16] for k in range(4)]
