@@ -1486,24 +1486,26 @@ gemm_f6_kernel(F6Args args) {
 // fifth fewer register accesses per MAC for the same LDS traffic and the
 // same number of MFMA cycles.  Configuration 0 (256 x 256, 8 waves of
 // 128 x 64, two whole-line stages) runs this kernel for FP16 and INT8 with
-// either B layout and for the INT8 dequantizing epilogues (column-major B);
-// configuration 10 keeps the 32 x 32 form for comparison.  FP16 results are
-// bit-identical to those of the 32 x 32 form.  The other tiles and INT4 keep
-// the 32 x 32 form.
+// either B layout and for the INT8 dequantizing epilogues (column-major B),
+// configuration 4 (256 x 128, 8 waves of 64 x 64, three stages) for the same
+// with column-major B; configuration 10 keeps the 32 x 32 form of 0 for
+// comparison.  FP16 results are bit-identical to those of the 32 x 32 form.
+// The other tiles and INT4 keep the 32 x 32 form.
 //
-// The stage geometry is that of the whole-line kernel (two stages of 128
-// bytes of K per row, 256 rows of A then 256 of B, each DMA instruction
-// writing 8 whole rows), with chunk c of row r at position c ^ swizzle16(r).
-// The MFMA takes 16 bytes of K per lane: lane l of a 16-row block holds row
-// l % 16 and bytes 16 (l / 16) .. + 15 of a 64-byte k-step (8 f16 or 16 int8
-// values; logical chunks 4 q .. 4 q + 3 of stage k-step q = 0, 1), and the
-// lanes of a 16-lane phase of the LDS read 8 consecutive rows at two logical
-// chunks, the pattern swizzle16 keeps free of bank conflicts.  A wave's
-// 128 x 64 block is 8 x 4 MFMA blocks (128 accumulator registers); its A
-// fragments are held in halves of four row blocks, so that the fragments of
-// the next half k-step fit beside the current ones and the accumulators
-// within the 256 registers of two waves per SIMD.  Result of block (i, j),
-// register e of lane l: row 16 i + 4 (l / 16) + e, column 16 j + l % 16.
+// The stage geometry is that of the whole-line kernel: stages of 128 bytes
+// of K per row (two for 256 x 256, three for 256 x 128), BM rows of A then BN
+// of B, each DMA instruction writing 8 whole rows, with chunk c of row r at
+// position c ^ swizzle16(r).  The MFMA takes 16 bytes of K per lane: lane l
+// of a 16-row block holds row l % 16 and bytes 16 (l / 16) .. + 15 of a
+// 64-byte k-step (8 f16 or 16 int8 values; logical chunks 4 q .. 4 q + 3 of
+// stage k-step q = 0, 1), and the lanes of a 16-lane phase of the LDS read 8
+// consecutive rows at two logical chunks, the pattern swizzle16 keeps free
+// of bank conflicts.  A wave's 128 x 64 block is 8 x 4 MFMA blocks (128
+// accumulator registers; a 64 x 64 block 4 x 4, 64); its A fragments are held
+// in halves of its row blocks, so that the fragments of the next half k-step
+// fit beside the current ones and the accumulators within the 256 registers
+// of two waves per SIMD.  Result of block (i, j), register e of lane l: row
+// 16 i + 4 (l / 16) + e, column 16 j + l % 16.
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 // LDS position of logical chunk c of 128-byte stage row r in this kernel:
@@ -1551,10 +1553,10 @@ __device__ __forceinline__ intx4_t mfma16_i8(const uint4 &a, const uint4 &b, con
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, c, 0, 0, 0);
 }
 
-template <int P, int E, int BR>
-__global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
+template <int P, int E, int BR, int BM, int BN, int WM, int WN, int LS>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_mf16_kernel(Args args) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    constexpr int BM = 256, BN = 256, WM = 128, WN = 64, GM = 4;
+    constexpr int GM = 4;
     constexpr int NW = (BM / WM) * (BN / WN);   // 8 waves
     constexpr int kWavesN = BN / WN;
     constexpr int kRows = BM + BN;              // LDS rows per stage
@@ -1563,8 +1565,13 @@ __global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
     constexpr int kStageK = 2 * kRowBytes;      // bytes of K per row per stage
     constexpr int FM = WM / 16, FN = WN / 16;   // MFMA blocks of a wave
     constexpr int FH = FM / 2;                  // A fragments per half k-step
+    static_assert(NW == 8 && BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "8 waves; stage rows split evenly");
+    static_assert(FN == 4 && FM % 2 == 0, "two column pairs per wave for the stores");
+    static_assert(LS == 2 || LS == 3, "two or three stages");
+    static_assert((LS - 1) * kDmaL <= 63, "vmcnt holds at most 63 outstanding loads");
     __shared__ uint4 ln0[kRows][2 * kChunks];
     __shared__ uint4 ln1[kRows][2 * kChunks];
+    __shared__ uint4 ln2[LS > 2 ? kRows : 1][2 * kChunks];
     using LStage = uint4[kRows][2 * kChunks];
 
     const int tid = threadIdx.x;
@@ -1584,7 +1591,7 @@ __global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
     using RB = RowB<P>;
     constexpr int kEs = P == kF16 ? 2 : 1;                  // bytes per element
     constexpr int kCpr = BN * kEs / 16;                     // row-major B: chunks per row of B
-    static_assert(BR == kBCol || 2 * RB::kKRows * kCpr == 8 * BN, "row-major B part of a stage");
+    static_assert(BR == kBCol || (BN == 256 && 2 * RB::kKRows * kCpr == 8 * BN), "row-major B part of a stage");
     constexpr bool kDeq = is_dequant(E);
     // Dequantizing epilogue: the block's 256 row and 256 column scales, one
     // per thread, loaded now, written to LDS after the first DMAs and
@@ -1593,8 +1600,9 @@ __global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
     __shared__ __align__(16) float lds_scale[kDeq ? BM + BN : 1];
     float scale_v = 0.0f;
     if constexpr (kDeq) {
-        static_assert(BM + BN == NW * kWave, "one scale per thread");
-        scale_v = tid < BM ? args.scale_a[min(m0 + tid, M - 1)] : args.scale_b[min(n0 + tid - BM, N - 1)];
+        static_assert(BM + BN <= NW * kWave, "one scale per thread at most");
+        if (tid < BM + BN)
+            scale_v = tid < BM ? args.scale_a[min(m0 + tid, M - 1)] : args.scale_b[min(n0 + tid - BM, N - 1)];
     }
     const int valid = P == kF16 ? 2 * K : K;        // data bytes per row
     const int valid16 = (valid + 15) & ~15;
@@ -1769,7 +1777,7 @@ __global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
     // the even (fbA) and odd (fbB) k-step of a stage
     uint4 fL[FH], fU[FH], fbA[FN], fbB[FN];
     // stage st (not the last) from `cur`, whose k-step 0 lower half is in
-    // fL / fbA; refills `cur` with stage st+2 and reads the first fragments
+    // fL / fbA; refills `cur` with stage st+LS and reads the first fragments
     // of stage st+1 from `nxt`
     auto full_stage = [&](LStage &cur, const LStage &nxt, int st) __attribute__((always_inline)) {
         read_a(cur, 0, 1, fU);
@@ -1782,10 +1790,11 @@ __global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
         read_a(cur, 1, 1, fU);
         mma_half(0, fL, fbB);
         interleave(kHalfA{}, kNone{});
-        // this wave's DMA of stage st+1 has landed and its reads of `cur`
-        // are done; after the barrier the same holds for every wave
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        stage_l(st + 2, cur);
+        // this wave's DMA of stage st+1 has landed (stages st+2 .. st+LS-1
+        // may still be in flight) and its reads of `cur` are done; after the
+        // barrier the same holds for every wave
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((LS - 2) * kDmaL) : "memory");
+        stage_l(st + LS, cur);
         read_a(nxt, 0, 0, fL);
         read_b(nxt, 0, fbA);
         mma_half(1, fU, fbB);
@@ -1812,22 +1821,39 @@ __global__ __launch_bounds__(512) void gemm_mf16_kernel(Args args) {
     if (n_st > 0) {
         stage_l(0, ln0);
         stage_l(1, ln1);
-        if constexpr (kDeq) lds_scale[tid] = scale_v;
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaL) : "memory");
+        if constexpr (LS > 2) stage_l(2, ln2);
+        if constexpr (kDeq)
+            if (tid < BM + BN) lds_scale[tid] = scale_v;
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((LS - 1) * kDmaL) : "memory");
         read_a(ln0, 0, 0, fL);
         read_b(ln0, 0, fbA);
         int st = 0;
-        for (; st + 2 < n_st; st += 2) {
-            full_stage(ln0, ln1, st);
-            full_stage(ln1, ln0, st + 1);
+        if constexpr (LS == 2) {
+            for (; st + 2 < n_st; st += 2) {
+                full_stage(ln0, ln1, st);
+                full_stage(ln1, ln0, st + 1);
+            }
+            if (st + 1 < n_st) full_stage(ln0, ln1, st++);
+            last_stage((st & 1) ? ln1 : ln0, st);
+        } else {
+            for (; st + 3 < n_st; st += 3) {
+                full_stage(ln0, ln1, st);
+                full_stage(ln1, ln2, st + 1);
+                full_stage(ln2, ln0, st + 2);
+            }
+            // 1 to 3 stages remain, the first of them in ln0
+            if (st + 1 < n_st) {
+                full_stage(ln0, ln1, st++);
+                if (st + 1 < n_st) full_stage(ln1, ln2, st++);
+            }
+            const int r = st % 3;
+            last_stage(r == 0 ? ln0 : r == 1 ? ln1 : ln2, st);
         }
-        if (st + 1 < n_st) full_stage(ln0, ln1, st++);
-        last_stage((st & 1) ? ln1 : ln0, st);
         // no DMA may still be writing this workgroup's LDS when it exits
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else if constexpr (kDeq) {
         // K == 0: no main loop, so stage the scales here
-        lds_scale[tid] = scale_v;
+        if (tid < BM + BN) lds_scale[tid] = scale_v;
         __syncthreads();
     }
 
@@ -2000,6 +2026,13 @@ const void *kernel_for() {
     return reinterpret_cast<const void *>(&gemm_kernel<P, c.bm, c.bn, c.wm, c.wn, c.gm, E, BR, c.ks, c.ls>);
 }
 
+template <int P, int C, int E, int BR>
+const void *mf16_for() {
+    constexpr Config c = kConfigs[C];
+    static_assert(c.ks == 1, "no K split inside the workgroup");
+    return reinterpret_cast<const void *>(&gemm_mf16_kernel<P, E, BR, c.bm, c.bn, c.wm, c.wn, c.ls>);
+}
+
 template <int P, int E, int BR>
 const void *kernel_ptr(int cfg) {
     switch (cfg) {
@@ -2007,13 +2040,19 @@ const void *kernel_ptr(int cfg) {
         // FP16 and INT8, either B layout (INT8 with column-major B also
         // dequantized): the same tile on 16 x 16 MFMAs
         if constexpr ((P == kF16 || P == kI8) && (E == kRaw || (P == kI8 && is_dequant(E) && BR == kBCol)))
-            return reinterpret_cast<const void *>(&gemm_mf16_kernel<P, E, BR>);
+            return mf16_for<P, 0, E, BR>();
         else
             return kernel_for<P, 0, E, BR>();
     case 1: return kernel_for<P, 1, E, BR>();
     case 2: return kernel_for<P, 2, E, BR>();
     case 3: return kernel_for<P, 3, E, BR>();
-    case 4: return kernel_for<P, 4, E, BR>();
+    case 4:
+        // 256 x 128 with column-major B: FP16, INT8 and its dequantizing
+        // epilogues on 16 x 16 MFMAs too
+        if constexpr ((P == kF16 || P == kI8) && (E == kRaw || P == kI8) && BR == kBCol)
+            return mf16_for<P, 4, E, BR>();
+        else
+            return kernel_for<P, 4, E, BR>();
     case 5: return kernel_for<P, 5, E, BR>();
     case 6: return kernel_for<P, 6, E, BR>();
     case 7: return kernel_for<P, 7, E, BR>();
