@@ -2103,14 +2103,15 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Steady throughput of each tile without K split, in TFLOP/s (FP16) or TOP/s
 // (INT8, INT4): back-to-back timings (HIP graphs of about 25 ms, medians of
-// three alternated rounds, mean of two GPUs) on a product that gives every
-// one of them whole rounds of workgroups (M = K = 8192, N = 6144); only the
-// ratios within a row matter.  0 = not a candidate (the K-split tiles, 7,
+// three alternated rounds; INT4 the mean of two GPUs, FP16 and INT8 one GPU
+// since 0 and 4 run 16 x 16 MFMAs) on a product that gives every one of them
+// whole rounds of workgroups (M = K = 8192, N = 6144); only the ratios within
+// a row matter.  0 = not a candidate (the K-split tiles, 7,
 // which stands in for 1, 9, which stands in for 2, 8, the 4-wave form of 0,
 // slower than 0 at N = 8192, and 10, 0 on 32 x 32 MFMAs).
 constexpr int kTileRate[3][kNumConfigs] = {
-    {1267, 1019, 703, 0, 1126, 778, 0, 0, 0, 0, 0},    // FP16
-    {2449, 2060, 1329, 0, 2171, 1616, 0, 0, 0, 0, 0},  // INT8
+    {1408, 1025, 707, 0, 1283, 789, 0, 0, 0, 0, 0},    // FP16
+    {2700, 2085, 1330, 0, 2445, 1612, 0, 0, 0, 0, 0},  // INT8
     {2824, 2440, 1863, 0, 2499, 2021, 0, 0, 0, 0, 0},  // INT4
 };
 
@@ -2121,10 +2122,12 @@ constexpr int kTileRate[3][kNumConfigs] = {
 // partial last round costs 0.35 + 0.65 * (its fill) of a full one: the fewer
 // CUs run, the higher their clock and the more L2 and HBM bandwidth each
 // gets.  The cheapest tile wins, the larger one on a tie.  (E.g. 144 tiles of
-// 256 x 256 rather than 576 of 128 x 128 at 3072^3, 384 of 256 x 256 rather
-// than 768 of 256 x 128 at 8192 x 3072 x 8192.)  Fitted to 69 shapes from
-// 1024^3 to 12288 x 4096 x 4096 in three precisions on two GPUs: 0.2-0.3%
-// slower than the fastest tile on average, at most 7.5% (INT4 1536^3).  When
+// 256 x 256 rather than 576 of 128 x 128 at 3072^3; for FP16 and INT8, 768
+// of 256 x 128 rather than 384 of 256 x 256 at 8192 x 3072 x 8192.)  Fitted
+// to 69 shapes from 1024^3 to 12288 x 4096 x 4096 in three precisions, the
+// partial-round rule on two GPUs, the FP16 and INT8 rates again on one after
+// the 16 x 16 MFMA kernels: 0.2-0.3% slower than the fastest tile on
+// average, at most 7.8% (INT4 1536^3).  When
 // even the 64 x 64 tile leaves CUs idle (small M or N), a K-split tile puts
 // 4 waves on each of up to 4 times as many tiles.  128 x 128 with at most
 // one tile per CU takes configuration 7.
