@@ -1487,9 +1487,8 @@ gemm_f6_kernel(F6Args args) {
 // same number of MFMA cycles.  Configuration 0 (256 x 256, 8 waves of
 // 128 x 64, two whole-line stages) runs this kernel for FP16 and INT8 with
 // either B layout and for the INT8 dequantizing epilogues (column-major B),
-// configuration 4 (256 x 128, 8 waves of 64 x 64, three stages) for the same
-// with column-major B; configuration 10 keeps the 32 x 32 form of 0 for
-// comparison.  FP16 results are bit-identical to those of the 32 x 32 form.
+// and so does configuration 4 (256 x 128, 8 waves of 64 x 64, three stages);
+// configuration 10 keeps the 32 x 32 form of 0 for comparison.  FP16 results are bit-identical to those of the 32 x 32 form.
 // The other tiles and INT4 keep the 32 x 32 form.
 //
 // The stage geometry is that of the whole-line kernel: stages of 128 bytes
@@ -1522,21 +1521,26 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int swizzle16(int r) { return ((r ^ (r >> 1)) & 1) | ((r >> 2) & 2) | (r & 4); }
 
 // Row-major B in this kernel: a stage's B part holds its rows of B (64 for
-// FP16, 128 for INT8: the K values of 128 bytes of A) as 256 columns, kCpr
-// 16-byte chunks each (32 for FP16, 16 for INT8, both multiples of the 16
-// bank groups), logical chunk c of B row r at position c ^ bswizzle16(r).  A
-// transposing read gives each 16-lane group g of a k-step the kR rows (FP16
-// 4, INT8 8) starting at row 2 kR g + kR t of its 16 columns (1 chunk of
-// INT8, 2 of FP16), so one read touches 16 (row, chunk) pairs of two groups;
-// they fall in distinct bank groups when the swizzle separates the rows of
-// one read (bits below log2 kR) and the groups g of either pairing, (0, 1)
-// with (2, 3) or (0, 2) with (1, 3) (the bit g0 ^ g1).
-template <int P>
+// FP16, 128 for INT8: the K values of 128 bytes of A) as BN columns, kCpr
+// 16-byte chunks each (FP16 32 or 16, INT8 16 or 8 for BN = 256 or 128),
+// logical chunk c of B row r at position c ^ bswizzle16(r).  A transposing
+// read gives each 16-lane group g of a k-step the kR rows (FP16 4, INT8 8)
+// starting at row 2 kR g + kR t of its 16 columns (1 chunk of INT8, 2 of
+// FP16), so one read touches 16 (row, chunk) pairs of two groups; they fall
+// in distinct bank groups when the swizzle separates the rows of one read
+// and the groups g of either pairing, (0, 1) with (2, 3) or (0, 2) with
+// (1, 3) (the bit g0 ^ g1).  With 16 or 32 chunks a row, position p of row
+// r is bank group p % 16 whatever r; with 8 (INT8, BN = 128) it is
+// 8 (r % 2) + p, so there the parity of the row separates half the pairs
+// and the swizzle needs one bit less.
+template <int P, int BN>
 __device__ __forceinline__ int bswizzle16(int r) {
     if constexpr (P == kF16)
         return 2 * ((r & 3) | ((((r >> 3) ^ (r >> 4)) & 1) << 2));
-    else
+    else if constexpr (BN == 256)
         return (r & 7) | ((((r >> 4) ^ (r >> 5)) & 1) << 3);
+    else
+        return ((r >> 1) & 3) | ((((r >> 4) ^ (r >> 5)) & 1) << 2);
 }
 
 __device__ __forceinline__ floatx4_t mfma16_f16(const uint4 &a, const uint4 &b, const floatx4_t &c) {
@@ -1591,7 +1595,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_mf16_kerne
     using RB = RowB<P>;
     constexpr int kEs = P == kF16 ? 2 : 1;                  // bytes per element
     constexpr int kCpr = BN * kEs / 16;                     // row-major B: chunks per row of B
-    static_assert(BR == kBCol || (BN == 256 && 2 * RB::kKRows * kCpr == 8 * BN), "row-major B part of a stage");
+    static_assert(BR == kBCol || 2 * RB::kKRows * kCpr == 8 * BN, "row-major B part of a stage");
     constexpr bool kDeq = is_dequant(E);
     // Dequantizing epilogue: the block's 256 row and 256 column scales, one
     // per thread, loaded now, written to LDS after the first DMAs and
@@ -1635,7 +1639,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_mf16_kerne
         } else {
             const int f = ((j * NW + wave) - BM / 8) * 64 + lane;
             const int krow = f / kCpr;
-            const int gchunk = (f % kCpr) ^ bswizzle16<P>(krow);
+            const int gchunk = (f % kCpr) ^ bswizzle16<P, BN>(krow);
             voffl[j] = (uint32_t)(krow * args.ldb_bytes) + gchunk * 16;
         }
     }
@@ -1684,7 +1688,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_mf16_kerne
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int col_bytes = (wn0 + j * 16) * kEs + tr_byte;
-            const int pos = (col_bytes >> 4) ^ bswizzle16<P>(krow0);
+            const int pos = (col_bytes >> 4) ^ bswizzle16<P, BN>(krow0);
             b_off[j] = (uint32_t)((krow0 * kCpr + pos) * 16 + (col_bytes & 15));
         }
     }
@@ -1760,12 +1764,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_mf16_kerne
     auto interleave = [&](auto reads_c, auto dma_c) __attribute__((always_inline)) {
         constexpr int reads = decltype(reads_c)::value;
         constexpr int dma = decltype(dma_c)::value;
-        static_assert(reads <= kMfma && dma <= kMfma, "one read and one DMA per MFMA slot at most");
+        constexpr int rper = (reads + kMfma - 1) / kMfma;   // LDS reads per MFMA slot (row-major B
+                                                            // on 64 x 64 waves: two in some)
+        static_assert(dma <= kMfma, "one DMA per MFMA slot at most");
 #pragma unroll
         for (int i = 0; i < kMfma; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // 1 MFMA
-            if (i < reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-            if (i < dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // 1 DMA
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // 1 MFMA
+            if (i * rper < reads) __builtin_amdgcn_sched_group_barrier(0x100, rper, 0);  // LDS reads
+            if (i < dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);              // 1 DMA
         }
     };
     using kNone = std::integral_constant<int, 0>;
@@ -2047,9 +2053,9 @@ const void *kernel_ptr(int cfg) {
     case 2: return kernel_for<P, 2, E, BR>();
     case 3: return kernel_for<P, 3, E, BR>();
     case 4:
-        // 256 x 128 with column-major B: FP16, INT8 and its dequantizing
-        // epilogues on 16 x 16 MFMAs too
-        if constexpr ((P == kF16 || P == kI8) && (E == kRaw || P == kI8) && BR == kBCol)
+        // 256 x 128: FP16 and INT8 with either B layout, INT8 dequantized
+        // (column-major B), on 16 x 16 MFMAs too
+        if constexpr ((P == kF16 || P == kI8) && (E == kRaw || (P == kI8 && BR == kBCol)))
             return mf16_for<P, 4, E, BR>();
         else
             return kernel_for<P, 4, E, BR>();

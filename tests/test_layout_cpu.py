@@ -107,23 +107,27 @@ def test_mf16_fragment_reads():
         assert sorted(c ^ swizzle16(r) for c in range(8)) == list(range(8))
 
 
-def bswizzle16(prec: str, r: int) -> int:
+def bswizzle16(prec: str, bn: int, r: int) -> int:
     # row-major B in the 16 x 16 tile: logical chunk c of B row r sits at c ^ bswizzle16(r)
     if prec == "f16":
         return 2 * ((r & 3) | ((((r >> 3) ^ (r >> 4)) & 1) << 2))
-    return (r & 7) | ((((r >> 4) ^ (r >> 5)) & 1) << 3)
+    if bn == 256:
+        return (r & 7) | ((((r >> 4) ^ (r >> 5)) & 1) << 3)
+    return ((r >> 1) & 3) | ((((r >> 4) ^ (r >> 5)) & 1) << 2)
 
 
 @pytest.mark.parametrize("prec", ["f16", "i8"])
-def test_mf16_rowmajor_b_reads(prec):
+@pytest.mark.parametrize("bn", [256, 128])
+def test_mf16_rowmajor_b_reads(prec, bn):
     # transposing reads (ds_read_b64_tr_b16 / _b8): lane i of 16-lane group g addresses row
     # 2 kR g + kR t + i // kQ of the k-step, bytes 8 (i % kQ) of the group's 16 columns, and
     # receives kR values of column i; the stage's B part holds rows of kCpr chunks
     es, kr = (2, 4) if prec == "f16" else (1, 8)
     kq = 16 // kr
-    kcpr = 256 * es // 16
+    kcpr = bn * es // 16
     krows = 32 if prec == "f16" else 64          # rows of B per 64-byte k-step
-    for wn0 in (0, 64, 128, 192):
+    assert 2 * krows * kcpr == 8 * bn            # the B part of a stage: bn rows of 128 bytes
+    for wn0 in range(0, bn, 64):
         for j in range(4):
             for q in (0, 1):
                 for t in (0, 1):
@@ -133,12 +137,12 @@ def test_mf16_rowmajor_b_reads(prec):
                         row = q * krows + g * 2 * kr + t * kr + i // kq
                         col_bytes = (wn0 + 16 * j) * es + 8 * (i % kq)
                         # the lane's swizzle does not depend on q or t (the kernel hoists it)
-                        assert bswizzle16(prec, row) == bswizzle16(prec, g * 2 * kr + i // kq)
-                        pos = (col_bytes >> 4) ^ bswizzle16(prec, row)
+                        assert bswizzle16(prec, bn, row) == bswizzle16(prec, bn, g * 2 * kr + i // kq)
+                        pos = (col_bytes >> 4) ^ bswizzle16(prec, bn, row)
                         assert 0 <= pos < kcpr
                         slots[lane] = (row * kcpr + pos) * 16 + (col_bytes & 15)
                         # the DMA put logical chunk (col_bytes >> 4) of this row at that position
-                        assert (pos ^ bswizzle16(prec, row)) == col_bytes >> 4
+                        assert (pos ^ bswizzle16(prec, bn, row)) == col_bytes >> 4
                     # 8-byte reads, 256 bytes per cycle: either pairing of 16-lane groups per cycle
                     # touches 16 distinct 16-byte bank groups with two lanes each
                     for pairing in (((0, 1), (2, 3)), ((0, 2), (1, 3))):
