@@ -104,10 +104,12 @@ SPLITS = {"f16": 2, "i8": 3, "i4": 3}
 
 
 @pytest.mark.parametrize("prec", ["f16", "i8", "i4"])
-@pytest.mark.parametrize("cfg,split", [(0, False), (3, False), (9, False), (2, True), (5, True)])
+@pytest.mark.parametrize("cfg,split", [(0, False), (4, False), (10, False), (3, False), (9, False), (2, True),
+                                       (5, True)])
 def test_largest_leading_dimensions(pd, dev, prec, cfg, split):
-    # 256 x 256 tiles (configuration 0), the K-split 32 x 32 and 64 x 64 tiles (3, 9), and
-    # K split across workgroups (2, 5), with rows of A, B and C of 4 MiB; M, N and K ragged
+    # 256 x 256 and 256 x 128 tiles (configurations 0 and 4, FP16 and INT8 on 16 x 16 MFMAs;
+    # 10: 0 on 32 x 32 ones), the K-split 32 x 32 and 64 x 64 tiles (3, 9), and K split
+    # across workgroups (2, 5), with rows of A, B and C of 4 MiB; M, N and K ragged
     M, N, K = 250, 70, 200 if not split else 1000
     splits = SPLITS[prec] if split else None
     ld = LD[prec]
@@ -144,9 +146,11 @@ def test_largest_leading_dimensions(pd, dev, prec, cfg, split):
 
 
 @pytest.mark.parametrize("prec", ["f16", "i8", "i4"])
-@pytest.mark.parametrize("cfg,split", [(0, False), (3, False), (6, False), (9, False), (2, True), (5, True)])
+@pytest.mark.parametrize("cfg,split", [(0, False), (4, False), (10, False), (3, False), (6, False), (9, False),
+                                       (2, True), (5, True)])
 def test_largest_leading_dimension_row_major_b(pd, dev, prec, cfg, split):
-    # B row-major with rows of 4 MiB, on the 256 x 256 tile (0) and on the K-split
+    # B row-major with rows of 4 MiB, on the 256 x 256 and 256 x 128 tiles (0, 4; 10: 0 on
+    # 32 x 32 MFMAs) and on the K-split
     # tiles (3: 32 x 32, 6: 64 x 32, 9: 64 x 64), whose waves each stage their own slice of
     # rows of B; K reaches the last slice of a stage (a 64 x 32 INT4 stage spans
     # 1024 rows of B, 4 GiB at this row size)
