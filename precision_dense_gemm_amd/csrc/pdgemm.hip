@@ -237,10 +237,33 @@ __device__ __forceinline__ int bswizzle(int r) {
 // range of tiles, and tiles are ordered in bands of GM block rows (column by
 // column within a band), so that the workgroups resident on one XCD share A
 // and B panels in its L2.
-template <int GM>
+//
+// With kWindows (the large tiles, GM = 4) and a grid of whole 16 x 16 windows
+// of tiles, the order is by window instead: window w takes block ids 256 w ..
+// 256 w + 255, one round of the 256 CUs at one workgroup each; in it XCD x
+// runs the 4 x 8 tiles at block row x % 4, block column x / 4 (column by
+// column), and the windows are taken row by row in serpentine order.  Each
+// XCD still shares 4 panels of A and 8 of B in its L2, but a round reads 16
+// panels of A and 16 of B from memory instead of all of A's and a quarter of
+// B's, and each window shares one side with the one before, which the MALL
+// still holds when the GEMM starts cold (8192^3 FP16 and INT8 in a sweep of
+// other GEMMs: 2-4% faster; the same back to back).
+template <int GM, bool kWindows = true>
 __device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int &tile_m, int &tile_n) {
     const int nb = gridDim.x;
     const int bid = blockIdx.x;
+    if constexpr (kWindows && GM == 4) {
+        if (((tiles_m | tiles_n) & 15) == 0) {
+            const int x = bid & 7, loc = bid >> 3;
+            const int w = loc >> 5, k = loc & 31;   // window; this XCD's k-th tile in it
+            const int wcols = tiles_n >> 4;
+            const int wm = w / wcols, wi = w - wm * wcols;
+            const int wn = (wm & 1) ? wcols - 1 - wi : wi;
+            tile_m = wm * 16 + (x & 3) * 4 + (k & 3);
+            tile_n = wn * 16 + (x >> 2) * 8 + (k >> 2);
+            return;
+        }
+    }
     const int q = nb >> 3, r = nb & 7;
     const int xcd = bid & 7, loc = bid >> 3;
     const int id = (xcd < r) ? xcd * (q + 1) + loc : r * (q + 1) + (xcd - r) * q + loc;
@@ -1280,8 +1303,10 @@ gemm_f6_kernel(F6Args args) {
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int M = args.M, N = args.N, nkb = args.nkb;
 
+    // band order: the operands are the images the pre-pass has just written,
+    // still in the MALL, and the window order measured 1% slower here
     int tile_m, tile_n;
-    tile_of<GM>(args.tiles_m, args.tiles_n, tile_m, tile_n);
+    tile_of<GM, false>(args.tiles_m, args.tiles_n, tile_m, tile_n);
     const int m0 = tile_m * BM;
     const int n0 = tile_n * BN;
 

@@ -214,6 +214,18 @@ def remap(bid, nb, tiles_m, tiles_n, band):
     return first + inb % rows, inb // rows
 
 
+def tile_order(bid, tiles_m, tiles_n, band, windows=True):
+    """tile_of: 16 x 16 windows of tiles where the large tiles (band 4) fill whole windows, else bands."""
+    if windows and band == 4 and (tiles_m | tiles_n) % 16 == 0:
+        x, loc = bid & 7, bid >> 3
+        w, k = loc >> 5, loc & 31
+        wcols = tiles_n >> 4
+        wm, wi = divmod(w, wcols)
+        wn = wcols - 1 - wi if wm & 1 else wi
+        return wm * 16 + (x & 3) * 4 + (k & 3), wn * 16 + (x >> 2) * 8 + (k >> 2)
+    return remap(bid, tiles_m * tiles_n, tiles_m, tiles_n, band)
+
+
 def test_block_remap_is_a_bijection():
     for tm, tn, band in itertools.product(range(1, 34), range(1, 34), (1, 4, 8)):
         nb = tm * tn
@@ -222,11 +234,41 @@ def test_block_remap_is_a_bijection():
         assert all(0 <= m < tm and 0 <= n < tn for m, n in seen)
 
 
+def test_window_order_is_a_bijection():
+    for tm, tn in itertools.product((16, 32, 48, 64, 80), repeat=2):
+        nb = tm * tn
+        seen = {tile_order(b, tm, tn, 4) for b in range(nb)}
+        assert len(seen) == nb
+        assert all(0 <= m < tm and 0 <= n < tn for m, n in seen)
+    # grids that are not whole windows keep the band order
+    for tm, tn in ((16, 24), (33, 32), (8, 64)):
+        assert [tile_order(b, tm, tn, 4) for b in range(tm * tn)] == \
+            [remap(b, tm * tn, tm, tn, 4) for b in range(tm * tn)]
+
+
 def test_xcd_locality_at_8192():
-    # N = 8192 with 256x256 tiles: the 32 workgroups first resident on XCD 0 cover 4 x 8 tiles
+    # N = 8192 with 256x256 tiles: the 32 workgroups first resident on each XCD cover 4 x 8 tiles,
+    # in both orders
     tiles = 32
-    first = [remap(b, tiles * tiles, tiles, tiles, 4) for b in range(0, 8 * 32, 8)]
-    assert len({m for m, _ in first}) == 4 and len({n for _, n in first}) == 8
+    for windows in (False, True):
+        for x in range(8):
+            first = [tile_order(b, tiles, tiles, 4, windows) for b in range(x, 8 * 32, 8)]
+            assert len({m for m, _ in first}) == 4 and len({n for _, n in first}) == 8
+
+
+def test_window_rounds_at_8192():
+    # each round of 256 workgroups covers one 16 x 16 window: 16 panels of A and 16 of B (the band
+    # order: all 32 of A and 8 of B), and each window shares its rows or columns with the one before
+    tiles = 32
+    rounds = [[tile_order(b, tiles, tiles, 4) for b in range(256 * r, 256 * (r + 1))] for r in range(4)]
+    bands = [[remap(b, tiles * tiles, tiles, tiles, 4) for b in range(256 * r, 256 * (r + 1))] for r in range(4)]
+    for r in range(4):
+        assert len({m for m, _ in rounds[r]}) == 16 and len({n for _, n in rounds[r]}) == 16
+        assert len({m for m, _ in bands[r]}) == 32 and len({n for _, n in bands[r]}) == 8
+    for r in range(1, 4):
+        rows = lambda t: {m for m, _ in t}
+        cols = lambda t: {n for _, n in t}
+        assert rows(rounds[r]) == rows(rounds[r - 1]) or cols(rounds[r]) == cols(rounds[r - 1])
 
 
 # --------------------------------------------------------------------------
