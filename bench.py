@@ -130,7 +130,7 @@ def parse():
 TILE_SWEEP_SHAPES = [(n, n, n) for n in (1024, 1536, 2048, 2560, 3072, 3584, 4096, 5120, 6144, 7168, 8192)] + [
     (8192, 6144, 8192), (4096, 8192, 4096), (12288, 4096, 4096), (2048, 8192, 8192), (1024, 8192, 8192),
     (6144, 4096, 8192), (3072, 8192, 4096), (8192, 3072, 8192), (1536, 4096, 8192), (5120, 3072, 4096),
-    (10240, 2048, 4096), (2560, 6144, 4096)]
+    (10240, 2048, 4096), (2560, 6144, 4096), (256, 8192, 8192), (384, 8192, 8192), (512, 8192, 8192)]
 
 
 def tile_sweep():

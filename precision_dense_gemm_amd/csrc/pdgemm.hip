@@ -18,7 +18,7 @@
 //    take, per lane, 16 contiguous bytes of K of one row of A and of one
 //    column of B, so FP16, INT8 and packed INT4 share one LDS geometry: a K
 //    tile is 64 bytes of K per row of A (32 f16, 64 int8, 128 int4 values).
-//    The largest FP16 and INT8 tile with column-major B runs
+//    The FP16 and INT8 tiles of 128 rows and more without K split run
 //    v_mfma_f32_16x16x32_f16 and v_mfma_i32_16x16x64_i8 instead (the same 16
 //    bytes per lane, fewer register accesses per MAC: see gemm_mf16_kernel).
 //  * INT4: gfx950 has no signed 4-bit MFMA (the paper's m16n8k64.s4 path,
@@ -1512,12 +1512,15 @@ gemm_f6_kernel(F6Args args) {
 // same number of MFMA cycles.  Configuration 0 (256 x 256, 8 waves of
 // 128 x 64, two whole-line stages) runs this kernel for FP16 and INT8 with
 // either B layout and for the INT8 dequantizing epilogues (column-major B),
-// and so does configuration 4 (256 x 128, 8 waves of 64 x 64, three stages);
-// configuration 10 keeps the 32 x 32 form of 0 for comparison.  FP16 results are bit-identical to those of the 32 x 32 form.
-// The other tiles and INT4 keep the 32 x 32 form.
+// and so do configuration 4 (256 x 128, 8 waves of 64 x 64, three stages)
+// and the 128 x 128 tiles 1 and 7 (8 waves of 32 x 64, two or three
+// stages; at one round of tiles, e.g. 2048^3, 9-13% faster than 4 waves of
+// 64 x 64 on 32 x 32 MFMAs); configuration 10 keeps the 32 x 32 form of 0
+// for comparison.  FP16 results are bit-identical to those of the 32 x 32
+// form.  The other tiles and INT4 keep the 32 x 32 form.
 //
 // The stage geometry is that of the whole-line kernel: stages of 128 bytes
-// of K per row (two for 256 x 256, three for 256 x 128), BM rows of A then BN
+// of K per row (two or three), BM rows of A then BN
 // of B, each DMA instruction writing 8 whole rows, with chunk c of row r at
 // position c ^ swizzle16(r).  The MFMA takes 16 bytes of K per lane: lane l
 // of a 16-row block holds row l % 16 and bytes 16 (l / 16) .. + 15 of a
@@ -1525,7 +1528,8 @@ gemm_f6_kernel(F6Args args) {
 // stage k-step q = 0, 1), and the lanes of a 16-lane phase of the LDS read 8
 // consecutive rows at two logical chunks, the pattern swizzle16 keeps free
 // of bank conflicts.  A wave's 128 x 64 block is 8 x 4 MFMA blocks (128
-// accumulator registers; a 64 x 64 block 4 x 4, 64); its A fragments are held
+// accumulator registers; a 64 x 64 block 4 x 4, 64; a 32 x 64 block 2 x 4,
+// 32); its A fragments are held
 // in halves of its row blocks, so that the fragments of the next half k-step
 // fit beside the current ones and the accumulators within the 256 registers
 // of two waves per SIMD.  Result of block (i, j), register e of lane l: row
@@ -2026,22 +2030,26 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_mf16_kerne
 // 256 x 256 fits two 64 KB stages; 128 x 128 keeps two so that two
 // workgroups share a CU, except in 7, which takes three for products of at
 // most one tile per CU (where a CU holds one workgroup anyway); the others
-// take three.  The 256-row tiles run 8 waves, two per SIMD, so that one
-// wave's fragment reads, INT4 unpacking and barrier wait overlap the other's
-// MFMAs (their accumulators then live in VGPRs); 128 x 128 ran slower so.
+// take three.  The 256-row and 128 x 128 tiles run 8 waves, two per SIMD
+// for each workgroup, so that one wave's fragment reads, INT4 unpacking and
+// barrier wait overlap the other's MFMAs (their accumulators then live in
+// VGPRs).  128 x 128 with 8 waves of 32 x 64 on 16 x 16 MFMAs (FP16, INT8)
+// beat 4 waves of 64 x 64 on 32 x 32 ones by 2-13%; for INT4 on 32 x 32
+// MFMAs the 8 waves gained 2-14% on three stages (7) and lost 1-3% on two
+// (1) at 10240 x 2048 x 4096 and 4096^3, and one geometry serves both.
 struct Config {
     int bm, bn, wm, wn, gm, ks, ls;
 };
 
 constexpr Config kConfigs[] = {
-    {256, 256, 128, 64, 4, 1, 2},   // 0: large shapes (8 waves; FP16, INT8 with column-major B on 16 x 16 MFMAs)
-    {128, 128, 64, 64, 8, 1, 2},    // 1: medium
+    {256, 256, 128, 64, 4, 1, 2},   // 0: large shapes (8 waves; FP16 and INT8 on 16 x 16 MFMAs)
+    {128, 128, 32, 64, 8, 1, 2},    // 1: medium (8 waves)
     {64, 64, 32, 32, 8, 1, 3},      // 2: small
     {32, 32, 32, 32, 8, 4, 0},      // 3: few tiles (small M or N): K split over 4 waves
     {256, 128, 64, 64, 4, 1, 3},    // 4: between 0 and 1 (e.g. M = 1024 of a wide product; 8 waves)
     {128, 64, 64, 32, 8, 1, 3},     // 5: between 1 and 2 (e.g. M = 256)
     {64, 32, 64, 32, 8, 4, 3},      // 6: K split over 4 waves, 64 rows (e.g. M = 64 of a wide product)
-    {128, 128, 64, 64, 8, 1, 3},    // 7: 1 with three stages, for at most one round of tiles
+    {128, 128, 32, 64, 8, 1, 3},    // 7: 1 with three stages, for at most one round of tiles
     {256, 256, 128, 128, 4, 1, 2},  // 8: 0 with 4 waves of 128 x 128 (never picked: kept to compare)
     {64, 64, 64, 64, 8, 4, 2},      // 9: 2 with K split over 4 waves, for one round of tiles and long K
     {256, 256, 128, 64, 4, 1, 2},   // 10: 0 on 32 x 32 MFMAs for FP16 and INT8 too (never picked: kept to compare)
@@ -2074,7 +2082,12 @@ const void *kernel_ptr(int cfg) {
             return mf16_for<P, 0, E, BR>();
         else
             return kernel_for<P, 0, E, BR>();
-    case 1: return kernel_for<P, 1, E, BR>();
+    case 1:
+        // 128 x 128 (8 waves of 32 x 64), two or three stages: as 4
+        if constexpr ((P == kF16 || P == kI8) && (E == kRaw || (P == kI8 && BR == kBCol)))
+            return mf16_for<P, 1, E, BR>();
+        else
+            return kernel_for<P, 1, E, BR>();
     case 2: return kernel_for<P, 2, E, BR>();
     case 3: return kernel_for<P, 3, E, BR>();
     case 4:
@@ -2086,7 +2099,11 @@ const void *kernel_ptr(int cfg) {
             return kernel_for<P, 4, E, BR>();
     case 5: return kernel_for<P, 5, E, BR>();
     case 6: return kernel_for<P, 6, E, BR>();
-    case 7: return kernel_for<P, 7, E, BR>();
+    case 7:
+        if constexpr ((P == kF16 || P == kI8) && (E == kRaw || (P == kI8 && BR == kBCol)))
+            return mf16_for<P, 7, E, BR>();
+        else
+            return kernel_for<P, 7, E, BR>();
     case 8: return kernel_for<P, 8, E, BR>();
     case 9: return kernel_for<P, 9, E, BR>();
     case 10: return kernel_for<P, 10, E, BR>();
@@ -2134,16 +2151,15 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Steady throughput of each tile without K split, in TFLOP/s (FP16) or TOP/s
 // (INT8, INT4): back-to-back timings (HIP graphs of about 25 ms, medians of
-// three alternated rounds; INT4 the mean of two GPUs, FP16 and INT8 one GPU
-// since 0 and 4 run 16 x 16 MFMAs) on a product that gives every one of them
-// whole rounds of workgroups (M = K = 8192, N = 6144); only the ratios within
-// a row matter.  0 = not a candidate (the K-split tiles, 7,
+// three alternated rounds, one GPU) on a product that gives every one of
+// them whole rounds of workgroups (M = K = 8192, N = 6144); only the ratios
+// within a row matter.  0 = not a candidate (the K-split tiles, 7,
 // which stands in for 1, 9, which stands in for 2, 8, the 4-wave form of 0,
 // slower than 0 at N = 8192, and 10, 0 on 32 x 32 MFMAs).
 constexpr int kTileRate[3][kNumConfigs] = {
-    {1408, 1025, 707, 0, 1283, 789, 0, 0, 0, 0, 0},    // FP16
-    {2700, 2085, 1330, 0, 2445, 1612, 0, 0, 0, 0, 0},  // INT8
-    {2824, 2440, 1863, 0, 2499, 2021, 0, 0, 0, 0, 0},  // INT4
+    {1463, 1167, 728, 0, 1319, 766, 0, 0, 0, 0, 0},    // FP16
+    {2771, 2254, 1372, 0, 2566, 1667, 0, 0, 0, 0, 0},  // INT8
+    {2947, 2462, 1950, 0, 2625, 2086, 0, 0, 0, 0, 0},  // INT4
 };
 
 // When the 64 x 64 tile fills the chip (at least one workgroup per CU), a

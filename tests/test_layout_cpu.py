@@ -162,13 +162,14 @@ def permlane16_swap(x, y):
     return xr[0] + yr[0] + xr[2] + yr[2], xr[1] + yr[1] + xr[3] + yr[3]
 
 
-def test_mf16_result_layout_covers_the_wave_tile():
+@pytest.mark.parametrize("fm", [8, 4, 2])
+def test_mf16_result_layout_covers_the_wave_tile(fm):
     # register e of lane l in block (i, j): row 16i + 4(l//16) + e, column 16j + l%16; the
     # epilogue swaps blocks 2h and 2h+1 and stores the first result at row 16i + e + 8(l//32),
-    # the second 4 rows below, column 32h + l%32: each element of the 128 x 64 wave tile once,
-    # each store two whole 128-byte rows
+    # the second 4 rows below, column 32h + l%32: each element of the 16 fm x 64 wave tile
+    # (128, 64 or 32 rows) once, each store two whole 128-byte rows
     stored = {}
-    for i in range(8):
+    for i in range(fm):
         for e in range(4):
             for h in range(2):
                 held = [[(16 * i + 4 * (l // 16) + e, 16 * j + l % 16) for l in range(64)] for j in (2 * h, 2 * h + 1)]
@@ -178,10 +179,10 @@ def test_mf16_result_layout_covers_the_wave_tile():
                         want = (16 * i + e + 4 * k + 8 * (l // 32), 32 * h + l % 32)
                         assert reg[l] == want
                         stored[want] = stored.get(want, 0) + 1
-    assert stored == {(r, c): 1 for r in range(128) for c in range(64)}
+    assert stored == {(r, c): 1 for r in range(16 * fm) for c in range(64)}
 
 
-@pytest.mark.parametrize("bm,bn,waves", [(256, 256, 8), (128, 128, 4), (64, 64, 4), (256, 128, 8), (128, 64, 4),
+@pytest.mark.parametrize("bm,bn,waves", [(256, 256, 8), (128, 128, 8), (64, 64, 4), (256, 128, 8), (128, 64, 4),
                                          (32, 32, 1), (64, 32, 1)])
 def test_line_dma_fills_every_row_once(bm, bn, waves):
     # instruction j of wave w writes LDS rows (j*waves + w)*8 .. +7, lane l to row l/8 at
@@ -374,7 +375,7 @@ def test_rowmajor_b_layout(prec, cfg):
 
 # the tiles without K split (4 or 8 waves), and one K slice of the K-split tiles (a slice is
 # staged and read by one wave, as a one-wave tile)
-LINE_CONFIGS = [(256, 256, 128, 64), (128, 128, 64, 64), (64, 64, 32, 32), (256, 128, 64, 64), (128, 64, 64, 32),
+LINE_CONFIGS = [(256, 256, 128, 64), (128, 128, 32, 64), (64, 64, 32, 32), (256, 128, 64, 64), (128, 64, 64, 32),
                 (32, 32, 32, 32), (64, 32, 64, 32)]
 
 
