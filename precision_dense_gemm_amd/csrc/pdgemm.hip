@@ -2170,11 +2170,12 @@ constexpr int kTileRate[3][kNumConfigs] = {
 // CUs run, the higher their clock and the more L2 and HBM bandwidth each
 // gets.  The cheapest tile wins, the larger one on a tie.  (E.g. 144 tiles of
 // 256 x 256 rather than 576 of 128 x 128 at 3072^3; for FP16 and INT8, 768
-// of 256 x 128 rather than 384 of 256 x 256 at 8192 x 3072 x 8192.)  Fitted
-// to 69 shapes from 1024^3 to 12288 x 4096 x 4096 in three precisions, the
-// partial-round rule on two GPUs, the FP16 and INT8 rates again on one after
-// the 16 x 16 MFMA kernels: 0.2-0.3% slower than the fastest tile on
-// average, at most 7.8% (INT4 1536^3).  When
+// of 256 x 128 rather than 384 of 256 x 256 at 8192 x 3072 x 8192.)  The
+// partial-round rule was fitted to 69 shapes from 1024^3 to 12288 x 4096 x
+// 4096 in three precisions on two GPUs, the rates measured again after the
+// 16 x 16 MFMA kernels: over 78 shapes (M = 256-512 x 8192 x 8192 added)
+// 0.06% slower than the fastest tile on average, at most 2.3% (FP16 6144^3).
+// When
 // even the 64 x 64 tile leaves CUs idle (small M or N), a K-split tile puts
 // 4 waves on each of up to 4 times as many tiles.  128 x 128 with at most
 // one tile per CU takes configuration 7.
