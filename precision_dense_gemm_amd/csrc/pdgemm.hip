@@ -2163,12 +2163,15 @@ constexpr int kTileRate[3][kNumConfigs] = {
 };
 
 // When the 64 x 64 tile fills the chip (at least one workgroup per CU), a
-// time model chooses among the tiles that give at least half of the CUs
+// time model chooses among the tiles that give more than half of the CUs
 // one: the busiest CU sets the time, so a product of T tiles takes T / 256
 // rounds, each of which costs the tile's area over its throughput.  A
 // partial last round costs 0.35 + 0.65 * (its fill) of a full one: the fewer
 // CUs run, the higher their clock and the more L2 and HBM bandwidth each
-// gets.  The cheapest tile wins, the larger one on a tie.  (E.g. 144 tiles of
+// gets.  (A tile that busies exactly half of the CUs lost to a full round
+// of a smaller one wherever it was timed, e.g. 128 x 128 against 128 x 64 at
+// 256 x 8192 x 8192 by 1-13%, most with row-major B.)  The cheapest tile
+// wins, the larger one on a tie.  (E.g. 144 tiles of
 // 256 x 256 rather than 576 of 128 x 128 at 3072^3; for FP16 and INT8, 768
 // of 256 x 128 rather than 384 of 256 x 256 at 8192 x 3072 x 8192.)  The
 // partial-round rule was fitted to 69 shapes from 1024^3 to 12288 x 4096 x
@@ -2186,7 +2189,7 @@ int pick(int prec, int64_t M, int64_t N, int64_t K) {
         double best_cost = 0;
         for (int c : kPickOrder) {
             const int64_t t = tiles(c);
-            if (kTileRate[prec][c] == 0 || t < 128) continue;
+            if (kTileRate[prec][c] == 0 || t <= 128) continue;
             const double partial = double(t % 256) / 256;
             const double rounds = double(t / 256) + (partial > 0 ? 0.35 + 0.65 * partial : 0.0);
             const double cost = rounds * kConfigs[c].bm * kConfigs[c].bn / kTileRate[prec][c];
