@@ -117,6 +117,23 @@ def test_every_config(pd, dev, prec, cfg, shape):
 
 
 # ---------------------------------------------------------------------------
+# grids of whole 16 x 16 windows of tiles, where the large tiles run in window
+# order (one window per round, windows row by row in serpentine order): one
+# window column, several in a row, and a 2 x 3 grid; every element checked
+
+WINDOW_CASES = [(0, (4096, 8192, 320)), (0, (8192, 4096, 192)), (0, (8192, 12288, 96)),
+                (4, (4096, 6144, 130)), (10, (4096, 8192, 200))]
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("cfg,shape", WINDOW_CASES, ids=[f"cfg{c}-{m}x{n}x{k}" for c, (m, n, k) in WINDOW_CASES])
+def test_window_order_grids(pd, dev, prec, cfg, shape):
+    M, N, K = shape
+    A, Bt, C = run_case(pd, dev, prec, M, N, K, 4242 + cfg, cfg=cfg)
+    gu.check_whole(prec, A, Bt, K, C, f"{prec} cfg{cfg} {shape}")
+
+
+# ---------------------------------------------------------------------------
 # the worked example and closed forms on the GPU
 
 def test_mma_lab_identity_on_gpu(pd, dev):
