@@ -238,7 +238,8 @@ __device__ __forceinline__ int bswizzle(int r) {
 // column within a band), so that the workgroups resident on one XCD share A
 // and B panels in its L2.
 //
-// With kWindows (the large tiles, GM = 4) and a grid of whole 16 x 16 windows
+// With kWindows and band 4 (the 256-row tiles, and every tile of the 16 x 16
+// MFMA kernel) and a grid of whole 16 x 16 windows
 // of tiles, the order is by window instead: window w takes block ids 256 w ..
 // 256 w + 255, one round of the 256 CUs at one workgroup each; in it XCD x
 // runs the 4 x 8 tiles at block row x % 4, block column x / 4 (column by

@@ -117,12 +117,13 @@ def test_every_config(pd, dev, prec, cfg, shape):
 
 
 # ---------------------------------------------------------------------------
-# grids of whole 16 x 16 windows of tiles, where the large tiles run in window
+# grids of whole 16 x 16 windows of tiles, where the tiles of band 4 (the
+# 256-row tiles, and every tile of the 16 x 16 MFMA kernel) run in window
 # order (one window per round, windows row by row in serpentine order): one
-# window column, several in a row, and a 2 x 3 grid; every element checked
+# window column, several in a row, 2 x 2 and 2 x 3 grids; every element checked
 
 WINDOW_CASES = [(0, (4096, 8192, 320)), (0, (8192, 4096, 192)), (0, (8192, 12288, 96)),
-                (4, (4096, 6144, 130)), (10, (4096, 8192, 200))]
+                (4, (4096, 6144, 130)), (10, (4096, 8192, 200)), (1, (4096, 4096, 130)), (7, (2048, 6144, 64))]
 
 
 @pytest.mark.parametrize("prec", PRECS)
