@@ -239,9 +239,9 @@ __device__ __forceinline__ int bswizzle(int r) {
 // and B panels in its L2.
 //
 // With kWindows and band 4 (the 256-row tiles, and every tile of the 16 x 16
-// MFMA kernel) and a grid of whole 16 x 16 windows
-// of tiles, the order is by window instead: window w takes block ids 256 w ..
-// 256 w + 255, one round of the 256 CUs at one workgroup each; in it XCD x
+// MFMA kernel) and a grid of whole 16 x 16 windows of tiles, the order is by
+// window instead: window w takes block ids 256 w .. 256 w + 255, one round of
+// the 256 CUs at one workgroup each; in it XCD x
 // runs the 4 x 8 tiles at block row x % 4, block column x / 4 (column by
 // column), and the windows are taken row by row in serpentine order.  Each
 // XCD still shares 4 panels of A and 8 of B in its L2, but a round reads 16
@@ -2178,8 +2178,8 @@ constexpr int kTileRate[3][kNumConfigs] = {
 // partial-round rule was fitted to 69 shapes from 1024^3 to 12288 x 4096 x
 // 4096 in three precisions on two GPUs, the rates measured again after the
 // 16 x 16 MFMA kernels: over 78 shapes (M = 256-512 x 8192 x 8192 added)
-// 0.06% slower than the fastest tile on average, at most 2.3% (FP16 6144^3).
-// When
+// 0.09% slower than the fastest tile on average, at most 2.5% (FP16 256 x
+// 8192 x 8192, a near tie there).  When
 // even the 64 x 64 tile leaves CUs idle (small M or N), a K-split tile puts
 // 4 waves on each of up to 4 times as many tiles.  128 x 128 with at most
 // one tile per CU takes configuration 7.
