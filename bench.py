@@ -311,7 +311,8 @@ def kernel_name(pd, prec, n, i4_path=None):
     if prec == "i4" and i4_path == "fp6":
         return "gemm_f6_kernel"
     cfg = pd.pick_config({"f16": pd.PREC_F16, "i8": pd.PREC_I8, "i4": pd.PREC_I4}[prec], n, n, n)
-    return "gemm_mf16_kernel" if prec in ("f16", "i8") and cfg == 0 else "gemm_kernel"
+    # FP16 and INT8 run the 16 x 16 MFMA kernel on the 256 x 256, 256 x 128 and 128 x 128 tiles
+    return "gemm_mf16_kernel" if prec in ("f16", "i8") and cfg in (0, 1, 4, 7) else "gemm_kernel"
 
 
 def shape_roofline(prec, M, N, K, ms):

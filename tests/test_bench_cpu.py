@@ -57,3 +57,6 @@ def test_roofline_names_the_kernel_that_runs():
     assert bench.kernel_name(pd, "i4", 8192) == "gemm_kernel"    # without a workspace: nibble planes
     assert bench.kernel_name(pd, "i4", 8192, "fp6") == "gemm_f6_kernel"
     assert bench.kernel_name(pd, "f16", 512) == "gemm_kernel"   # a smaller tile, 32 x 32 MFMAs
+    assert bench.kernel_name(pd, "i8", 2048) == "gemm_mf16_kernel"   # 128 x 128, 16 x 16 MFMAs
+    assert bench.kernel_name(pd, "i4", 2048) == "gemm_kernel"
+    assert bench.kernel_name(pd, "f16", 1024) == "gemm_kernel"   # 64 x 64
